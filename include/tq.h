@@ -1,0 +1,185 @@
+/*
+ * tq.h -- C ABI of the TurboQuant hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the two quantizers and the scoring paths described by
+ * the pages on TurboQuant (arXiv 2504.19874):
+ *
+ *   Algorithm 1 (TurboQuant_mse): keep the vector norm, rotate by a random
+ *     orthogonal matrix Pi, map every rotated coordinate to the nearest
+ *     Lloyd-Max centroid of the coordinate law at dimension d, invert the
+ *     rotation on decode.  [ai-navigate-news Gemma 4 post, section
+ *     "仕組み（技術的）"; AiBoss overview, section "TurboQuantの技術原理"]
+ *   Algorithm 2 (TurboQuant_prod): Algorithm 1 at b-1 bits, then the sign
+ *     bits of S r for the residual r together with ||r|| -- an unbiased
+ *     inner-product estimate.  [same post and section; AIgent Lab explainer,
+ *     section "視点1" (QJL)]
+ *   Dense records: index bit planes and sign bits packed into bytes, norms and
+ *     residual norms ("gammas") as fp16.  [same post, same section]
+ *   Attention and inner-product search computed on the packed codes.
+ *     [AiBoss overview, sections "TurboQuantの主な機能" and
+ *     "TurboQuantの応用事例"]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns a tq_status (0 = TQ_OK, negative = error) unless
+ *   stated otherwise.  Nothing throws across the ABI.  Arguments are checked
+ *   on the host before anything is launched; a rejected call launches nothing
+ *   and writes nothing.
+ * - "device pointer" arguments are caller-owned device memory on the device
+ *   that was current when the quantizer was created.  The library never frees
+ *   them.  "host pointer" arguments are read (or written) synchronously.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Device work is enqueued on it and the call returns without waiting.
+ * - A quantizer is immutable after creation and may be used from several
+ *   streams or threads at once.
+ * - Record layout (one vector): P planes of d bits, P*d/8 bytes.  Bit j of a
+ *   plane lives in byte j/8 at bit position j%8 (equivalently: little-endian
+ *   64-bit word j/64, bit j%64).  TQ_MSE with b bits: planes 0..b-1 hold bit p
+ *   of the centroid index.  TQ_PROD with b bits: planes 0..b-2 hold the index
+ *   of the (b-1)-bit codebook, plane b-1 holds the sign bits of S r
+ *   (1 = non-negative).  Norms and gammas are IEEE fp16 bit patterns in
+ *   separate uint16 arrays.
+ * - Non-finite input values are a precondition violation (codes unspecified).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID = -1,     /* bad argument: null, size, alignment, mismatch */
+  TQ_ERR_UNSUPPORTED = -2, /* valid request outside what the library implements */
+  TQ_ERR_HIP = -3,         /* a HIP runtime call failed; see tq_last_hip_error() */
+  TQ_ERR_NOMEM = -4,       /* device or host allocation failed */
+  TQ_ERR_WORKSPACE = -5    /* workspace pointer null or smaller than required */
+} tq_status;
+
+typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_mode;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef struct tq_quantizer tq_quantizer; /* opaque */
+
+/* Lloyd-Max codebook of the coordinate law at dimension d (host, synchronous).
+ * The law is that of one coordinate of a uniform point on the unit sphere
+ * S^{d-1}: density proportional to (1-u^2)^((d-3)/2) on [-1, 1], the
+ * Beta-shaped law of the AiBoss overview, section "TurboQuantの技術原理".
+ * Lloyd-Max (boundaries at midpoints, centroids at conditional means) is
+ * iterated to the fp64 floor; the codebook is symmetric.
+ *   d:         3 <= d <= 65536
+ *   bits:      1 <= bits <= 8
+ *   centroids: host, 2^bits doubles, written ascending
+ *   bounds:    host, 2^bits - 1 doubles (midpoints), may be NULL
+ * Returns TQ_ERR_INVALID on bad d/bits or null centroids. */
+int tq_codebook_build(int d, int bits, double *centroids, double *bounds);
+
+/* Create a quantizer for dimension d on the current HIP device.
+ *   mode TQ_MSE : 1 <= bits <= 4, s ignored (may be NULL)
+ *   mode TQ_PROD: 2 <= bits <= 4, s required
+ *   d:  multiple of 64, 64 <= d <= 2048
+ *   pi: host, d*d floats row-major, the rotation (caller keeps ownership;
+ *       it is copied).  The library assumes it is orthogonal to fp32
+ *       precision and does not check.
+ *   s:  host, d*d floats row-major, the QJL projection with d rows.
+ * The codebook (bits for TQ_MSE, bits-1 for TQ_PROD) is built here.
+ * On success *out receives the quantizer; destroy it with
+ * tq_quantizer_destroy. */
+int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const float *pi, const float *s);
+void tq_quantizer_destroy(tq_quantizer *q);
+
+/* Shape of a quantizer.  Any output pointer may be NULL.
+ *   planes     : bit planes per record
+ *   code_bytes : planes * d / 8, bytes of one record in `codes` arrays */
+int tq_quantizer_info(const tq_quantizer *q, int *d, int *bits, int *mode, int *planes, size_t *code_bytes);
+
+/* Algorithm 1 encode of n vectors.
+ *   x:     device, n rows of d values of type xt, row stride ldx elements
+ *          (ldx >= d); TQ_F32, TQ_BF16 or TQ_F16
+ *   codes: device, n * code_bytes bytes, 16-byte aligned
+ *   norms: device, n fp16 bit patterns: fp16(||x||) round-to-nearest-even,
+ *          saturating at 65504
+ * Index j of a vector is the number of codebook boundaries t_k with
+ * t_k * ||x|| < (Pi x)_j (a value on a boundary goes to the lower cell; the
+ * zero vector gets index 2^(b-1) - 1 everywhere).  q must be TQ_MSE.
+ * n == 0 is a no-op. */
+int tq_encode_mse(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx,
+                  uint8_t *codes, uint16_t *norms, void *stream);
+
+/* Algorithm 2 encode of n vectors (q must be TQ_PROD).  As tq_encode_mse with
+ * the (b-1)-bit codebook, then r = x - n_hat * Pi^T c[idx], sign plane bit i =
+ * [(S r)_i >= 0] and gammas[i] = fp16(||r||).
+ *   gammas: device, n fp16 bit patterns */
+int tq_encode_prod(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx,
+                   uint8_t *codes, uint16_t *norms, uint16_t *gammas, void *stream);
+
+/* Decode n records to fp32 rows.
+ *   TQ_MSE : out = n_hat * Pi^T c[idx]
+ *   TQ_PROD: out = n_hat * Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T (2 bits - 1)
+ *   gammas: device, required for TQ_PROD, ignored for TQ_MSE
+ *   out:    device, n rows, row stride ldo >= d floats */
+int tq_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas,
+              int64_t n, float *out, int64_t ldo, void *stream);
+
+/* Inner-product scores of m fp32 queries against n records: est = <q, decode(x)>,
+ * computed as n_hat <Pi q, c[idx]> (+ sqrt(pi/2)/d * gamma <S q, s> for TQ_PROD).
+ *   queries: device, m rows, stride ldq >= d floats
+ *   k == 0 : scores = device [m * n] floats, row-major; idx unused
+ *   k >= 1 : per query the k best records by descending score (ties -> lower
+ *            record index): scores = device [m * k] floats, idx = device
+ *            [m * k] int64.  k <= 64 and k <= n.
+ *   ws/ws_bytes: device workspace of at least tq_score_ws_bytes(...) bytes */
+int tq_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
+             const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx,
+             void *ws, size_t ws_bytes, void *stream);
+size_t tq_score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
+
+/* Decode attention of one new query token per sequence against a compressed
+ * cache: keys through Algorithm 1 (kq, TQ_MSE), values through Algorithm 2
+ * (vq, TQ_PROD), as the ai-navigate-news Gemma 4 post assigns them (section
+ * "仕組み（技術的）").  For batch b and query head h, with g = h / (Hq/Hkv):
+ *   s_t = scale * <q[b,h], K~[b,g,t]>  for t < seq_len[b]
+ *   out[b,h] = sum_t softmax(s)_t V~[b,g,t]      (zero when seq_len[b] == 0)
+ * where K~, V~ are the decodes of the records.
+ *   q:       device [B, Hq, d] of type qt (TQ_F32, TQ_BF16 or TQ_F16)
+ *   kcodes:  device [B, Hkv, Tstride, kcode_bytes], knorms [B, Hkv, Tstride]
+ *   vcodes:  device [B, Hkv, Tstride, vcode_bytes], vnorms, vgammas [B, Hkv, Tstride]
+ *   seq_len: device [B] int32, 0 <= seq_len[b] <= Tstride
+ *   out:     device [B, Hq, d] fp32
+ *   ws:      device workspace of at least tq_attn_decode_ws_bytes(...) bytes
+ * kq and vq must share d; Hq % Hkv == 0. */
+int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                   int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
+                   const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len,
+                   float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride);
+
+/* Optional per-kernel timing.  When enabled, the library records a pair of
+ * HIP events on the launch stream around every kernel it launches (a few
+ * microseconds of overhead per launch); disabled by default.
+ *   tq_profile_enable(on): on != 0 enables, 0 disables (recorded data kept).
+ *   tq_profile_query(name, total_ms, count): waits for the recorded events and
+ *     returns the summed elapsed time and number of launches of kernels whose
+ *     name contains `name` (NULL or "" = all).  Kernel names are listed in the
+ *     design notes (e.g. "attn_split", "attn_combine", "encode").
+ *   tq_profile_reset(): drops all recorded launches.
+ * Thread-safe; events are shared by all streams of the process. */
+int tq_profile_enable(int on);
+int tq_profile_query(const char *name, double *total_ms, int64_t *count);
+int tq_profile_reset(void);
+
+/* Human-readable name of a status code (static string). */
+const char *tq_status_str(int status);
+/* hipError_t of the last HIP failure seen by this thread (0 if none). */
+int tq_last_hip_error(void);
+/* Library version, e.g. "0.1.0" (static string). */
+const char *tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,90 @@
+"""Host-side checks of libtq.so that need no GPU.
+
+* the library loads and exports every function include/tq.h declares;
+* the host Lloyd-Max builder agrees with the oracle's codebook;
+* argument validation rejects bad calls before any device work.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from vector_quantization_rotation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for need in ["tq_codebook_build", "tq_encode_mse", "tq_encode_prod", "tq_decode", "tq_score", "tq_attn_decode"]:
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert {n for n, _, _ in _lib.SIGNATURES} == set(_declared())
+
+
+def test_status_strings():
+    lib = _lib.load()
+    assert lib.tq_status_str(0) == b"TQ_OK"
+    assert lib.tq_status_str(-5) == b"TQ_ERR_WORKSPACE"
+    assert lib.tq_version() == b"0.1.0"
+
+
+@pytest.mark.parametrize("d", [3, 64, 128, 256, 512, 1536])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(d, bits):
+    c, t = _lib.codebook_build(d, bits)
+    co, to = oracle.lloyd_max(d, bits)
+    # the two builders normalise the law differently; they agree far below fp32 resolution
+    assert np.allclose(c, co, rtol=5e-11, atol=0)
+    assert np.allclose(t, to, rtol=5e-11, atol=1e-300)
+    assert np.array_equal(c, -c[::-1])
+
+
+def test_codebook_invalid_arguments():
+    lib = _lib.load()
+    buf = (C.c_double * 16)()
+    assert lib.tq_codebook_build(2, 2, buf, None) == _lib.TQ_ERR_INVALID
+    assert lib.tq_codebook_build(128, 0, buf, None) == _lib.TQ_ERR_INVALID
+    assert lib.tq_codebook_build(128, 2, None, None) == _lib.TQ_ERR_INVALID
+
+
+def test_quantizer_create_rejects_bad_shapes_without_device():
+    lib = _lib.load()
+    h = C.c_void_p()
+    pi = (C.c_float * (100 * 100))()
+    assert lib.tq_quantizer_create(C.byref(h), 100, 2, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID  # d % 64
+    assert lib.tq_quantizer_create(C.byref(h), 4096, 2, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID
+    assert lib.tq_quantizer_create(C.byref(h), 128, 5, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_UNSUPPORTED
+    assert lib.tq_quantizer_create(C.byref(h), 128, 1, _lib.TQ_PROD, pi, pi) == _lib.TQ_ERR_UNSUPPORTED
+    assert lib.tq_quantizer_create(C.byref(h), 128, 3, _lib.TQ_PROD, pi, None) == _lib.TQ_ERR_INVALID
+    assert lib.tq_quantizer_create(C.byref(h), 128, 3, 7, pi, pi) == _lib.TQ_ERR_INVALID
+    assert lib.tq_quantizer_create(None, 128, 3, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID
+    assert h.value is None
+
+
+def test_entry_points_reject_null_quantizer():
+    lib = _lib.load()
+    z = C.c_void_p(0)
+    assert lib.tq_encode_mse(z, z, 0, 1, 128, z, z, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_encode_prod(z, z, 0, 1, 128, z, z, z, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_decode(z, z, z, z, 1, z, 128, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_score(z, z, 1, 128, z, z, z, 1, 0, z, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_decode_ws_bytes(z, 1, 4, 1, 16) == 0
+    assert lib.tq_score_ws_bytes(z, 1, 1, 0) == 0
+    assert lib.tq_quantizer_info(z, None, None, None, None, None) == _lib.TQ_ERR_INVALID
+    lib.tq_quantizer_destroy(z)  # no-op on null

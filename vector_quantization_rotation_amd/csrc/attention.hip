@@ -1,0 +1,259 @@
+// Decode attention on a TurboQuant-compressed KV cache, split over the sequence.
+//
+// Keys are Algorithm-1 records and values Algorithm-2 records, the assignment
+// made on the ai-navigate-news Gemma 4 post (section "仕組み（技術的）"): K~ for
+// the scores, V~ (unbiased) for attn_weights . V.  Nothing is dequantized into
+// the original domain: with q' = Pi_K q,
+//     <q, K~_t> = n_t <q', c_K[idx_t]>,
+//     sum_t p_t V~_t = Pi_V^T (sum_t p_t n_t c_V[idx_t]) + k_d S_V^T (sum_t p_t g_t s_t),
+// so the kernels score in the rotated domain, accumulate in the rotated and the
+// sign domains, and rotate back once per (batch, head) in the combine step.
+//
+// Generic path: one wavefront per (batch, kv head, head subgroup, sequence
+// split); lane j owns coordinates j, j+64, ...; online softmax per head.
+#include "common.cuh"
+
+namespace tq {
+
+namespace {
+
+constexpr int kAttnChunkMin = 256;
+
+struct AttnPlan {
+  int G, GW, nsub, nsplit, chunk, CP;
+};
+
+int coords_per_lane_supported(int d) {
+  const int cp = d / 64;
+  return (cp == 1 || cp == 2 || cp == 4 || cp == 8 || cp == 16 || cp == 24 || cp == 32) ? cp : 0;
+}
+
+AttnPlan make_plan(int d, int B, int Hq, int Hkv, int64_t T) {
+  AttnPlan p{};
+  p.CP = coords_per_lane_supported(d);
+  p.G = Hq / Hkv;
+  p.GW = p.CP ? std::min(p.G, std::max(1, 32 / p.CP)) : 1;
+  p.nsub = (p.G + p.GW - 1) / p.GW;
+  const int64_t units = (int64_t)B * Hkv * p.nsub;
+  int64_t want = std::max<int64_t>(1, 4096 / std::max<int64_t>(units, 1));
+  int64_t chunk = std::max<int64_t>(kAttnChunkMin, (T + want - 1) / std::max<int64_t>(want, 1));
+  chunk = (chunk + 63) / 64 * 64;
+  p.chunk = (int)std::min<int64_t>(chunk, 1 << 30);
+  p.nsplit = (int)std::max<int64_t>(1, (T + p.chunk - 1) / p.chunk);
+  return p;
+}
+
+size_t partial_floats(int d) { return 2 + 2 * (size_t)d; }
+
+}  // namespace
+
+// q'[b,h,:] = Pi_K q[b,h,:]
+template <int QT>
+__global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *pi, float *qrot) {
+  extern __shared__ float sq[];
+  const int64_t bh = blockIdx.x;
+  for (int j = threadIdx.x; j < d; j += 256) {
+    float v;
+    if (QT == TQ_F32) v = static_cast<const float *>(q)[bh * d + j];
+    else if (QT == TQ_BF16) v = bf16_to_f32(static_cast<const uint16_t *>(q)[bh * d + j]);
+    else v = f16_to_f32(static_cast<const uint16_t *>(q)[bh * d + j]);
+    sq[j] = v;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += 256) {
+    const float *row = pi + (int64_t)j * d;
+    float acc = 0.f;
+    for (int k = 0; k < d; ++k) acc = fmaf(row[k], sq[k], acc);
+    qrot[bh * d + j] = acc;
+  }
+}
+
+template <int CP, int GW>
+__global__ __launch_bounds__(64) void attn_split_kernel(
+    const float *qrot, int Hq, int Hkv, int G, int nsub, int d, const uint8_t *kcodes, const uint16_t *knorms,
+    int64_t kcb, int kbits, const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t vcb,
+    int vbmse, int64_t Tstride, const int32_t *seq_len, float scale_log2, float vqjl, Codebook kc, Codebook vc,
+    int chunk, int nsplit, float *part) {
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;  // ((b * Hkv) + g) * nsub + sub
+  const int split = blockIdx.y;
+  const int sub = unit % nsub;
+  const int bg = unit / nsub;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int h0 = g * G + sub * GW;
+  const int gw = min(GW, G - sub * GW);
+  const int64_t T = seq_len[b];
+  const int64_t t0 = (int64_t)split * chunk;
+  const int64_t t1 = min<int64_t>(T, t0 + chunk);
+
+  float qv[GW][CP];
+#pragma unroll
+  for (int h = 0; h < GW; ++h)
+#pragma unroll
+    for (int c = 0; c < CP; ++c)
+      qv[h][c] = h < gw ? qrot[((int64_t)b * Hq + h0 + h) * d + lane + 64 * c] : 0.f;
+  float m[GW], l[GW], am[GW][CP], aq[GW][CP];
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CP; ++c) am[h][c] = aq[h][c] = 0.f;
+  }
+  const int64_t base = ((int64_t)b * Hkv + g) * Tstride;
+  const int wbytes = d >> 3;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint8_t *kr = kcodes + (base + t) * kcb;
+    const uint8_t *vr = vcodes + (base + t) * vcb;
+    float kval[CP], vm[CP], vs[CP];
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      int idx = 0;
+      for (int p = 0; p < kbits; ++p) {
+        unsigned long long w = *reinterpret_cast<const unsigned long long *>(kr + p * wbytes + 8 * c);
+        idx |= (int)((w >> lane) & 1ull) << p;
+      }
+      kval[c] = kc.c[idx];
+      int vi = 0;
+      for (int p = 0; p < vbmse; ++p) {
+        unsigned long long w = *reinterpret_cast<const unsigned long long *>(vr + p * wbytes + 8 * c);
+        vi |= (int)((w >> lane) & 1ull) << p;
+      }
+      vm[c] = vc.c[vi];
+      unsigned long long ws = *reinterpret_cast<const unsigned long long *>(vr + vbmse * wbytes + 8 * c);
+      vs[c] = ((ws >> lane) & 1ull) ? 1.f : -1.f;
+    }
+    const float kn = f16_to_f32(knorms[base + t]) * scale_log2;
+    const float vn = f16_to_f32(vnorms[base + t]);
+    const float vg = f16_to_f32(vgammas[base + t]) * vqjl;
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+      if (h >= gw) break;
+      float part_s = 0.f;
+#pragma unroll
+      for (int c = 0; c < CP; ++c) part_s = fmaf(qv[h][c], kval[c], part_s);
+      const float s = wave_sum_f32(part_s) * kn;  // log2-domain score
+      if (s > m[h]) {
+        const float corr = exp2f(m[h] - s);
+        l[h] *= corr;
+#pragma unroll
+        for (int c = 0; c < CP; ++c) { am[h][c] *= corr; aq[h][c] *= corr; }
+        m[h] = s;
+      }
+      const float p = exp2f(s - m[h]);
+      l[h] += p;
+      const float pm = p * vn, pq = p * vg;
+#pragma unroll
+      for (int c = 0; c < CP; ++c) {
+        am[h][c] = fmaf(pm, vm[c], am[h][c]);
+        aq[h][c] = fmaf(pq, vs[c], aq[h][c]);
+      }
+    }
+  }
+  // partial record: [m (log2 domain), l, acc_mse[d], acc_qjl[d]]
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    if (h >= gw) break;
+    float *dst = part + (((int64_t)b * Hq + h0 + h) * nsplit + split) * (2 + 2 * (int64_t)d);
+    if (lane == 0) { dst[0] = m[h]; dst[1] = l[h]; }
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      dst[2 + lane + 64 * c] = am[h][c];
+      dst[2 + d + lane + 64 * c] = aq[h][c];
+    }
+  }
+}
+
+// merge the splits of one (batch, head) and rotate back:
+// out = (Pi_V^T A_mse + S_V^T A_qjl) / L   (A_qjl already carries the QJL constant)
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float *part, int nsplit, int d, const float *piT,
+                                                           const float *sT, float *out) {
+  extern __shared__ float sh[];  // [2d] merged accumulators
+  const int64_t bh = blockIdx.x;
+  const float *pp = part + bh * nsplit * (2 + 2 * (int64_t)d);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (2 + 2 * (int64_t)d)]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float *q = pp + s * (2 + 2 * (int64_t)d);
+    if (q[1] > 0.f) L += q[1] * exp2f(q[0] - M);
+  }
+  for (int j = threadIdx.x; j < 2 * d; j += 256) {
+    float a = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float *q = pp + s * (2 + 2 * (int64_t)d);
+      if (q[1] > 0.f) a = fmaf(q[2 + j], exp2f(q[0] - M), a);
+    }
+    sh[j] = a;
+  }
+  __syncthreads();
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float *r1 = piT + (int64_t)i * d;
+    const float *r2 = sT + (int64_t)i * d;
+    float acc = 0.f;
+    for (int j = 0; j < d; ++j) acc = fmaf(r1[j], sh[j], acc);
+    for (int j = 0; j < d; ++j) acc = fmaf(r2[j], sh[d + j], acc);
+    out[bh * d + i] = acc * inv;
+  }
+}
+
+size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride) {
+  const int d = kq->d;
+  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
+  size_t qb = ((size_t)B * Hq * d * 4 + 255) & ~(size_t)255;
+  return qb + (size_t)B * Hq * p.nsplit * partial_floats(d) * 4;
+}
+
+template <int CP>
+static void launch_split(const AttnPlan &p, dim3 grid, hipStream_t st, const float *qrot, int Hq, int Hkv, int d,
+                         const tq_quantizer *kq, const tq_quantizer *vq, const uint8_t *kcodes,
+                         const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
+                         const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale_log2,
+                         float *part) {
+  constexpr int GW = (32 / CP) > 0 ? (32 / CP) : 1;
+  hipLaunchKernelGGL((attn_split_kernel<CP, GW>), grid, dim3(64), 0, st, qrot, Hq, Hkv, p.G, p.nsub, d, kcodes,
+                     knorms, (int64_t)kq->code_bytes, kq->bits, vcodes, vnorms, vgammas, (int64_t)vq->code_bytes,
+                     vq->bmse, Tstride, seq_len, scale_log2, vq->qjl_scale, kq->cb, vq->cb, p.chunk, p.nsplit, part);
+}
+
+int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
+                    const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
+                    const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
+                    void *ws, size_t ws_bytes, hipStream_t st) {
+  const int d = kq->d;
+  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
+  if (!p.CP) return TQ_ERR_UNSUPPORTED;
+  float *qrot = static_cast<float *>(ws);
+  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + (((size_t)B * Hq * d * 4 + 255) & ~(size_t)255));
+  const size_t shq = (size_t)d * 4;
+  {
+  ProfScope ps("attn_qrot", st);
+  if (qt == TQ_F32) hipLaunchKernelGGL(attn_qrot_kernel<TQ_F32>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
+  else if (qt == TQ_BF16) hipLaunchKernelGGL(attn_qrot_kernel<TQ_BF16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
+  else hipLaunchKernelGGL(attn_qrot_kernel<TQ_F16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
+  }
+  int rc = launch_check();
+  if (rc != TQ_OK) return rc;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid((unsigned)(B * Hkv * p.nsub), (unsigned)p.nsplit);
+  {
+  ProfScope ps("attn_split", st);
+  switch (p.CP) {
+    case 1: launch_split<1>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 2: launch_split<2>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 4: launch_split<4>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 8: launch_split<8>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 16: launch_split<16>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 24: launch_split<24>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    default: launch_split<32>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+  }
+  }
+  if ((rc = launch_check()) != TQ_OK) return rc;
+  ProfScope ps("attn_combine", st);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(256), 2 * (size_t)d * 4, st, part, p.nsplit, d, vq->piT,
+                     vq->sT, out);
+  return launch_check();
+}
+
+}  // namespace tq

@@ -1,0 +1,56 @@
+// Device helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// fp64 -> fp16 bits, round to nearest even, saturating at 65504 (v >= 0 expected;
+// negative and NaN inputs give 0).
+__device__ __forceinline__ uint16_t f64_to_f16_rne_sat(double v) {
+  if (!(v > 0.0)) return 0;
+  if (v >= 65520.0) return 0x7BFF;
+  int e;
+  frexp(v, &e);        // v = m 2^e, m in [0.5, 1): unbiased exponent e-1
+  int E = e - 1;
+  if (E < -14) E = -14;  // subnormal range shares the 2^-24 spacing
+  double ulp = ldexp(1.0, E - 10);
+  double r = rint(v / ulp) * ulp;  // exact scaling, rint rounds half to even
+  return __half_as_ushort(__float2half((float)r));  // r is an fp16 value: exact
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// number of codebook boundaries strictly below y/n (n > 0), as t_k * n < y
+__device__ __forceinline__ int cell_index(const Codebook &cb, float y, float n) {
+  int idx = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxCentroids - 1; ++k)
+    if (k < cb.L - 1) idx += (cb.t[k] * n < y) ? 1 : 0;
+  return idx;
+}
+
+__host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace tq

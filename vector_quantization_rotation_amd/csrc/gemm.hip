@@ -1,0 +1,421 @@
+// Rotations and projections as dense contractions on the fp32 matrix cores.
+//
+// One tiled kernel computes Z = A B^T (A: M x K, B: N x K, both read through
+// operand loaders) with v_mfma_f32_16x16x4_f32 and hands the 64 x 64 output
+// tile, staged in LDS, to an epilogue.  Loaders read dense fp32/bf16/fp16 rows
+// or dequantize packed records on the fly; epilogues store fp32, quantize and
+// pack index planes with wavefront ballots (Algorithm 1), or pack QJL sign bits
+// (Algorithm 2).  Algorithm steps as on the ai-navigate-news Gemma 4 post,
+// section "仕組み（技術的）".
+//
+// fp32 operands keep the rotated coordinates within ~1e-7 of their norm scale,
+// far inside the 1e-5 tie zone the codes are checked against.
+#include <algorithm>
+
+#include "common.cuh"
+
+namespace tq {
+
+constexpr int GBM = 64, GBN = 64, GBK = 16, GPAD = 16;
+
+// ----------------------------------------------------------------------------
+// operand loaders: fill v[0..3] with elements k..k+3 of row r (k % 4 == 0)
+// ----------------------------------------------------------------------------
+struct LoadF32 {
+  const float *p;
+  int64_t ld;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    float4 t = *reinterpret_cast<const float4 *>(p + r * ld + k);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
+
+struct LoadBF16 {
+  const uint16_t *p;
+  int64_t ld;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    uint2 t = *reinterpret_cast<const uint2 *>(p + r * ld + k);
+    v[0] = __uint_as_float(t.x << 16);
+    v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16);
+    v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+  }
+};
+
+struct LoadF16 {
+  const uint16_t *p;
+  int64_t ld;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    uint2 t = *reinterpret_cast<const uint2 *>(p + r * ld + k);
+    v[0] = f16_to_f32(t.x & 0xFFFF);
+    v[1] = f16_to_f32(t.x >> 16);
+    v[2] = f16_to_f32(t.y & 0xFFFF);
+    v[3] = f16_to_f32(t.y >> 16);
+  }
+};
+
+// rows [0, split) from a, rows [split, ...) from b (same row length ld)
+struct LoadRows2 {
+  const float *a, *b;
+  int64_t split, ld;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    const float *p = r < split ? a + r * ld : b + (r - split) * ld;
+    float4 t = *reinterpret_cast<const float4 *>(p + k);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
+
+// columns [0, split) from a, [split, 2 split) from b (both row length split)
+struct LoadCols2 {
+  const float *a, *b;
+  int split;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    const float *p = k < split ? a + r * split + k : b + r * split + (k - split);
+    float4 t = *reinterpret_cast<const float4 *>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
+
+// A record row dequantized to [n_hat c[idx] | qjl * gamma * (2 bit - 1)]
+// (the second half only for Algorithm-2 records).
+struct LoadDequant {
+  const uint8_t *codes;
+  const uint16_t *norms, *gammas;
+  int64_t code_bytes;
+  int d, bmse;
+  float qjl;
+  Codebook cb;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    const uint8_t *rec = codes + r * code_bytes;
+    const int sh = k & 7;
+    if (k < d) {
+      int idx[4] = {0, 0, 0, 0};
+      for (int p = 0; p < bmse; ++p) {
+        int byte = rec[p * (d >> 3) + (k >> 3)] >> sh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) idx[i] |= ((byte >> i) & 1) << p;
+      }
+      float nh = f16_to_f32(norms[r]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = cb.c[idx[i]] * nh;
+    } else {
+      int kk = k - d;
+      int byte = rec[bmse * (d >> 3) + (kk >> 3)] >> sh;
+      float g = qjl * f16_to_f32(gammas[r]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = ((byte >> i) & 1) ? g : -g;
+    }
+  }
+};
+
+typedef float CTile[GBN + 1];
+
+// ----------------------------------------------------------------------------
+// epilogues (run by all 256 threads with the tile in LDS)
+// ----------------------------------------------------------------------------
+struct EpiStore {
+  float *out;
+  int64_t ldo;
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    for (int e = threadIdx.x; e < GBM * GBN; e += 256) {
+      int r = e / GBN, c = e % GBN;
+      if (row0 + r < M && col0 + c < N) out[(row0 + r) * ldo + col0 + c] = Cs[r][c];
+    }
+  }
+};
+
+// Algorithm-1 index planes for 64 coordinates (one tile column block) per row.
+// For Algorithm 2 also the rotated residual y - n_hat c[idx] and its squared norm.
+struct EpiQuant {
+  uint8_t *codes;
+  int64_t code_bytes;
+  int d, bmse;
+  const float *n32;        // fp32 norms of the rows (chunk-relative)
+  const uint16_t *nhat;    // fp16 norms (chunk-relative)
+  float *resid;            // [rows, d] rotated residual, or null (Algorithm 1)
+  double *rsq;             // [rows] accumulated ||r||^2, or null
+  Codebook cb;
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = wave * 16 + rr;
+      const int64_t row = row0 + r;
+      if (row >= M) break;
+      float y = Cs[r][lane];
+      float n = n32[row];
+      float yq = y, nq = n;
+      if (n == 0.0f) { yq = 0.0f; nq = 1.0f; }
+      int idx = cell_index(cb, yq, nq);
+      uint8_t *dst = codes + row * code_bytes + (col0 >> 3);
+      for (int p = 0; p < bmse; ++p) {
+        unsigned long long m = __ballot(((idx >> p) & 1) != 0);
+        if (lane == 0) *reinterpret_cast<unsigned long long *>(dst + p * (d >> 3)) = m;
+      }
+      if (resid) {
+        float rv = y - f16_to_f32(nhat[row]) * cb.c[idx];
+        resid[row * d + col0 + lane] = rv;
+        double s = wave_sum_f64((double)rv * (double)rv);
+        if (lane == 0) atomicAdd(rsq + row, s);
+      }
+    }
+  }
+};
+
+// QJL sign plane: bit = [(S r)_i >= 0]
+struct EpiSign {
+  uint8_t *codes;
+  int64_t code_bytes;
+  int d, plane;
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = wave * 16 + rr;
+      const int64_t row = row0 + r;
+      if (row >= M) break;
+      unsigned long long m = __ballot(Cs[r][lane] >= 0.0f);
+      if (lane == 0)
+        *reinterpret_cast<unsigned long long *>(codes + row * code_bytes + plane * (d >> 3) + (col0 >> 3)) = m;
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// the tiled contraction
+// ----------------------------------------------------------------------------
+template <class LA, class LB, class EP>
+__global__ __launch_bounds__(256) void gemm_kernel(LA la, LB lb, EP ep, int64_t M, int64_t N, int K) {
+  __shared__ float As[GBK][GBM + GPAD];
+  __shared__ float Bs[GBK][GBN + GPAD];
+  __shared__ float Cs[GBM][GBN + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * GBM, col0 = (int64_t)blockIdx.y * GBN;
+  const int wm = wave >> 1, wn = wave & 1;
+  floatx4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int64_t ra = row0 + lr, rb = col0 + lr;
+  for (int k0 = 0; k0 < K; k0 += GBK) {
+    float va[4] = {0.f, 0.f, 0.f, 0.f}, vb[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ra < M) la(ra, k0 + lk, va);
+    if (rb < N) lb(rb, k0 + lk, vb);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      As[lk + i][lr] = va[i];
+      Bs[lk + i][lr] = vb[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kk = ks * 4 + (lane >> 4);
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = As[kk][wm * 32 + i * 16 + (lane & 15)];
+        b[i] = Bs[kk][wn * 32 + i * 16 + (lane & 15)];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Cs[wm * 32 + i * 16 + 4 * (lane >> 4) + e][wn * 32 + j * 16 + (lane & 15)] = acc[i][j][e];
+  __syncthreads();
+  ep(Cs, row0, col0, M, N);
+}
+
+template <class LA, class LB, class EP>
+static int gemm(const char *name, LA la, LB lb, EP ep, int64_t M, int64_t N, int K, hipStream_t st) {
+  if (M <= 0 || N <= 0) return TQ_OK;
+  dim3 grid((unsigned)cdiv64(M, GBM), (unsigned)cdiv64(N, GBN));
+  ProfScope ps(name, st);
+  hipLaunchKernelGGL((gemm_kernel<LA, LB, EP>), grid, dim3(256), 0, st, la, lb, ep, M, N, K);
+  return launch_check();
+}
+
+// ----------------------------------------------------------------------------
+// small kernels: norms, zero fill, gamma finalisation, M = S Pi^T
+// ----------------------------------------------------------------------------
+template <int XT>
+__global__ __launch_bounds__(256) void norm_kernel(const void *x, int64_t ldx, int d, int64_t n, uint16_t *nhat,
+                                                   float *n32) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  double s = 0.0;
+  for (int j = lane; j < d; j += 64) {
+    double v;
+    if (XT == TQ_F32) v = static_cast<const float *>(x)[row * ldx + j];
+    else if (XT == TQ_BF16) v = bf16_to_f32(static_cast<const uint16_t *>(x)[row * ldx + j]);
+    else v = f16_to_f32(static_cast<const uint16_t *>(x)[row * ldx + j]);
+    s += v * v;
+  }
+  s = wave_sum_f64(s);
+  if (lane == 0) {
+    double nn = sqrt(s);
+    nhat[row] = f64_to_f16_rne_sat(nn);
+    n32[row] = (float)nn;
+  }
+}
+
+__global__ void zero_f64_kernel(double *p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
+__global__ void gamma_kernel(const double *rsq, int64_t n, uint16_t *gam) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) gam[i] = f64_to_f16_rne_sat(sqrt(rsq[i]));
+}
+
+// m[i][j] = sum_k s[i][k] pi[j][k] in fp64, rounded to fp32
+__global__ void spit_kernel(int d, const float *s, const float *pi, float *m) {
+  int i = blockIdx.y, j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= d) return;
+  double acc = 0.0;
+  for (int k = 0; k < d; ++k) acc += (double)s[(int64_t)i * d + k] * (double)pi[(int64_t)j * d + k];
+  m[(int64_t)i * d + j] = (float)acc;
+}
+
+int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st) {
+  hipLaunchKernelGGL(spit_kernel, dim3((d + 127) / 128, d), dim3(128), 0, st, d, s, pi, m);
+  return launch_check();
+}
+
+// ----------------------------------------------------------------------------
+// encode / decode / score drivers
+// ----------------------------------------------------------------------------
+namespace {
+
+struct Scratch {
+  void *p = nullptr;
+  hipStream_t st;
+  explicit Scratch(hipStream_t s) : st(s) {}
+  int alloc(size_t bytes) {
+    hipError_t e = hipMallocAsync(&p, bytes, st);
+    if (e != hipSuccess) { p = nullptr; return hip_fail(e); }
+    return TQ_OK;
+  }
+  ~Scratch() { if (p) hipFreeAsync(p, st); }
+};
+
+template <class LX>
+int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ldx, int64_t cn, uint8_t *codes,
+                 uint16_t *norms, uint16_t *gammas, float *n32, float *resid, double *rsq, hipStream_t st) {
+  const int d = q->d;
+  int rc;
+  dim3 ng((unsigned)cdiv64(cn, 4));
+  {
+  ProfScope ps("encode_norm", st);
+  if (xt == TQ_F32) hipLaunchKernelGGL(norm_kernel<TQ_F32>, ng, dim3(256), 0, st, x, ldx, d, cn, norms, n32);
+  else if (xt == TQ_BF16) hipLaunchKernelGGL(norm_kernel<TQ_BF16>, ng, dim3(256), 0, st, x, ldx, d, cn, norms, n32);
+  else hipLaunchKernelGGL(norm_kernel<TQ_F16>, ng, dim3(256), 0, st, x, ldx, d, cn, norms, n32);
+  }
+  if ((rc = launch_check()) != TQ_OK) return rc;
+  const bool prod = q->mode == TQ_PROD;
+  if (prod) {
+    hipLaunchKernelGGL(zero_f64_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, cn);
+    if ((rc = launch_check()) != TQ_OK) return rc;
+  }
+  EpiQuant eq{codes, (int64_t)q->code_bytes, d, q->bmse, n32, norms, prod ? resid : nullptr, prod ? rsq : nullptr,
+              q->cb};
+  LoadF32 lpi{q->pi, d};
+  if ((rc = gemm("encode_rotate", lx, lpi, eq, cn, d, d, st)) != TQ_OK) return rc;
+  if (!prod) return TQ_OK;
+  LoadF32 lr{resid, d};
+  LoadF32 lm{q->m, d};
+  EpiSign es{codes, (int64_t)q->code_bytes, d, q->planes - 1};
+  if ((rc = gemm("encode_qjl", lr, lm, es, cn, d, d, st)) != TQ_OK) return rc;
+  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, cn, gammas);
+  return launch_check();
+}
+
+}  // namespace
+
+int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes, uint16_t *norms,
+               uint16_t *gammas, hipStream_t st) {
+  const int d = q->d;
+  const bool prod = q->mode == TQ_PROD;
+  const int64_t chunk = prod ? std::max<int64_t>(64, (int64_t(1) << 27) / d) : (int64_t(1) << 22);
+  const int64_t cmax = std::min(n, chunk);
+  size_t bytes = (size_t)cmax * 4 + 256;
+  if (prod) bytes += (size_t)cmax * d * 4 + (size_t)cmax * 8 + 256;
+  Scratch sc(st);
+  int rc = sc.alloc(bytes);
+  if (rc != TQ_OK) return rc;
+  char *base = static_cast<char *>(sc.p);
+  float *n32 = reinterpret_cast<float *>(base);
+  float *resid = nullptr;
+  double *rsq = nullptr;
+  if (prod) {
+    size_t off = ((size_t)cmax * 4 + 255) & ~(size_t)255;
+    resid = reinterpret_cast<float *>(base + off);
+    off += ((size_t)cmax * d * 4 + 255) & ~(size_t)255;
+    rsq = reinterpret_cast<double *>(base + off);
+  }
+  const size_t esz = xt == TQ_F32 ? 4 : 2;
+  for (int64_t r0 = 0; r0 < n; r0 += chunk) {
+    const int64_t cn = std::min(chunk, n - r0);
+    const void *xc = static_cast<const char *>(x) + (size_t)r0 * ldx * esz;
+    uint8_t *cc = codes + (size_t)r0 * q->code_bytes;
+    uint16_t *nc = norms + r0;
+    uint16_t *gc = gammas ? gammas + r0 : nullptr;
+    if (xt == TQ_F32) rc = encode_chunk(q, LoadF32{static_cast<const float *>(xc), ldx}, xc, xt, ldx, cn, cc, nc, gc, n32, resid, rsq, st);
+    else if (xt == TQ_BF16) rc = encode_chunk(q, LoadBF16{static_cast<const uint16_t *>(xc), ldx}, xc, xt, ldx, cn, cc, nc, gc, n32, resid, rsq, st);
+    else rc = encode_chunk(q, LoadF16{static_cast<const uint16_t *>(xc), ldx}, xc, xt, ldx, cn, cc, nc, gc, n32, resid, rsq, st);
+    if (rc != TQ_OK) return rc;
+  }
+  return TQ_OK;
+}
+
+int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas, int64_t n,
+               float *out, int64_t ldo, hipStream_t st) {
+  const int d = q->d;
+  const bool prod = q->mode == TQ_PROD;
+  LoadDequant ld{codes, norms, gammas, (int64_t)q->code_bytes, d, q->bmse, q->qjl_scale, q->cb};
+  LoadCols2 lb{q->piT, prod ? q->sT : q->piT, d};
+  EpiStore es{out, ldo};
+  return gemm("decode", ld, lb, es, n, d, prod ? 2 * d : d, st);
+}
+
+size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k) {
+  const int kq = q->mode == TQ_PROD ? 2 * q->d : q->d;
+  size_t b = (((size_t)m * kq * 4) + 255) & ~(size_t)255;
+  if (k > 0) b += (size_t)m * n * 4;
+  return b;
+}
+
+int run_topk(const float *scores, int64_t m, int64_t n, int k, float *vals, int64_t *idx, hipStream_t st);
+
+int run_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
+              const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx, void *ws,
+              size_t ws_bytes, hipStream_t st) {
+  const int d = q->d;
+  const bool prod = q->mode == TQ_PROD;
+  const int kq = prod ? 2 * d : d;
+  float *qrot = static_cast<float *>(ws);
+  int rc;
+  // rotated queries [Pi q | S q]
+  if ((rc = gemm("score_qrot", LoadF32{queries, ldq}, LoadRows2{q->pi, prod ? q->s : q->pi, d, d}, EpiStore{qrot, kq}, m, kq, d,
+                 st)) != TQ_OK)
+    return rc;
+  if (n == 0) return TQ_OK;
+  float *dst = scores;
+  if (k > 0) dst = reinterpret_cast<float *>(static_cast<char *>(ws) + ((((size_t)m * kq * 4) + 255) & ~(size_t)255));
+  LoadDequant lb{codes, norms, gammas, (int64_t)q->code_bytes, d, q->bmse, q->qjl_scale, q->cb};
+  if ((rc = gemm("score_scan", LoadF32{qrot, kq}, lb, EpiStore{dst, n}, m, n, kq, st)) != TQ_OK) return rc;
+  if (k == 0) return TQ_OK;
+  return run_topk(dst, m, n, k, scores, idx, st);
+}
+
+}  // namespace tq

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host entry points and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxCentroids = 16;  // 4-bit Algorithm-1 codebook at most
+
+// Codebook passed to kernels by value (kernel-argument memory).
+struct Codebook {
+  int L;                          // number of centroids (2^bmse)
+  float c[kMaxCentroids];         // ascending centroids (unit-sphere coordinate domain)
+  float t[kMaxCentroids - 1];     // boundaries (midpoints)
+};
+
+}  // namespace tq
+
+struct tq_quantizer {
+  int d;
+  int bits;        // bits per coordinate of a record (incl. the sign bit for TQ_PROD)
+  int mode;        // TQ_MSE / TQ_PROD
+  int bmse;        // bits of the Algorithm-1 index (bits or bits-1)
+  int planes;      // bit planes per record
+  size_t code_bytes;
+  int device;
+  double c64[tq::kMaxCentroids];
+  double t64[tq::kMaxCentroids - 1];
+  tq::Codebook cb;
+  float qjl_scale;  // sqrt(pi/2)/d
+  // device fp32 d*d row-major matrices
+  float *pi = nullptr;   // Pi
+  float *piT = nullptr;  // Pi^T
+  float *s = nullptr;    // S            (TQ_PROD)
+  float *sT = nullptr;   // S^T          (TQ_PROD)
+  float *m = nullptr;    // S Pi^T       (TQ_PROD): S r = M (Pi x - n_hat c[idx]) up to Pi's fp32 orthogonality
+};
+
+namespace tq {
+
+// optional event timing of launches (profile.cpp)
+bool profiling();
+void *prof_begin(const char *name, hipStream_t st);
+void prof_end(void *tok, hipStream_t st);
+struct ProfScope {
+  void *tok;
+  hipStream_t st;
+  ProfScope(const char *name, hipStream_t s) : tok(prof_begin(name, s)), st(s) {}
+  ~ProfScope() { prof_end(tok, st); }
+};
+
+// status helpers (tq_host.cpp)
+int hip_fail(hipError_t e);
+int launch_check();
+
+// kernel launchers (defined in the .hip files); all return a tq_status
+int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
+               uint16_t *norms, uint16_t *gammas, hipStream_t st);
+int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas,
+               int64_t n, float *out, int64_t ldo, hipStream_t st);
+size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
+int run_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
+              const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx,
+              void *ws, size_t ws_bytes, hipStream_t st);
+size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride);
+int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
+                    const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len,
+                    float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
+
+}  // namespace tq
