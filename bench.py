@@ -45,32 +45,6 @@ def parse():
     return ap.parse_args()
 
 
-def build_attention_cache(api, synth, torch, B, Hkv, T, d, seeds):
-    """Encode synthetic bf16 K/V into packed caches, one batch row at a time."""
-    piK = synth.haar_rotation(d, seeds["piK"])
-    piV = synth.haar_rotation(d, seeds["piV"])
-    sV = synth.gaussian_projection(d, seeds["sV"])
-    kq = api.Quantizer(d, 3, api.TQ_MSE, piK)
-    vq = api.Quantizer(d, 2, api.TQ_PROD, piV, sV)
-    dev = torch.device("cuda")
-    kcodes = torch.empty((B, Hkv, T, kq.code_bytes), dtype=torch.uint8, device=dev)
-    vcodes = torch.empty((B, Hkv, T, vq.code_bytes), dtype=torch.uint8, device=dev)
-    knorms = torch.empty((B, Hkv, T), dtype=torch.int16, device=dev)
-    vnorms = torch.empty((B, Hkv, T), dtype=torch.int16, device=dev)
-    vgam = torch.empty((B, Hkv, T), dtype=torch.int16, device=dev)
-    chans = synth.outlier_channels(Hkv, d, 4, seeds["chan"])
-    for b in range(B):
-        k = synth.kv_bf16_torch((1, Hkv, T, d), seeds["K"] * 1000 + b, chans, dev)
-        kq.encode(k.view(-1, d), codes=kcodes[b].view(-1, kq.code_bytes), norms=knorms[b].view(-1))
-        del k
-        v = synth.kv_bf16_torch((1, Hkv, T, d), seeds["V"] * 1000 + b, chans, dev)
-        vq.encode(v.view(-1, d), codes=vcodes[b].view(-1, vq.code_bytes), norms=vnorms[b].view(-1),
-                  gammas=vgam[b].view(-1))
-        del v
-    torch.cuda.synchronize()
-    return kq, vq, (piK, piV, sV), kcodes, knorms, vcodes, vnorms, vgam
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -88,22 +62,25 @@ def main():
     torch.cuda.set_device(0)
 
     # ---------------- decode attention (timed steps) ----------------
+    from vector_quantization_rotation_amd import workloads
     B, Hq, Hkv, d, T = 16, 32, 8, 128, 131072
-    seeds = {"K": 301, "V": 302, "chan": 303, "q": 304, "piK": 311, "piV": 312, "sV": 313}
     log("building compressed cache ...")
     t0 = time.time()
-    kq, vq, mats, kc, kn, vc, vn, vg = build_attention_cache(api, synth, torch, B, Hkv, T, d, seeds)
+    cache = workloads.build_attention_cache(B, Hq, Hkv, T, d)
     log(f"cache built in {time.time() - t0:.1f}s")
-    qh = synth.round_bf16(np.random.default_rng(seeds["q"]).standard_normal((B, Hq, d)).astype(np.float32))
-    q = torch.from_numpy(qh).cuda().to(torch.bfloat16)
+    kq, vq = cache.kq, cache.vq
+    kc, kn, vc, vn, vg, vt = cache.kcodes, cache.knorms, cache.vcodes, cache.vnorms, cache.vgammas, cache.vtiles
+    qh, q = cache.q_host, cache.q
+    mats = (cache.piK, cache.piV, cache.sV)
     seq = torch.full((B,), T, dtype=torch.int32, device="cuda")
     scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty((api.attn_decode_ws_bytes(kq, B, Hq, Hkv, T),), dtype=torch.uint8, device="cuda")
-    packed = (kc.numel() + kn.numel() * 2 + vc.numel() + vn.numel() * 2 + vg.numel() * 2)
+    layout = api.TQ_LAYOUT_TILE32
+    ws = torch.empty((api.attn_decode_ws_bytes(kq, B, Hq, Hkv, T, layout),), dtype=torch.uint8, device="cuda")
+    packed = cache.packed_bytes()
 
     def step():
-        api.attn_decode(kq, vq, q, kc, kn, vc, vn, vg, seq, scale, out=out, ws=ws)
+        api.attn_decode(kq, vq, q, kc, kn, vt, vn, vg, seq, scale, out=out, ws=ws, vlayout=layout)
 
     for _ in range(args.warmup):
         step()
@@ -212,11 +189,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i8 matrix cores on bit planes, i32 accumulate, f32 softmax",
         "data": "synthetic",
         "config": {"workload": "decode attention over a TurboQuant-packed KV cache",
                    "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "seq_len": T,
                    "key_bits_mse": 3, "value_bits_prod": 2, "query_dtype": "bf16",
+                   "value_layout": "token-tiled (32 tokens per word)",
                    "packed_bytes": int(packed), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

@@ -62,6 +62,14 @@ typedef enum {
 
 typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_mode;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+/* Arrangement of a sequence of records in memory.
+ *   TQ_LAYOUT_ROWS  : one record after another ([T][code_bytes]).
+ *   TQ_LAYOUT_TILE32: token-tiled, bit-transposed: tokens are grouped in tiles
+ *     of 32; tile k of a sequence holds planes * d uint32 words, word
+ *     [k][p][j] has bit i = bit j of plane p of token 32k + i (bits of tokens
+ *     past the sequence length are zero).  The same bits as the row layout,
+ *     arranged so that a contraction over tokens reads whole words. */
+typedef enum { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_TILE32 = 1 } tq_layout;
 
 typedef struct tq_quantizer tq_quantizer; /* opaque */
 
@@ -138,6 +146,13 @@ int tq_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq
              void *ws, size_t ws_bytes, void *stream);
 size_t tq_score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
 
+/* Rearrange nseq sequences of T row-layout records into TQ_LAYOUT_TILE32.
+ *   codes: device [nseq][T][code_bytes] (16-byte aligned)
+ *   tiles: device [nseq][ceil(T/32)][planes][d] uint32 (every word written)
+ * Bits of token slots T..32*ceil(T/32)-1 are written as zero. */
+int tq_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
+                    void *stream);
+
 /* Decode attention of one new query token per sequence against a compressed
  * cache: keys through Algorithm 1 (kq, TQ_MSE), values through Algorithm 2
  * (vq, TQ_PROD), as the ai-navigate-news Gemma 4 post assigns them (section
@@ -147,16 +162,21 @@ size_t tq_score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
  * where K~, V~ are the decodes of the records.
  *   q:       device [B, Hq, d] of type qt (TQ_F32, TQ_BF16 or TQ_F16)
  *   kcodes:  device [B, Hkv, Tstride, kcode_bytes], knorms [B, Hkv, Tstride]
- *   vcodes:  device [B, Hkv, Tstride, vcode_bytes], vnorms, vgammas [B, Hkv, Tstride]
+ *   vcodes:  device, value records in layout `vlayout`:
+ *            TQ_LAYOUT_ROWS   [B, Hkv, Tstride, vcode_bytes]
+ *            TQ_LAYOUT_TILE32 [B, Hkv, ceil(Tstride/32), planes, d] uint32 words
+ *            (the fast int8 matrix-core kernel; d in {128, 256}, key bits
+ *            with 2^(kbits-1) * d/64 <= 16; other shapes TQ_ERR_UNSUPPORTED)
+ *   vnorms, vgammas: device [B, Hkv, Tstride]
  *   seq_len: device [B] int32, 0 <= seq_len[b] <= Tstride
  *   out:     device [B, Hq, d] fp32
  *   ws:      device workspace of at least tq_attn_decode_ws_bytes(...) bytes
  * kq and vq must share d; Hq % Hkv == 0. */
 int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
-                   const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len,
-                   float scale, float *out, void *ws, size_t ws_bytes, void *stream);
-size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride);
+                   const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
+                   const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout);
 
 /* Optional per-kernel timing.  When enabled, the library records a pair of
  * HIP events on the launch stream around every kernel it launches (a few

@@ -23,7 +23,7 @@ it: both sides receive the same seeded inputs and nothing else.
 from .codebook import coord_density, coord_tail, lloyd_max, gaussian_lloyd_max  # noqa: F401
 from .quantizer import (  # noqa: F401
     fp16_rne_sat, encode_mse, decode_mse, encode_prod, decode_prod, pack_planes,
-    unpack_planes, mse_record, prod_record, parse_mse_record, parse_prod_record,
+    unpack_planes, tile_records, mse_record, prod_record, parse_mse_record, parse_prod_record,
     inner_product_estimate, qjl_scale, code_margins, sign_margins, fp16_midpoint_margin,
 )
 from .attention import decode_attention  # noqa: F401

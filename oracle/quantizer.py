@@ -158,6 +158,26 @@ def parse_prod_record(codes, d: int, bits: int):
     return idx, planes[-1]
 
 
+def tile_records(codes, d: int, nplanes: int) -> np.ndarray:
+    """Token-tiled layout of T row records: [ceil(T/32), nplanes, d] uint32.
+
+    Word [k][p][j] has bit i equal to bit j of plane p of record 32k + i
+    (zero past the last record).  The same bits as the rows, transposed per
+    32-record tile.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    T = codes.shape[0]
+    nt = (T + 31) // 32
+    bits = np.zeros((nt * 32, nplanes, d), dtype=np.uint64)
+    for p, pl in enumerate(unpack_planes(codes, d, nplanes)):
+        bits[:T, p, :] = pl
+    bits = bits.reshape(nt, 32, nplanes, d)
+    words = np.zeros((nt, nplanes, d), dtype=np.uint64)
+    for i in range(32):
+        words |= bits[:, i] << np.uint64(i)
+    return words.astype(np.uint32)
+
+
 # --------------------------------------------------------------------------
 # inner-product estimate (plain form: <q, decode(x)>)
 # --------------------------------------------------------------------------

@@ -163,7 +163,7 @@ def test_score_topk_ties_to_lower_index(api):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
-def _attn_case(api, B, Hq, Hkv, T, d, seq, qdtype, seed=0):
+def _attn_case(api, B, Hq, Hkv, T, d, seq, qdtype, seed=0, layout=0, kbits=3, vbits=2):
     rng = np.random.default_rng(seed)
     chans = synth.outlier_channels(Hkv, d, 4, seed + 1)
     K = synth.bf16_bits_to_f32(synth.kv_bf16((B, Hkv, T, d), seed + 2, chans))
@@ -172,18 +172,21 @@ def _attn_case(api, B, Hq, Hkv, T, d, seq, qdtype, seed=0):
     if qdtype == "bf16":
         q = synth.round_bf16(q)
     piK, piV, sV = synth.haar_rotation(d, seed + 4), synth.haar_rotation(d, seed + 5), synth.gaussian_projection(d, seed + 6)
-    kq = api.Quantizer(d, 3, api.TQ_MSE, piK)
-    vq = api.Quantizer(d, 2, api.TQ_PROD, piV, sV)
+    kq = api.Quantizer(d, kbits, api.TQ_MSE, piK)
+    vq = api.Quantizer(d, vbits, api.TQ_PROD, piV, sV)
     kc, kn, _ = kq.encode(_dev(K.reshape(-1, d)))
     vc, vn, vg = vq.encode(_dev(V.reshape(-1, d)))
     qt = _dev(q) if qdtype == "f32" else _dev(q).to(torch.bfloat16)
     seq_t = torch.tensor(seq, dtype=torch.int32, device="cuda")
-    out = api.attn_decode(kq, vq, qt, kc.view(B, Hkv, T, -1), kn.view(B, Hkv, T), vc.view(B, Hkv, T, -1),
-                          vn.view(B, Hkv, T), vg.view(B, Hkv, T), seq_t, 1.0 / math.sqrt(d)).cpu().numpy()
-    cK, _ = oracle.lloyd_max(d, 3)
-    cV, _ = oracle.lloyd_max(d, 1)
-    kidx = oracle.parse_mse_record(kc.cpu().numpy(), d, 3)
-    vidx, vsb = oracle.parse_prod_record(vc.cpu().numpy(), d, 2)
+    vsrc = vc.view(B, Hkv, T, -1)
+    if layout == api.TQ_LAYOUT_TILE32:
+        vsrc = api.tile_records(vq, vc.view(B * Hkv, T, -1)).view(B, Hkv, -1, vq.planes, d)
+    out = api.attn_decode(kq, vq, qt, kc.view(B, Hkv, T, -1), kn.view(B, Hkv, T), vsrc,
+                          vn.view(B, Hkv, T), vg.view(B, Hkv, T), seq_t, 1.0 / math.sqrt(d), vlayout=layout).cpu().numpy()
+    cK, _ = oracle.lloyd_max(d, kbits)
+    cV, _ = oracle.lloyd_max(d, vbits - 1)
+    kidx = oracle.parse_mse_record(kc.cpu().numpy(), d, kbits)
+    vidx, vsb = oracle.parse_prod_record(vc.cpu().numpy(), d, vbits)
     Kt = oracle.decode_mse(kidx, parity.f16_from_bits(kn.cpu().numpy()), piK, cK).reshape(B, Hkv, T, d)
     Vt = oracle.decode_prod(vidx, parity.f16_from_bits(vn.cpu().numpy()), vsb, parity.f16_from_bits(vg.cpu().numpy()),
                             piV, sV, cV).reshape(B, Hkv, T, d)
@@ -200,6 +203,44 @@ def test_attn_decode_parity(api, B, Hq, Hkv, T, seq):
             continue
         err = parity.rel_rows(out[b], ref[b])
         assert np.all(err <= parity.RTOL), (b, err.max())
+
+
+ATTN_FAST_CASES = [
+    # (B, Hq, Hkv, T, seq, d, kbits, vbits)
+    (2, 8, 2, 300, [300, 137], 128, 3, 2),
+    (1, 4, 4, 64, [1], 128, 3, 2),
+    (3, 32, 8, 520, [520, 0, 33], 128, 3, 2),
+    (2, 16, 2, 1100, [1100, 700], 128, 3, 2),   # 8 heads per kv head: two head groups
+    (1, 6, 2, 777, [777], 128, 3, 2),           # 3 heads per kv head: partial head group
+    (2, 8, 4, 513, [513, 256], 128, 2, 3),
+    (1, 4, 1, 400, [399], 128, 4, 2),
+    (1, 4, 1, 333, [333], 128, 1, 2),
+    (2, 32, 16, 1024, [1024, 1000], 256, 3, 2),  # local-layer shape
+    (1, 8, 2, 20000, [19999], 128, 3, 2),        # long sequence: many sub-chunks per work-group
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,seq,d,kb,vb", ATTN_FAST_CASES)
+def test_attn_decode_tiled_parity(api, B, Hq, Hkv, T, seq, d, kb, vb):
+    out, ref = _attn_case(api, B, Hq, Hkv, T, d, seq, "bf16", seed=5, layout=api.TQ_LAYOUT_TILE32, kbits=kb, vbits=vb)
+    for b in range(B):
+        if seq[b] == 0:
+            assert np.all(out[b] == 0)
+            continue
+        err = parity.rel_rows(out[b], ref[b])
+        assert np.all(err <= parity.RTOL), (b, err.max())
+        print(f"tiled attention case b={b}: max rel err {err.max():.2e}")
+
+
+def test_tile_records_matches_oracle(api):
+    d, T = 128, 100
+    x = synth.unit_test_vectors(3 * T, d, 51, 52)
+    vq = api.Quantizer(d, 2, api.TQ_PROD, synth.haar_rotation(d, 53), synth.gaussian_projection(d, 54))
+    codes, _, _ = vq.encode(_dev(x))
+    tiles = api.tile_records(vq, codes.view(3, T, -1)).cpu().numpy().view(np.uint32)
+    c = codes.cpu().numpy().reshape(3, T, -1)
+    for sq in range(3):
+        assert np.array_equal(tiles[sq], oracle.tile_records(c[sq], d, 2))
 
 
 def test_encode_zero_and_empty(api):

@@ -83,8 +83,9 @@ def test_entry_points_reject_null_quantizer():
     assert lib.tq_encode_prod(z, z, 0, 1, 128, z, z, z, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_decode(z, z, z, z, 1, z, 128, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_score(z, z, 1, 128, z, z, z, 1, 0, z, z, z, 0, z) == _lib.TQ_ERR_INVALID
-    assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
-    assert lib.tq_attn_decode_ws_bytes(z, 1, 4, 1, 16) == 0
+    assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_decode_ws_bytes(z, 1, 4, 1, 16, 0) == 0
+    assert lib.tq_tile_records(z, z, 1, 32, z, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_score_ws_bytes(z, 1, 1, 0) == 0
     assert lib.tq_quantizer_info(z, None, None, None, None, None) == _lib.TQ_ERR_INVALID
     lib.tq_quantizer_destroy(z)  # no-op on null

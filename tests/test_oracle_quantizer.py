@@ -199,3 +199,29 @@ def test_margins_helpers():
     assert sm.shape == (16, d) and np.all(sm >= 0)
     mm = oracle.fp16_midpoint_margin(np.array([1.0 + 2.0 ** -11, 1.0]))
     assert mm[0] == 0.0 and mm[1] == pytest.approx(2.0 ** -11)
+
+
+def test_tile_layout_hand_example():
+    # 33 records of d = 8, 1 plane: record t has only bit (t % 8) set
+    codes = np.array([[1 << (t % 8)] for t in range(33)], dtype=np.uint8)
+    w = oracle.tile_records(codes, 8, 1)
+    assert w.shape == (2, 1, 8)
+    # tile 0, coordinate j: bit i set iff i % 8 == j
+    for j in range(8):
+        assert w[0, 0, j] == sum(1 << i for i in range(32) if i % 8 == j)
+    # tile 1 holds record 32 only (bit 0 -> coordinate 0), the rest is zero
+    assert w[1, 0, 0] == 1 and np.all(w[1, 0, 1:] == 0)
+
+
+def test_tile_layout_roundtrip():
+    rng = np.random.default_rng(3)
+    d, P, T = 64, 3, 70
+    codes = rng.integers(0, 256, size=(T, P * d // 8), dtype=np.uint8)
+    w = oracle.tile_records(codes, d, P)
+    back = np.zeros((w.shape[0] * 32, P, d), dtype=np.uint8)
+    for i in range(32):
+        back.reshape(w.shape[0], 32, P, d)[:, i] = (w >> np.uint32(i)) & 1
+    planes = oracle.unpack_planes(codes, d, P)
+    for p in range(P):
+        assert np.array_equal(back[:T, p], planes[p])
+    assert np.all(back[T:] == 0)

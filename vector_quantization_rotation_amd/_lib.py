@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libtq.so")
 TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP, TQ_ERR_NOMEM, TQ_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_LAYOUT_ROWS, TQ_LAYOUT_TILE32 = 0, 1
 
 # (name, restype, argtypes) for every symbol declared in include/tq.h
 _P, _I, _I64, _SZ, _F, _D = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_float, C.c_double
@@ -30,8 +31,9 @@ SIGNATURES = [
     ("tq_decode", _I, [_P, _P, _P, _P, _I64, _P, _I64, _P]),
     ("tq_score", _I, [_P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _P, _SZ, _P]),
     ("tq_score_ws_bytes", _SZ, [_P, _I64, _I64, _I]),
-    ("tq_attn_decode", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _P, _F, _P, _P, _SZ, _P]),
-    ("tq_attn_decode_ws_bytes", _SZ, [_P, _I, _I, _I, _I64]),
+    ("tq_tile_records", _I, [_P, _P, _I64, _I64, _P, _P]),
+    ("tq_attn_decode", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ, _P]),
+    ("tq_attn_decode_ws_bytes", _SZ, [_P, _I, _I, _I, _I64, _I]),
     ("tq_profile_enable", _I, [_I]),
     ("tq_profile_query", _I, [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     ("tq_profile_reset", _I, []),

@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import TQ_BF16, TQ_F16, TQ_F32, TQ_MSE, TQ_PROD, TQError, codebook_build, load  # noqa: F401
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_LAYOUT_ROWS, TQ_LAYOUT_TILE32, TQ_MSE, TQ_PROD,  # noqa: F401
+                   TQError, codebook_build, load)
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
 
@@ -118,23 +119,34 @@ class Quantizer:
         return scores if k == 0 else (scores, idx)
 
 
-def attn_decode_ws_bytes(kq: Quantizer, B: int, Hq: int, Hkv: int, Tstride: int) -> int:
-    return load().tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride)
+def tile_records(q: Quantizer, codes: torch.Tensor, out=None):
+    """Row-layout records [nseq, T, code_bytes] -> TQ_LAYOUT_TILE32 words [nseq, ceil(T/32), planes, d] (int32)."""
+    nseq, T = codes.shape[0], codes.shape[1]
+    ntile = (T + 31) // 32
+    if out is None:
+        out = torch.empty((nseq, ntile, q.planes, q.d), dtype=torch.int32, device=codes.device)
+    rc = load().tq_tile_records(q.handle, _ptr(codes), nseq, T, _ptr(out), _stream())
+    _lib._check("tq_tile_records", rc)
+    return out
+
+
+def attn_decode_ws_bytes(kq: Quantizer, B: int, Hq: int, Hkv: int, Tstride: int, vlayout: int = TQ_LAYOUT_ROWS) -> int:
+    return load().tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
 
 
 def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
-                seq_len: torch.Tensor, scale: float, out=None, ws=None):
-    """q [B, Hq, d]; caches [B, Hkv, Tstride, ...]; seq_len int32 [B] -> out [B, Hq, d] fp32."""
+                seq_len: torch.Tensor, scale: float, out=None, ws=None, vlayout: int = TQ_LAYOUT_ROWS):
+    """q [B, Hq, d]; key caches [B, Hkv, Tstride, ...]; value records in `vlayout`; -> out [B, Hq, d] fp32."""
     lib = load()
     B, Hq, d = q.shape
     Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    ws_b = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride)
+    ws_b = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
     if ws is None:
         ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=q.device)
     rc = lib.tq_attn_decode(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms),
-                            _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), Tstride, _ptr(seq_len), float(scale),
+                            _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), float(scale),
                             _ptr(out), _ptr(ws), ws.numel(), _stream())
     _lib._check("tq_attn_decode", rc)
     return out

@@ -198,7 +198,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *part, in
   }
 }
 
-size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride) {
+int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *out,
+                 hipStream_t st) {
+  ProfScope ps("attn_combine", st);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(BH), dim3(256), 2 * (size_t)d * 4, st, part, nsplit, d, piT, sT, out);
+  return launch_check();
+}
+
+size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T);
+int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
+                  const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
+                  const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
+                  void *ws, hipStream_t st);
+
+size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout) {
+  if (vlayout == TQ_LAYOUT_TILE32) return attn_fast_ws_bytes(kq->d, kq->bits, B, Hq, Hkv, Tstride);
   const int d = kq->d;
   AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
   size_t qb = ((size_t)B * Hq * d * 4 + 255) & ~(size_t)255;
@@ -219,8 +233,11 @@ static void launch_split(const AttnPlan &p, dim3 grid, hipStream_t st, const flo
 
 int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                     const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
-                    const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                    void *ws, size_t ws_bytes, hipStream_t st) {
+                    const uint16_t *vgammas, int vlayout, int64_t Tstride, const int32_t *seq_len, float scale,
+                    float *out, void *ws, size_t ws_bytes, hipStream_t st) {
+  if (vlayout == TQ_LAYOUT_TILE32)
+    return run_attn_fast(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, reinterpret_cast<const uint32_t *>(vcodes), vnorms,
+                         vgammas, Tstride, seq_len, scale, out, ws, st);
   const int d = kq->d;
   AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
   if (!p.CP) return TQ_ERR_UNSUPPORTED;
@@ -250,10 +267,7 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   }
   }
   if ((rc = launch_check()) != TQ_OK) return rc;
-  ProfScope ps("attn_combine", st);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(256), 2 * (size_t)d * 4, st, part, p.nsplit, d, vq->piT,
-                     vq->sT, out);
-  return launch_check();
+  return attn_combine(part, B * Hq, p.nsplit, d, vq->piT, vq->sT, out, st);
 }
 
 }  // namespace tq

@@ -301,28 +301,40 @@ int tq_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq
                        (hipStream_t)stream);
 }
 
-size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride) {
+size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout) {
   if (!kq || B < 0 || Hq <= 0 || Hkv <= 0 || Tstride < 0) return 0;
-  return tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride);
+  if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return 0;
+  return tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride, vlayout);
+}
+
+int tq_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
+                    void *stream) {
+  if (!q || nseq < 0 || T < 0) return TQ_ERR_INVALID;
+  if (nseq == 0 || T == 0) return TQ_OK;
+  if (!codes || !tiles || !aligned16(codes) || !aligned16(tiles)) return TQ_ERR_INVALID;
+  if (nseq > 65535) return TQ_ERR_UNSUPPORTED;
+  return tq::run_tile_records(q, codes, nseq, T, tiles, (hipStream_t)stream);
 }
 
 int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                    const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
-                   const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                   void *ws, size_t ws_bytes, void *stream) {
+                   const uint16_t *vgammas, int vlayout, int64_t Tstride, const int32_t *seq_len, float scale,
+                   float *out, void *ws, size_t ws_bytes, void *stream) {
   if (!kq || !vq || kq->mode != TQ_MSE || vq->mode != TQ_PROD || kq->d != vq->d) return TQ_ERR_INVALID;
   if (kq->device != vq->device) return TQ_ERR_INVALID;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tstride < 0 || !valid_dtype(qt)) return TQ_ERR_INVALID;
+  if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return TQ_ERR_INVALID;
+  if ((int64_t)B * Hq > 2147483647 / 2 || (int64_t)B * Hkv * ((Hq / Hkv + 3) / 4) > 2147483647) return TQ_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return TQ_ERR_INVALID;
   if (B == 0) return TQ_OK;
   if (!q || !out || !seq_len) return TQ_ERR_INVALID;
   if (Tstride > 0 && (!kcodes || !knorms || !vcodes || !vnorms || !vgammas)) return TQ_ERR_INVALID;
   if ((Tstride > 0 && (!aligned16(kcodes) || !aligned16(vcodes))) || !aligned16(out) || !aligned16(q))
     return TQ_ERR_INVALID;
-  size_t need = tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride);
+  size_t need = tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride, vlayout);
   if (need > 0 && (!ws || ws_bytes < need)) return TQ_ERR_WORKSPACE;
-  return tq::run_attn_decode(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len,
-                             scale, out, ws, ws_bytes, (hipStream_t)stream);
+  return tq::run_attn_decode(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, vcodes, vnorms, vgammas, vlayout, Tstride,
+                             seq_len, scale, out, ws, ws_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -66,11 +66,13 @@ size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
 int run_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
               const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx,
               void *ws, size_t ws_bytes, hipStream_t st);
-size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride);
+size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout);
 int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
                     int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
-                    const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len,
-                    float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+                    const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
+                    const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
+                     hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
 
 }  // namespace tq
