@@ -216,7 +216,9 @@ ATTN_FAST_CASES = [
     (1, 4, 1, 400, [399], 128, 4, 2),
     (1, 4, 1, 333, [333], 128, 1, 2),
     (2, 32, 16, 1024, [1024, 1000], 256, 3, 2),  # local-layer shape
-    (1, 8, 2, 20000, [19999], 128, 3, 2),        # long sequence: many sub-chunks per work-group
+    (1, 8, 2, 20000, [19999], 128, 3, 2),        # long sequence: many steps per work-group
+    (1, 4, 4, 64, [2], 128, 3, 2),               # the largest weight maps to the top int8 digit
+    (2, 8, 8, 64, [1, 1], 128, 3, 2),            # one token: output is that token's value
 ]
 
 

@@ -81,10 +81,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   const int bg = unit / nsub;
   const int g = bg % Hkv, b = bg / Hkv;
   const int h0 = g * G + sub * GW;
-  const int gw = min(GW, G - sub * GW);
+  const int gw = imin32(GW, G - sub * GW);
   const int64_t T = seq_len[b];
   const int64_t t0 = (int64_t)split * chunk;
-  const int64_t t1 = min<int64_t>(T, t0 + chunk);
+  const int64_t t1 = imin64(T, t0 + chunk);
 
   float qv[GW][CP];
 #pragma unroll

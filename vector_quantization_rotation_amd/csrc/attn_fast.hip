@@ -15,15 +15,15 @@
 //   holds four bits as bytes of value 2^k (k = 7 reads as -128); the 2^-k (and
 //   the sign for k = 7) is folded into the other operand.
 // * The other operand (query or softmax weights) is split into four int8
-//   terms (a1 + a2/2^7 + a3/2^14 + a4/2^21), one per MFMA row of a head, so
-//   integer accumulation is exact and the only rounding is the split itself.
+//   digits of 7 bits each, one per MFMA row of a head, so integer
+//   accumulation is exact and the only rounding is the split itself.
 // * Keys stay in per-token records (their bits run along the contraction).
 //   Values are read from the token-tiled layout (32 tokens per word) so that
 //   the contraction over tokens also runs along the word bits.
-// * Each work-group owns a (batch, kv-head, head group, sequence chunk); inside,
-//   sub-chunks of 256 tokens are scored (pass K), their softmax weights split
-//   to int8 in LDS, then aggregated (pass V) and folded into fp32 accumulators
-//   with the running maximum (online softmax across sub-chunks).
+// * Each work-group owns a (batch, kv-head, head group, sequence chunk) and
+//   walks it in 256-token steps: score (key pass), turn the scores into int8
+//   weight digits in LDS, aggregate (value pass); online softmax with a
+//   rarely-moving reference maximum.
 #include <algorithm>
 
 #include "common.cuh"
@@ -31,7 +31,7 @@
 namespace tq {
 
 constexpr int FA_THREADS = 256;
-constexpr int FA_SUB = 256;     // tokens per sub-chunk
+constexpr int FA_SUB = 256;     // chunk granularity: 4 waves x 64-token steps
 constexpr int FA_GMAX = 4;      // query heads per work-group (16 MFMA rows = 4 heads x 4 splits)
 
 struct FastAttnArgs {
@@ -86,87 +86,178 @@ __device__ __forceinline__ float rows16_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// value B operand: four registers of one tile word for token bits kofs..kofs+3
+// of every byte.  Byte values are 2^k'(k) with k' = k except k = 3, 7 -> k - 1
+// (the top bit of a byte is shifted down so every byte stays non-negative).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ intx4 value_bits(uint32_t w, int kofs) {
+  intx4 r;
+  r[0] = (int)(w & (0x01010101u << kofs));
+  r[1] = (int)(w & (0x02020202u << kofs));
+  r[2] = (int)(w & (0x04040404u << kofs));
+  r[3] = (int)((w >> 1) & (0x04040404u << kofs));
+  return r;
+}
+// raw buffer descriptor from wave-uniform values (forced into scalar registers)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)imin64(bytes, 0x7FFFFFFF));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ int value_kexp(int kbit) { return ((kbit & 3) == 3) ? kbit - 1 : kbit; }
+
+// prefetch helpers (descriptors by value so they stay in scalar registers)
+template <int D, int KB>
+__device__ __forceinline__ void fa_load_keys(uint32_t (&kw)[4][KB * (D / 128)], __amdgpu_buffer_rsrc_t rk, int vo,
+                                             int so) {
+  constexpr int KCB = KB * D / 8;
+  so = __builtin_amdgcn_readfirstlane(so);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+    for (int p = 0; p < KB; ++p)
+#pragma unroll
+      for (int wb = 0; wb < D / 128; ++wb)
+        kw[grp][p * (D / 128) + wb] =
+            __builtin_amdgcn_raw_buffer_load_b32(rk, vo + grp * 16 * KCB + p * (D / 8) + wb * 16, so, 0);
+}
+
+__device__ __forceinline__ void fa_load_norms(uint32_t &nk, uint32_t &nv, uint32_t &ng, __amdgpu_buffer_rsrc_t rkn,
+                                              __amdgpu_buffer_rsrc_t rvn, __amdgpu_buffer_rsrc_t rvg, int vo, int so) {
+  so = __builtin_amdgcn_readfirstlane(so);
+  nk = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo, so, 0);
+  nv = __builtin_amdgcn_raw_buffer_load_b16(rvn, vo, so, 0);
+  ng = __builtin_amdgcn_raw_buffer_load_b16(rvg, vo, so, 0);
+}
+
+template <int D, int VB>
+__device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1], __amdgpu_buffer_rsrc_t rv, int vo,
+                                               int so) {
+  constexpr int VPL = VB + 1;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int st = __builtin_amdgcn_readfirstlane(so + tt * 2 * VPL * D * 4);
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+      for (int p = 0; p < VPL; ++p) vw[tt][c][p] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo + (p * D + c * 16) * 4, st, 0);
+  }
+}
+
 // D: head dim; KB: key index bits; VB: value index bits (Algorithm-2 records hold VB+1 planes)
+//
+// Work-group = 4 waves over one (batch, kv head, head group, sequence chunk),
+// walked in steps of 256 tokens.  In a step wave w scores tokens 64w..64w+63
+// (all heads), writes their int8 weight digits to LDS, and after a barrier
+// aggregates all 256 tokens for its quarter of the value columns.  The next
+// step's key words, norms and value words are loaded while the current step
+// runs.  Softmax weights are scaled by a reference (running maximum, largest
+// value norm and gamma) that moves only when a step exceeds it; the int32
+// accumulators are folded into fp32 then.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
   constexpr int KP = walsh_count(KB);        // key Walsh planes
   constexpr int VMP = walsh_count(VB);       // value Walsh planes (index part)
   constexpr int VPL = VB + 1;                // stored value planes per tile
   constexpr int KW = D / 32;                 // 32-bit words per key plane
+  constexpr int KWL = KB * (D / 128);        // key words per lane per 16-token group
   constexpr int NINS = KP * (D / 128) * 2;   // key-side MFMAs per 16 tokens
-  constexpr int NT = D / 16;                 // value column tiles
-  constexpr int NT_W = NT / 4;               // column tiles per wave
+  constexpr int NTW = D / 64;                // value column tiles per wave
   constexpr int KCB = KB * D / 8;            // key record bytes
+  constexpr float WMAX = 268435328.f;        // 2^28 - 128: largest fp32 whose top 7-bit digit is 127
 
-  __shared__ float s_sc[FA_GMAX][FA_SUB];
-  __shared__ float s_vn[FA_SUB], s_vg[FA_SUB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][FA_SUB / 64][16][64];  // int8 weight operands
-  __shared__ float s_red[4][FA_GMAX][4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][4][16][64];  // weight digits [plane][token tile][row][slot]
+  __shared__ float s_norm[4][2][64];                                   // per wave: n_V, gamma_V of its tokens
+  __shared__ float s_kn[4][64];                                        // per wave: n_K
+  __shared__ float s_max[4][FA_GMAX + 2];                              // per wave: score max per head, n_V max, gamma max
+  __shared__ float s_merge[4][FA_GMAX][3];                             // per wave and head: l, Ym, Yq
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, split = blockIdx.y;
   const int sub = unit % a.nsub, bg = unit / a.nsub;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
-  const int gw = min(FA_GMAX, a.G - sub * FA_GMAX);
-  const int64_t T = min<int64_t>(max<int64_t>(a.seq_len[b], 0), a.Tstride);
-  const int64_t c0 = (int64_t)split * a.chunk;
-  const int64_t c1 = min<int64_t>(T, c0 + a.chunk);
+  const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
+  // sequence length is wave-uniform: keep it (and everything derived) in scalar registers
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0), a.Tstride);
   const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = imin64(T, c0 + a.chunk);
 
-  // query operand image (constant over the chunk)
+  const int hl = lane >> 4;      // head owned by this lane in score / accumulator layouts
+  const int ln = lane & 15;      // token (score layout) or column (value layout) within 16
+  const int kofs = (hl & 1) * 4; // value operand: token-bit offset of this lane group
+  const bool head_ok = hl < gw;
+
   intx4 qa[NINS];
   {
     const intx4 *img = reinterpret_cast<const intx4 *>(a.qimg) + (int64_t)unit * NINS * 64;
 #pragma unroll
     for (int i = 0; i < NINS; ++i) qa[i] = img[i * 64 + lane];
   }
-  const int hl = lane >> 4;  // head owned by this lane in score/accumulator layouts
   const float qinv = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0];
   const float qconst = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1];
 
-  // zero the weight operand tiles once: unused rows stay zero
+  // rows of heads >= gw stay zero for the whole chunk
   for (int i = tid; i < (int)sizeof(s_w) / 4; i += FA_THREADS) reinterpret_cast<uint32_t *>(&s_w[0][0][0][0])[i] = 0u;
 
-  // per-lane constants for the value B operand: k offset 0 or 4 by lane group parity
-  const int kofs = ((lane >> 4) & 1) * 4;
-  // fp32 accumulators: [plane (VMP mse + 1 sign)][column tile of this wave][split-combined]
-  float acc[VMP + 1][NT_W];
+  // buffer descriptors over this sequence (scalar registers); reads past the chunk end return 0
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.kcodes + seq * a.Tstride * KCB, c1 * KCB);
+  const __amdgpu_buffer_rsrc_t rkn = uniform_rsrc(a.knorms + seq * a.Tstride, c1 * 2);
+  const __amdgpu_buffer_rsrc_t rvn = uniform_rsrc(a.vnorms + seq * a.Tstride, c1 * 2);
+  const __amdgpu_buffer_rsrc_t rvg = uniform_rsrc(a.vgammas + seq * a.Tstride, c1 * 2);
+  const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.vtiles + seq * a.ntile * VPL * D, ((c1 + 31) >> 5) * VPL * D * 4);
+  const int vo_k = (64 * wave + ln) * KCB + hl * 4;                       // per-lane, fixed
+  const int vo_n = (64 * wave + lane) * 2;
+  const int vo_v = ((hl >> 1) * VPL * D + wave * (NTW * 16) + ln) * 4;
+
+  float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f;  // work-group uniform (m_ref per lane head)
+  float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;        // this lane's tokens, head hl
+  float accf[VMP + 1][NTW];
+  intx4 vacc[VMP + 1][NTW];
 #pragma unroll
   for (int p = 0; p <= VMP; ++p)
 #pragma unroll
-    for (int c = 0; c < NT_W; ++c) acc[p][c] = 0.f;
-  float m_run[FA_GMAX];                       // running maxima, identical in every thread
-#pragma unroll
-  for (int h = 0; h < FA_GMAX; ++h) m_run[h] = -INFINITY;
-  float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;  // sums for head hl (this lane's head)
+    for (int c = 0; c < NTW; ++c) {
+      accf[p][c] = 0.f;
+      vacc[p][c] = intx4{0, 0, 0, 0};
+    }
 
-  const uint8_t *kbase = a.kcodes + seq * a.Tstride * KCB;
-  const uint16_t *knb = a.knorms + seq * a.Tstride;
-  const uint16_t *vnb = a.vnorms + seq * a.Tstride;
-  const uint16_t *vgb = a.vgammas + seq * a.Tstride;
-  const uint32_t *vtb = a.vtiles + seq * a.ntile * VPL * D;
-
+  // ---- prefetch registers ----
+  uint32_t kw[4][KWL];
+  uint32_t nk = 0, nv = 0, ng = 0;
+  uint32_t vw[4][NTW][VPL];
+  if (c0 < c1) {
+    fa_load_keys<D, KB>(kw, rk, vo_k, (int)(c0 * KCB));
+    fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(c0 * 2));
+    fa_load_values<D, VB>(vw, rv, vo_v, (int)((c0 >> 5) * VPL * D * 4));
+  }
   for (int64_t s0 = c0; s0 < c1; s0 += FA_SUB) {
-    __syncthreads();  // previous sub-chunk fully consumed
-    // ---------------- pass K: scores for FA_SUB tokens ----------------
-    float lmax = -INFINITY, vnmax = 0.f, vgmax = 0.f;
-    for (int grp = wave; grp < FA_SUB / 16; grp += 4) {
-      const int tl = grp * 16 + (lane & 15);
-      const int64_t t = s0 + tl;
-      const bool valid = t < c1;
-      uint32_t w[KB];
-      const int gq = lane >> 4;  // lane group: which 32-coordinate words
+    const int64_t sn = s0 + FA_SUB;
+    // ---- norms of this wave's tokens ----
+    const float fvn = f16_to_f32((uint16_t)nv), fvg = f16_to_f32((uint16_t)ng);
+    s_kn[wave][lane] = f16_to_f32((uint16_t)nk);
+    s_norm[wave][0][lane] = fvn;
+    s_norm[wave][1][lane] = fvg;
+    // other lanes of this wave read these below: order the LDS writes before their reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- key pass: this wave's 64 tokens in 4 groups of 16 ----
+    float sc[4];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) w[p] = 0u;
+    for (int grp = 0; grp < 4; ++grp) {
       intx4 cacc = {0, 0, 0, 0};
 #pragma unroll
       for (int wb = 0; wb < D / 128; ++wb) {
-        if (valid) {
-          const uint32_t *rec = reinterpret_cast<const uint32_t *>(kbase + t * KCB);
+        uint32_t w[KB];
 #pragma unroll
-          for (int p = 0; p < KB; ++p) w[p] = rec[p * KW + wb * 4 + gq];
-        }
+        for (int p = 0; p < KB; ++p) w[p] = kw[grp][p * (D / 128) + wb];
         uint32_t wp[KP];
         walsh_planes<KB>(w, wp);
 #pragma unroll
@@ -180,172 +271,153 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
           }
         }
       }
-      // lane (token tl, head hl) holds the four split partial sums in cacc[0..3]
-      const float raw = (float)cacc[0] + (float)cacc[1] * (1.f / 128.f) + (float)cacc[2] * (1.f / 16384.f) +
-                        (float)cacc[3] * (1.f / 2097152.f);
-      float sc = -INFINITY;
-      if (valid && hl < gw) sc = (raw * qinv - qconst) * f16_to_f32(knb[t]) * a.scale_log2;
-      s_sc[hl][tl] = sc;
-      lmax = fmaxf(lmax, sc);
-      if (hl == 0) {
-        const float vn = valid ? f16_to_f32(vnb[t]) : 0.f;
-        s_vn[tl] = vn;
-        vnmax = fmaxf(vnmax, vn);
-      } else if (hl == 1) {
-        const float vg = valid ? f16_to_f32(vgb[t]) : 0.f;
-        s_vg[tl] = vg;
-        vgmax = fmaxf(vgmax, vg);
-      }
+      sc[grp] = (float)cacc[0] + (float)cacc[1] * (1.f / 128.f) + (float)cacc[2] * (1.f / 16384.f) +
+                (float)cacc[3] * (1.f / 2097152.f);
     }
-    lmax = rows16_max(lmax);
-    vnmax = wave_max_f32(vnmax);
-    vgmax = wave_max_f32(vgmax);
-    if ((lane & 15) == 0) s_red[wave][hl][0] = lmax;
-    if (lane == 0) { s_red[wave][0][1] = vnmax; s_red[wave][0][2] = vgmax; }
-    __syncthreads();
-    float msub[FA_GMAX];
-    float vnm = 0.f, vgm = 0.f;
+    if (sn < c1) {  // key/norm registers are free now
+      fa_load_keys<D, KB>(kw, rk, vo_k, (int)(sn * KCB));
+      fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(sn * 2));
+    }
+    float smax = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < FA_GMAX; ++h)
-      msub[h] = fmaxf(fmaxf(s_red[0][h][0], s_red[1][h][0]), fmaxf(s_red[2][h][0], s_red[3][h][0]));
+    for (int grp = 0; grp < 4; ++grp) {
+      const int tl = grp * 16 + ln;
+      const bool ok = head_ok && (s0 + 64 * wave + tl) < c1;
+      sc[grp] = ok ? (sc[grp] * qinv - qconst) * s_kn[wave][tl] * a.scale_log2 : -INFINITY;
+      smax = fmaxf(smax, sc[grp]);
+    }
+    smax = rows16_max(smax);
+    const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
+    if (ln == 0) s_max[wave][hl] = smax;
+    if (lane == 0) { s_max[wave][FA_GMAX] = vnm; s_max[wave][FA_GMAX + 1] = vgm; }
+    __syncthreads();  // B1: step maxima visible; previous step's value pass done everywhere
+    float step_m = -INFINITY, step_vn = 0.f, step_vg = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) { vnm = fmaxf(vnm, s_red[wv][0][1]); vgm = fmaxf(vgm, s_red[wv][0][2]); }
-    // per-head int8 scales: the largest weight of the sub-chunk maps to 127
-    // (p <= 2^(msub - mnew) and n <= vnm bound every weight of head h)
-    float mnew[FA_GMAX], swm[FA_GMAX], swq[FA_GMAX];
+    for (int wv = 0; wv < 4; ++wv) {
+      step_m = fmaxf(step_m, s_max[wv][hl]);
+      step_vn = fmaxf(step_vn, s_max[wv][FA_GMAX]);
+      step_vg = fmaxf(step_vg, s_max[wv][FA_GMAX + 1]);
+    }
+    // ---- move the reference when the step exceeds it (work-group uniform decision) ----
+    bool grow = step_vn > vn_ref || step_vg > vg_ref;
 #pragma unroll
     for (int h = 0; h < FA_GMAX; ++h) {
-      mnew[h] = fmaxf(m_run[h], msub[h]);
-      const float pm = msub[h] == -INFINITY ? 0.f : exp2f(msub[h] - mnew[h]);
-      swm[h] = (pm * vnm > 0.f) ? 127.f / (pm * vnm) : 0.f;
-      swq[h] = (pm * vgm > 0.f) ? 127.f / (pm * vgm) : 0.f;
+      float mh = -INFINITY;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) mh = fmaxf(mh, s_max[wv][h]);
+      float mr = __shfl(m_ref, h * 16, 64);
+      grow = grow || mh > mr;
     }
-
-    // ---------------- weights: p, p*n, p*gamma -> four int8 splits each ----------------
-    float psum[FA_GMAX], pmsum[FA_GMAX], pqsum[FA_GMAX];
-#pragma unroll
-    for (int h = 0; h < FA_GMAX; ++h) psum[h] = pmsum[h] = pqsum[h] = 0.f;
-    {
-      const int tl = tid;  // one token per thread (FA_SUB == FA_THREADS)
-      const int within = tl & 31, blk = (tl >> 5) & 1, tile = tl >> 6;
-      const int kbit = within & 7, ib = within >> 3;
-      const int gpos = 2 * blk + (kbit >> 2);
-      const int bpos = gpos * 16 + (kbit & 3) * 4 + ib;
-      const float kscale = (kbit == 7) ? -1.f / 128.f : 1.f / (float)(1 << kbit);
-      const float vn = s_vn[tl], vg = s_vg[tl];
-#pragma unroll
-      for (int h = 0; h < FA_GMAX; ++h) {
-        if (h >= gw) break;
-        const float p = exp2f(s_sc[h][tl] - mnew[h]);
-        const float wm = p * vn, wq = p * vg;
-        psum[h] = p; pmsum[h] = wm; pqsum[h] = wq;
-        int8_t o[4];
-        split4(wm * swm[h] * kscale, o);
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) s_w[0][tile][4 * h + sp][bpos] = (uint8_t)o[sp];
-        split4(wq * swq[h] * kscale, o);
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) s_w[1][tile][4 * h + sp][bpos] = (uint8_t)o[sp];
-      }
-    }
-    // block sums of p, p n, p gamma per head
-#pragma unroll
-    for (int h = 0; h < FA_GMAX; ++h) {
-      psum[h] = wave_sum_f32(psum[h]);
-      pmsum[h] = wave_sum_f32(pmsum[h]);
-      pqsum[h] = wave_sum_f32(pqsum[h]);
-    }
-    __syncthreads();  // s_red maxima read by everyone; weights written
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < FA_GMAX; ++h) { s_red[wave][h][0] = psum[h]; s_red[wave][h][1] = pmsum[h]; s_red[wave][h][2] = pqsum[h]; }
-    }
-
-    // ---------------- pass V: int8 MFMA over token tiles ----------------
-    intx4 vacc[VMP + 1][NT_W];
-#pragma unroll
-    for (int p = 0; p <= VMP; ++p)
-#pragma unroll
-      for (int c = 0; c < NT_W; ++c) vacc[p][c] = intx4{0, 0, 0, 0};
-    const int64_t tile0 = s0 >> 5;
-#pragma unroll
-    for (int tt = 0; tt < FA_SUB / 64; ++tt) {
-      const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_w[0][tt][lane & 15][16 * (lane >> 4)]);
-      const intx4 wa_q = *reinterpret_cast<const intx4 *>(&s_w[1][tt][lane & 15][16 * (lane >> 4)]);
-      const int64_t vt = tile0 + 2 * tt + ((lane >> 4) >> 1);
-      const bool tvalid = vt < a.ntile && (vt << 5) < c1;
-      const uint32_t *tp = vtb + vt * (VPL * D);
-#pragma unroll
-      for (int c = 0; c < NT_W; ++c) {
-        const int col = (wave * NT_W + c) * 16 + (lane & 15);
-        uint32_t wv[VPL];
-#pragma unroll
-        for (int p = 0; p < VPL; ++p) wv[p] = tvalid ? tp[p * D + col] : 0u;
-        uint32_t wpl[VMP];
-        walsh_planes<VB>(wv, wpl);
-#pragma unroll
-        for (int p = 0; p < VMP; ++p) {
-          intx4 bb;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) bb[r] = (int)(wpl[p] & (0x01010101u << (kofs + r)));
-          vacc[p][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m, bb, vacc[p][c], 0, 0, 0);
-        }
-        intx4 bs;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bs[r] = (int)(wv[VB] & (0x01010101u << (kofs + r)));
-        vacc[VMP][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q, bs, vacc[VMP][c], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // partial sums visible
-    // ---------------- fold into fp32 (online softmax) ----------------
-    {
-      float ps = 0.f, pm = 0.f, pq = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) { ps += s_red[wv][hl][0]; pm += s_red[wv][hl][1]; pq += s_red[wv][hl][2]; }
-      float mr = m_run[0], mn = mnew[0];
-#pragma unroll
-      for (int h = 1; h < FA_GMAX; ++h)
-        if (hl == h) { mr = m_run[h]; mn = mnew[h]; }
-      const float alpha = (mr == -INFINITY) ? 0.f : exp2f(mr - mn);
-      float sm = swm[0], sq = swq[0];
-#pragma unroll
-      for (int h = 1; h < FA_GMAX; ++h)
-        if (hl == h) { sm = swm[h]; sq = swq[h]; }
-      const float im = sm > 0.f ? 1.f / sm : 0.f, iq = sq > 0.f ? 1.f / sq : 0.f;
+    if (grow) {
+      const float m_new = fmaxf(m_ref, step_m);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      const float im = vn_ref / WMAX, iq = vg_ref / WMAX;
 #pragma unroll
       for (int p = 0; p <= VMP; ++p) {
         const float isc = p < VMP ? im : iq;
 #pragma unroll
-        for (int c = 0; c < NT_W; ++c) {
-          const float x = ((float)vacc[p][c][0] + (float)vacc[p][c][1] * (1.f / 128.f) +
-                           (float)vacc[p][c][2] * (1.f / 16384.f) + (float)vacc[p][c][3] * (1.f / 2097152.f)) * isc;
-          acc[p][c] = acc[p][c] * alpha + x;
+        for (int c = 0; c < NTW; ++c) {
+          const float x = (((float)vacc[p][c][0] * 128.f + (float)vacc[p][c][1]) * 128.f + (float)vacc[p][c][2]) *
+                              128.f + (float)vacc[p][c][3];
+          accf[p][c] = (accf[p][c] + x * isc) * alpha;
+          vacc[p][c] = intx4{0, 0, 0, 0};
         }
       }
-      l_run = l_run * alpha + ps;
-      ym_run = ym_run * alpha + pm;
-      yq_run = yq_run * alpha + pq;
+      l_run *= alpha;
+      ym_run *= alpha;
+      yq_run *= alpha;
+      m_ref = m_new;
+      vn_ref = fmaxf(vn_ref, step_vn);
+      vg_ref = fmaxf(vg_ref, step_vg);
+    }
+    // ---- weights of this wave's tokens: p = 2^(s - m_ref) <= 1; p n and p gamma as 7-bit digits ----
+    const float sm = vn_ref > 0.f ? WMAX / vn_ref : 0.f, sq = vg_ref > 0.f ? WMAX / vg_ref : 0.f;
 #pragma unroll
-      for (int h = 0; h < FA_GMAX; ++h) m_run[h] = mnew[h];
+    for (int grp = 0; grp < 4; ++grp) {
+      const int tl = grp * 16 + ln;
+      const float p = exp2f(sc[grp] - m_ref);
+      const float wm = p * s_norm[wave][0][tl], wq = p * s_norm[wave][1][tl];
+      l_run += p;
+      ym_run += wm;
+      yq_run += wq;
+      const int within = tl & 31, kbit = within & 7;
+      const int bpos = (2 * (tl >> 5) + (kbit >> 2)) * 16 + (kbit & 3) * 4 + (within >> 3);
+      const float ks = __builtin_amdgcn_ldexpf(1.f, -value_kexp(kbit));
+      const uint32_t um = (uint32_t)__float2uint_rn(fminf(wm * sm * ks, WMAX));
+      const uint32_t uq = (uint32_t)__float2uint_rn(fminf(wq * sq * ks, WMAX));
+      if (head_ok) {
+        uint8_t *rm = &s_w[0][wave][4 * hl][bpos];
+        uint8_t *rq = &s_w[1][wave][4 * hl][bpos];
+        rm[0] = (uint8_t)(um >> 21);
+        rm[64] = (uint8_t)((um >> 14) & 127u);
+        rm[128] = (uint8_t)((um >> 7) & 127u);
+        rm[192] = (uint8_t)(um & 127u);
+        rq[0] = (uint8_t)(uq >> 21);
+        rq[64] = (uint8_t)((uq >> 14) & 127u);
+        rq[128] = (uint8_t)((uq >> 7) & 127u);
+        rq[192] = (uint8_t)(uq & 127u);
+      }
+    }
+    __syncthreads();  // B2: weight digits of all 256 tokens visible
+    // ---- value pass: 256 tokens x this wave's D/4 columns ----
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_w[0][tt][ln][16 * hl]);
+      const intx4 wa_q = *reinterpret_cast<const intx4 *>(&s_w[1][tt][ln][16 * hl]);
+#pragma unroll
+      for (int c = 0; c < NTW; ++c) {
+        uint32_t wpl[VMP];
+        walsh_planes<VB>(vw[tt][c], wpl);
+#pragma unroll
+        for (int p = 0; p < VMP; ++p)
+          vacc[p][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m, value_bits(wpl[p], kofs), vacc[p][c], 0, 0, 0);
+        vacc[VMP][c] =
+            __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q, value_bits(vw[tt][c][VB], kofs), vacc[VMP][c], 0, 0, 0);
+      }
+    }
+    if (sn < c1) fa_load_values<D, VB>(vw, rv, vo_v, (int)((sn >> 5) * VPL * D * 4));
+  }
+  // ---- final fold, reductions, partial record: m, l, acc_mse[D], acc_qjl[D] ----
+  {
+    const float im = vn_ref / WMAX, iq = vg_ref / WMAX;
+#pragma unroll
+    for (int p = 0; p <= VMP; ++p) {
+      const float isc = p < VMP ? im : iq;
+#pragma unroll
+      for (int c = 0; c < NTW; ++c) {
+        const float x = (((float)vacc[p][c][0] * 128.f + (float)vacc[p][c][1]) * 128.f + (float)vacc[p][c][2]) *
+                            128.f + (float)vacc[p][c][3];
+        accf[p][c] += x * isc;
+      }
     }
   }
-
-  // ---------------- partial record: m, l, acc_mse[D], acc_qjl[D] ----------------
-  if (hl < gw) {
+  l_run = rows16_sum(l_run);
+  ym_run = rows16_sum(ym_run);
+  yq_run = rows16_sum(yq_run);
+  if (ln == 0) {
+    s_merge[wave][hl][0] = l_run;
+    s_merge[wave][hl][1] = ym_run;
+    s_merge[wave][hl][2] = yq_run;
+  }
+  __syncthreads();
+  if (head_ok) {
+    float L = 0.f, YM = 0.f, YQ = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) {
+      L += s_merge[wv][hl][0];
+      YM += s_merge[wv][hl][1];
+      YQ += s_merge[wv][hl][2];
+    }
     float *dst = a.part + (((int64_t)b * a.Hq + h0 + hl) * a.nsplit + split) * (2 + 2 * (int64_t)D);
-    float mr = m_run[0];
+    if (wave == 0 && ln == 0) { dst[0] = m_ref; dst[1] = L; }
 #pragma unroll
-    for (int h = 1; h < FA_GMAX; ++h)
-      if (hl == h) mr = m_run[h];
-    if (wave == 0 && (lane & 15) == 0) { dst[0] = mr; dst[1] = l_run; }
-#pragma unroll
-    for (int c = 0; c < NT_W; ++c) {
-      const int col = (wave * NT_W + c) * 16 + (lane & 15);
+    for (int c = 0; c < NTW; ++c) {
+      const int col = (wave * NTW + c) * 16 + ln;
       float am = 0.f;
 #pragma unroll
-      for (int p = 0; p < VMP; ++p) am += a.vbeta[p] * (2.f * acc[p][c] - ym_run);
+      for (int p = 0; p < VMP; ++p) am += a.vbeta[p] * (2.f * accf[p][c] - YM);
       dst[2 + col] = am;
-      dst[2 + D + col] = a.vqjl * (2.f * acc[VMP][c] - yq_run);
+      dst[2 + D + col] = a.vqjl * (2.f * accf[VMP][c] - YQ);
     }
   }
 }
@@ -374,7 +446,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   const int sub = unit % a.nsub, bg = unit / a.nsub;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
-  const int gw = min(FA_GMAX, a.G - sub * FA_GMAX);
+  const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   for (int e = threadIdx.x; e < FA_GMAX * D; e += 256) {
     const int h = e / D, j = e % D;
     float v = 0.f;

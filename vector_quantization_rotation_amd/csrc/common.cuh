@@ -52,5 +52,9 @@ __device__ __forceinline__ int cell_index(const Codebook &cb, float y, float n) 
 }
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// integer min/max (the generic device min/max overloads may go through floating point)
+__host__ __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+__host__ __device__ __forceinline__ int imin32(int a, int b) { return a < b ? a : b; }
 
 }  // namespace tq
