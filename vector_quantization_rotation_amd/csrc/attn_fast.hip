@@ -124,7 +124,7 @@ __device__ __forceinline__ void fa_load_keys(uint32_t (&kw)[4][KB * (D / 128)], 
 #pragma unroll
       for (int wb = 0; wb < D / 128; ++wb)
         kw[grp][p * (D / 128) + wb] =
-            __builtin_amdgcn_raw_buffer_load_b32(rk, vo + grp * 16 * KCB + p * (D / 8) + wb * 16, so, 0);
+            __builtin_amdgcn_raw_buffer_load_b32(rk, vo + grp * 8 * KCB + p * (D / 8) + wb * 16, so, 0);
 }
 
 __device__ __forceinline__ void fa_load_norms(uint32_t &nk, uint32_t &nv, uint32_t &ng, __amdgpu_buffer_rsrc_t rkn,
@@ -176,6 +176,7 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
   __shared__ float s_kn[4][64];                                        // per wave: n_K
   __shared__ float s_max[4][FA_GMAX + 2];                              // per wave: score max per head, n_V max, gamma max
   __shared__ float s_merge[4][FA_GMAX][3];                             // per wave and head: l, Ym, Yq
+  __shared__ int s_flag[4];                                            // per wave: a step value above the reference
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, split = blockIdx.y;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
   const __amdgpu_buffer_rsrc_t rvn = uniform_rsrc(a.vnorms + seq * a.Tstride, c1 * 2);
   const __amdgpu_buffer_rsrc_t rvg = uniform_rsrc(a.vgammas + seq * a.Tstride, c1 * 2);
   const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.vtiles + seq * a.ntile * VPL * D, ((c1 + 31) >> 5) * VPL * D * 4);
-  const int vo_k = (64 * wave + ln) * KCB + hl * 4;                       // per-lane, fixed
+  const int vo_k = (64 * wave + 32 * (ln >> 3) + (ln & 7)) * KCB + hl * 4;  // per-lane, fixed
   const int vo_n = (64 * wave + lane) * 2;
   const int vo_v = ((hl >> 1) * VPL * D + wave * (NTW * 16) + ln) * 4;
 
@@ -237,9 +238,15 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
     fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(c0 * 2));
     fa_load_values<D, VB>(vw, rv, vo_v, (int)((c0 >> 5) * VPL * D * 4));
   }
+  // token of this wave's 64 scored by (group grp, lane): 32 (ln / 8) + 8 grp + ln % 8, so that a
+  // lane's four tokens fill four consecutive bytes of the value operand's contraction slots
+  const int tbase = 32 * (ln >> 3) + (ln & 7);
+  const int slot = (2 * (ln >> 3) + ((ln & 7) >> 2)) * 16 + (ln & 3) * 4;  // byte offset of grp 0
+  const float kscale = __builtin_amdgcn_ldexpf(1.f, -value_kexp(ln & 7));
   for (int64_t s0 = c0; s0 < c1; s0 += FA_SUB) {
     const int64_t sn = s0 + FA_SUB;
-    // ---- norms of this wave's tokens ----
+    const int64_t wbase = s0 + 64 * wave;
+    // ---- norms of this wave's tokens (lane = token) ----
     const float fvn = f16_to_f32((uint16_t)nv), fvg = f16_to_f32((uint16_t)ng);
     s_kn[wave][lane] = f16_to_f32((uint16_t)nk);
     s_norm[wave][0][lane] = fvn;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- key pass: this wave's 64 tokens in 4 groups of 16 ----
+    // ---- key pass: 4 groups of 16 tokens ----
     float sc[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -278,37 +285,33 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
       fa_load_keys<D, KB>(kw, rk, vo_k, (int)(sn * KCB));
       fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(sn * 2));
     }
-    float smax = -INFINITY;
+    bool over = fvn > vn_ref || fvg > vg_ref;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      const int tl = grp * 16 + ln;
-      const bool ok = head_ok && (s0 + 64 * wave + tl) < c1;
-      sc[grp] = ok ? (sc[grp] * qinv - qconst) * s_kn[wave][tl] * a.scale_log2 : -INFINITY;
-      smax = fmaxf(smax, sc[grp]);
+      const int tw = tbase + 8 * grp;
+      const bool ok = head_ok && (wbase + tw) < c1;
+      sc[grp] = ok ? (sc[grp] * qinv - qconst) * s_kn[wave][tw] * a.scale_log2 : -INFINITY;
+      over = over || sc[grp] > m_ref;
     }
-    smax = rows16_max(smax);
-    const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
-    if (ln == 0) s_max[wave][hl] = smax;
-    if (lane == 0) { s_max[wave][FA_GMAX] = vnm; s_max[wave][FA_GMAX + 1] = vgm; }
-    __syncthreads();  // B1: step maxima visible; previous step's value pass done everywhere
-    float step_m = -INFINITY, step_vn = 0.f, step_vg = 0.f;
+    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0ull;  // every lane votes
+    if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
+    __syncthreads();  // B1: flags visible; previous step's value pass done everywhere
+    const int any_over = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+    if (any_over) {
+      // ---- rare: move the reference to this step's maxima and fold the int32 accumulators ----
+      float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      smax = rows16_max(smax);
+      const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
+      if (ln == 0) s_max[wave][hl] = smax;
+      if (lane == 0) { s_max[wave][FA_GMAX] = vnm; s_max[wave][FA_GMAX + 1] = vgm; }
+      __syncthreads();
+      float step_m = -INFINITY, step_vn = 0.f, step_vg = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) {
-      step_m = fmaxf(step_m, s_max[wv][hl]);
-      step_vn = fmaxf(step_vn, s_max[wv][FA_GMAX]);
-      step_vg = fmaxf(step_vg, s_max[wv][FA_GMAX + 1]);
-    }
-    // ---- move the reference when the step exceeds it (work-group uniform decision) ----
-    bool grow = step_vn > vn_ref || step_vg > vg_ref;
-#pragma unroll
-    for (int h = 0; h < FA_GMAX; ++h) {
-      float mh = -INFINITY;
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) mh = fmaxf(mh, s_max[wv][h]);
-      float mr = __shfl(m_ref, h * 16, 64);
-      grow = grow || mh > mr;
-    }
-    if (grow) {
+      for (int wv = 0; wv < 4; ++wv) {
+        step_m = fmaxf(step_m, s_max[wv][hl]);
+        step_vn = fmaxf(step_vn, s_max[wv][FA_GMAX]);
+        step_vg = fmaxf(step_vg, s_max[wv][FA_GMAX + 1]);
+      }
       const float m_new = fmaxf(m_ref, step_m);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref / WMAX, iq = vg_ref / WMAX;
@@ -330,32 +333,35 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
       vn_ref = fmaxf(vn_ref, step_vn);
       vg_ref = fmaxf(vg_ref, step_vg);
     }
-    // ---- weights of this wave's tokens: p = 2^(s - m_ref) <= 1; p n and p gamma as 7-bit digits ----
-    const float sm = vn_ref > 0.f ? WMAX / vn_ref : 0.f, sq = vg_ref > 0.f ? WMAX / vg_ref : 0.f;
+    // ---- weights: p = 2^(s - m_ref) <= 1; p n and p gamma as four 7-bit digits, one dword per digit row ----
+    {
+      const float sm = vn_ref > 0.f ? WMAX * kscale / vn_ref : 0.f;
+      const float sq = vg_ref > 0.f ? WMAX * kscale / vg_ref : 0.f;
+      uint32_t dm[4] = {0u, 0u, 0u, 0u}, dq[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int tl = grp * 16 + ln;
-      const float p = exp2f(sc[grp] - m_ref);
-      const float wm = p * s_norm[wave][0][tl], wq = p * s_norm[wave][1][tl];
-      l_run += p;
-      ym_run += wm;
-      yq_run += wq;
-      const int within = tl & 31, kbit = within & 7;
-      const int bpos = (2 * (tl >> 5) + (kbit >> 2)) * 16 + (kbit & 3) * 4 + (within >> 3);
-      const float ks = __builtin_amdgcn_ldexpf(1.f, -value_kexp(kbit));
-      const uint32_t um = (uint32_t)__float2uint_rn(fminf(wm * sm * ks, WMAX));
-      const uint32_t uq = (uint32_t)__float2uint_rn(fminf(wq * sq * ks, WMAX));
+      for (int grp = 0; grp < 4; ++grp) {
+        const int tw = tbase + 8 * grp;
+        const float p = exp2f(sc[grp] - m_ref);
+        const float wm = p * s_norm[wave][0][tw], wq = p * s_norm[wave][1][tw];
+        l_run += p;
+        ym_run += wm;
+        yq_run += wq;
+        const uint32_t um = __float2uint_rn(wm * sm), uq = __float2uint_rn(wq * sq);
+        dm[0] |= (um >> 21) << (8 * grp);
+        dm[1] |= ((um >> 14) & 127u) << (8 * grp);
+        dm[2] |= ((um >> 7) & 127u) << (8 * grp);
+        dm[3] |= (um & 127u) << (8 * grp);
+        dq[0] |= (uq >> 21) << (8 * grp);
+        dq[1] |= ((uq >> 14) & 127u) << (8 * grp);
+        dq[2] |= ((uq >> 7) & 127u) << (8 * grp);
+        dq[3] |= (uq & 127u) << (8 * grp);
+      }
       if (head_ok) {
-        uint8_t *rm = &s_w[0][wave][4 * hl][bpos];
-        uint8_t *rq = &s_w[1][wave][4 * hl][bpos];
-        rm[0] = (uint8_t)(um >> 21);
-        rm[64] = (uint8_t)((um >> 14) & 127u);
-        rm[128] = (uint8_t)((um >> 7) & 127u);
-        rm[192] = (uint8_t)(um & 127u);
-        rq[0] = (uint8_t)(uq >> 21);
-        rq[64] = (uint8_t)((uq >> 14) & 127u);
-        rq[128] = (uint8_t)((uq >> 7) & 127u);
-        rq[192] = (uint8_t)(uq & 127u);
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+          *reinterpret_cast<uint32_t *>(&s_w[0][wave][4 * hl + sp][slot]) = dm[sp];
+          *reinterpret_cast<uint32_t *>(&s_w[1][wave][4 * hl + sp][slot]) = dq[sp];
+        }
       }
     }
     __syncthreads();  // B2: weight digits of all 256 tokens visible
