@@ -79,8 +79,7 @@ def main():
     ws = torch.empty((api.attn_decode_ws_bytes(kq, B, Hq, Hkv, T, layout),), dtype=torch.uint8, device="cuda")
     packed = cache.packed_bytes()
 
-    def step():
-        api.attn_decode(kq, vq, q, kc, kn, vt, vn, vg, seq, scale, out=out, ws=ws, vlayout=layout)
+    step = api.attn_decode_bound(kq, vq, q, kc, kn, vt, vn, vg, seq, scale, out, ws, vlayout=layout)
 
     for _ in range(args.warmup):
         step()

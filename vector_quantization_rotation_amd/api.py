@@ -150,3 +150,23 @@ def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, v
                             _ptr(out), _ptr(ws), ws.numel(), _stream())
     _lib._check("tq_attn_decode", rc)
     return out
+
+
+def attn_decode_bound(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
+                      seq_len: torch.Tensor, scale: float, out: torch.Tensor, ws: torch.Tensor,
+                      vlayout: int = TQ_LAYOUT_ROWS):
+    """attn_decode with every argument marshalled once: returns a no-argument callable that
+    enqueues the same call on the current stream (for tight decode loops)."""
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
+    args = (kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms), _ptr(vcodes),
+            _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), C.c_float(scale), _ptr(out), _ptr(ws),
+            C.c_size_t(ws.numel()), _stream())
+    fn = lib.tq_attn_decode
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            _lib._check("tq_attn_decode", rc)
+    return call

@@ -49,7 +49,7 @@ size_t partial_floats(int d) { return 2 + 2 * (size_t)d; }
 
 // q'[b,h,:] = Pi_K q[b,h,:]
 template <int QT>
-__global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *pi, float *qrot) {
+__global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *piT, float *qrot) {
   extern __shared__ float sq[];
   const int64_t bh = blockIdx.x;
   for (int j = threadIdx.x; j < d; j += 256) {
@@ -60,10 +60,10 @@ __global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, co
     sq[j] = v;
   }
   __syncthreads();
+  // q'_j = sum_k Pi[j][k] q_k = sum_k Pi^T[k][j] q_k: lanes read consecutive entries of row k of Pi^T
   for (int j = threadIdx.x; j < d; j += 256) {
-    const float *row = pi + (int64_t)j * d;
     float acc = 0.f;
-    for (int k = 0; k < d; ++k) acc = fmaf(row[k], sq[k], acc);
+    for (int k = 0; k < d; ++k) acc = fmaf(piT[(int64_t)k * d + j], sq[k], acc);
     qrot[bh * d + j] = acc;
   }
 }
@@ -164,45 +164,43 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   }
 }
 
-// merge the splits of one (batch, head) and rotate back:
-// out = (Pi_V^T A_mse + S_V^T A_qjl) / L   (A_qjl already carries the QJL constant)
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float *part, int nsplit, int d, const float *piT,
-                                                           const float *sT, float *out) {
-  extern __shared__ float sh[];  // [2d] merged accumulators
-  const int64_t bh = blockIdx.x;
+// merge the sequence splits of one (batch, head) with their log-sum-exp weights:
+// A[bh] = [sum_s 2^(m_s - M) acc_mse_s, sum_s 2^(m_s - M) acc_qjl_s] / sum_s 2^(m_s - M) l_s
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int nsplit, int d, int64_t rows,
+                                                         float *merged) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * 2 * d) return;
+  const int64_t bh = e / (2 * d);
+  const int j = (int)(e % (2 * d));
   const float *pp = part + bh * nsplit * (2 + 2 * (int64_t)d);
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (2 + 2 * (int64_t)d)]);
-  float L = 0.f;
+  float L = 0.f, a = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const float *q = pp + s * (2 + 2 * (int64_t)d);
-    if (q[1] > 0.f) L += q[1] * exp2f(q[0] - M);
-  }
-  for (int j = threadIdx.x; j < 2 * d; j += 256) {
-    float a = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float *q = pp + s * (2 + 2 * (int64_t)d);
-      if (q[1] > 0.f) a = fmaf(q[2 + j], exp2f(q[0] - M), a);
+    if (q[1] > 0.f) {
+      const float f = exp2f(q[0] - M);
+      L = fmaf(q[1], f, L);
+      a = fmaf(q[2 + j], f, a);
     }
-    sh[j] = a;
   }
-  __syncthreads();
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float *r1 = piT + (int64_t)i * d;
-    const float *r2 = sT + (int64_t)i * d;
-    float acc = 0.f;
-    for (int j = 0; j < d; ++j) acc = fmaf(r1[j], sh[j], acc);
-    for (int j = 0; j < d; ++j) acc = fmaf(r2[j], sh[d + j], acc);
-    out[bh * d + i] = acc * inv;
-  }
+  merged[bh * 2 * d + j] = L > 0.f ? a / L : 0.f;
 }
 
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *out,
-                 hipStream_t st) {
-  ProfScope ps("attn_combine", st);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(BH), dim3(256), 2 * (size_t)d * 4, st, part, nsplit, d, piT, sT, out);
-  return launch_check();
+// out[bh] = Pi_V^T A_mse + S_V^T A_qjl: one contraction on the fp32 matrix cores
+int rotate_back(const float *merged, int64_t rows, int d, const float *piT, const float *sT, float *out, hipStream_t st);
+
+int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *merged,
+                 float *out, hipStream_t st) {
+  {
+    ProfScope ps("attn_combine", st);
+    const int64_t n = (int64_t)BH * 2 * d;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, part, nsplit, d,
+                       (int64_t)BH, merged);
+  }
+  int rc = launch_check();
+  if (rc != TQ_OK) return rc;
+  return rotate_back(merged, BH, d, piT, sT, out, st);
 }
 
 size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T);
@@ -216,7 +214,7 @@ size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tst
   const int d = kq->d;
   AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
   size_t qb = ((size_t)B * Hq * d * 4 + 255) & ~(size_t)255;
-  return qb + (size_t)B * Hq * p.nsplit * partial_floats(d) * 4;
+  return qb + (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255) + (size_t)B * Hq * 2 * d * 4;
 }
 
 template <int CP>
@@ -246,9 +244,9 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   const size_t shq = (size_t)d * 4;
   {
   ProfScope ps("attn_qrot", st);
-  if (qt == TQ_F32) hipLaunchKernelGGL(attn_qrot_kernel<TQ_F32>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
-  else if (qt == TQ_BF16) hipLaunchKernelGGL(attn_qrot_kernel<TQ_BF16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
-  else hipLaunchKernelGGL(attn_qrot_kernel<TQ_F16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->pi, qrot);
+  if (qt == TQ_F32) hipLaunchKernelGGL(attn_qrot_kernel<TQ_F32>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
+  else if (qt == TQ_BF16) hipLaunchKernelGGL(attn_qrot_kernel<TQ_BF16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
+  else hipLaunchKernelGGL(attn_qrot_kernel<TQ_F16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
   }
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
@@ -267,7 +265,9 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   }
   }
   if ((rc = launch_check()) != TQ_OK) return rc;
-  return attn_combine(part, B * Hq, p.nsplit, d, vq->piT, vq->sT, out, st);
+  float *merged = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
+                                            (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255));
+  return attn_combine(part, B * Hq, p.nsplit, d, vq->piT, vq->sT, merged, out, st);
 }
 
 }  // namespace tq

@@ -160,7 +160,7 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
 // value norm and gamma) that moves only when a step exceeds it; the int32
 // accumulators are folded into fp32 then.
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
+__global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attn_fast_kernel(FastAttnArgs a) {
   constexpr int KP = walsh_count(KB);        // key Walsh planes
   constexpr int VMP = walsh_count(VB);       // value Walsh planes (index part)
   constexpr int VPL = VB + 1;                // stored value planes per tile
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(FA_THREADS) void attn_fast_kernel(FastAttnArgs a) {
 struct PrepArgs {
   const void *q;
   int qt, Hq, Hkv, G, nsub;
-  const float *pi;
+  const float *piT;
   float kbeta[8];
   float ctop;
   int *qimg;
@@ -466,13 +466,12 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   }
   if (threadIdx.x < FA_GMAX * 2) red[threadIdx.x / 2][threadIdx.x % 2] = 0.f;
   __syncthreads();
+  // q'_j = sum_k Pi^T[k][j] q_k: consecutive lanes read consecutive entries of row k of Pi^T
   for (int e = threadIdx.x; e < FA_GMAX * D; e += 256) {
     const int h = e / D, j = e % D;
     float acc = 0.f;
-    if (h < gw) {
-      const float *row = a.pi + (int64_t)j * D;
-      for (int k = 0; k < D; ++k) acc = fmaf(row[k], qs[h][k], acc);
-    }
+    if (h < gw)
+      for (int k = 0; k < D; ++k) acc = fmaf(a.piT[(int64_t)k * D + j], qs[h][k], acc);
     qp[h][j] = acc;
   }
   __syncthreads();
@@ -583,7 +582,7 @@ void walsh_coeffs(const double *c, int bits, double *beta) {
 
 struct FastPlan {
   int nsub, nsplit, chunk, nins;
-  size_t img_off, info_off, part_off, total;
+  size_t img_off, info_off, part_off, merge_off, total;
 };
 
 FastPlan fast_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
@@ -601,7 +600,8 @@ FastPlan fast_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   p.img_off = 0;
   p.info_off = al((size_t)units * p.nins * 64 * 16);
   p.part_off = p.info_off + al((size_t)units * FA_GMAX * 2 * 4);
-  p.total = p.part_off + (size_t)B * Hq * p.nsplit * (2 + 2 * (size_t)D) * 4;
+  p.merge_off = p.part_off + al((size_t)B * Hq * p.nsplit * (2 + 2 * (size_t)D) * 4);
+  p.total = p.merge_off + (size_t)B * Hq * 2 * (size_t)D * 4;
   return p;
 }
 
@@ -630,8 +630,8 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   return fast_plan(D, KB, B, Hq, Hkv, T).total;
 }
 
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *out,
-                 hipStream_t st);
+int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *merged,
+                 float *out, hipStream_t st);
 
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
@@ -646,7 +646,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   walsh_coeffs(kq->c64, KB, kb64);
   walsh_coeffs(vq->c64, VB, vb64);
   PrepArgs pa{};
-  pa.q = q; pa.qt = qt; pa.Hq = Hq; pa.Hkv = Hkv; pa.G = Hq / Hkv; pa.nsub = fp.nsub; pa.pi = kq->pi;
+  pa.q = q; pa.qt = qt; pa.Hq = Hq; pa.Hkv = Hkv; pa.G = Hq / Hkv; pa.nsub = fp.nsub; pa.piT = kq->piT;
   for (int i = 0; i < 8; ++i) pa.kbeta[i] = (float)kb64[i];
   pa.ctop = (float)kq->c64[(1 << KB) - 1];
   pa.qimg = reinterpret_cast<int *>(w + fp.img_off);
@@ -671,7 +671,8 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   TQ_FAST(256, 1, 3) TQ_FAST(256, 2, 3) TQ_FAST(256, 3, 3)
 #undef TQ_FAST
   if (rc != TQ_OK) return rc;
-  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->piT, vq->sT, out, st);
+  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->piT, vq->sT, reinterpret_cast<float *>(w + fp.merge_off), out,
+                      st);
 }
 
 }  // namespace tq
