@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-slices", type=int, default=48, help="(batch, kv-head) slices the oracle times")
+    ap.add_argument("--cpu-slices", type=int, default=24, help="(batch, kv-head) slices the oracle times")
     return ap.parse_args()
 
 
@@ -147,32 +147,50 @@ def main():
             blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:
             blas_threads = os.cpu_count()
+        from tests import parity as parity_helpers
         piK, piV, sV = mats
-        cK, _ = oracle.lloyd_max(d, 3)
-        cV, _ = oracle.lloyd_max(d, 1)
+        chans = synth.outlier_channels(Hkv, d, 4, workloads.ATTN_SEEDS["chan"])
         rng = np.random.default_rng(7)
-        slices = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(args.cpu_slices)]
+        slices = sorted({(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(args.cpu_slices)})
         G = Hq // Hkv
         errs = []
         t_cpu = 0.0
         bytes_cpu = 0
+        raw = {}
+        refs = {}
         for (b, g) in slices:
-            kcs, kns = kc[b, g].cpu().numpy(), kn[b, g].cpu().numpy().view(np.float16)
-            vcs, vns, vgs = vc[b, g].cpu().numpy(), vn[b, g].cpu().numpy().view(np.float16), vg[b, g].cpu().numpy().view(np.float16)
+            # the oracle works from the raw K/V of this slice, regenerated from the workload's seeds,
+            # and encodes them itself (untimed); its records replace the library's in that slice of
+            # the device cache.  The timed part is what a decode step does: packed records ->
+            # decoded caches -> attention
+            if b not in raw:
+                raw = {b: {w: synth.kv_bf16_torch((1, Hkv, T, d), workloads.ATTN_SEEDS[w] * 1000 + b, chans, "cuda")
+                           for w in ("K", "V")}}
+            K = raw[b]["K"][0, g].float().cpu().numpy()
+            V = raw[b]["V"][0, g].float().cpu().numpy()
+            ke, ve = parity_helpers.install_oracle_slice(cache, b, g, K, V)
+            krec, vrec = ke["record"], ve["record"]
+            kns, vns, vgs = ke["n_hat"], ve["n_hat"], ve["gamma"]
             t1 = time.perf_counter()
-            kidx = oracle.parse_mse_record(kcs, d, 3)
-            vidx, vsb = oracle.parse_prod_record(vcs, d, 2)
-            Kt = oracle.decode_mse(kidx, kns, piK, cK)[None, None]
-            Vt = oracle.decode_prod(vidx, vns, vsb, vgs, piV, sV, cV)[None, None]
-            ref = oracle.decode_attention(qh[b:b + 1, g * G:(g + 1) * G], Kt, Vt, np.array([T]), scale)
+            kidx = oracle.parse_mse_record(krec, d, 3)
+            vidx, vsb = oracle.parse_prod_record(vrec, d, 2)
+            Kt = oracle.decode_mse(kidx, kns, piK, ke["c"])[None, None]
+            Vt = oracle.decode_prod(vidx, vns, vsb, vgs, piV, sV, ve["c"])[None, None]
+            refs[(b, g)] = oracle.decode_attention(qh[b:b + 1, g * G:(g + 1) * G], Kt, Vt, np.array([T]), scale)[0]
             t_cpu += time.perf_counter() - t1
-            bytes_cpu += T * (kc.shape[-1] + 2 + vc.shape[-1] + 4)
+            bytes_cpu += T * (krec.shape[-1] + 2 + vrec.shape[-1] + 4)
+        del raw
+        # the sampled slices now hold the oracle's records: one more launch of the timed call
+        step()
+        out_gpu = out.cpu().numpy()
+        for (b, g), ref in refs.items():
             got = out_gpu[b, g * G:(g + 1) * G]
-            errs.append(float(np.max(np.linalg.norm(got - ref[0], axis=-1) / np.linalg.norm(ref[0], axis=-1))))
+            errs.append(float(np.max(np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1))))
         cpu = {"value": round(bytes_cpu / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
                "kind": "oracle",
                "sample": f"{len(slices)} of {B * Hkv} (batch, kv-head) slices, {T} tokens x {G} query heads each: "
-                         f"fp64 decode of the packed records + two-pass softmax attention, {t_cpu:.1f}s",
+                         f"fp64 decode of the oracle's own packed records + two-pass softmax attention, {t_cpu:.1f}s "
+                         f"(the oracle's encode of the raw slices is not timed)",
                "host_cpus": os.cpu_count()}
         parity = {"max_rel_err": max(errs), "tolerance": 2e-3, "slices": slices}
         log(f"cpu oracle: {cpu['value']} GB/s over {t_cpu:.1f}s; parity max rel err {max(errs):.2e}")

@@ -71,3 +71,66 @@ def rel_rows(got, ref):
 def residual_given_index(x, idx, nhat, pi, centroids):
     """Oracle residual r = x - n_hat Pi^T c[idx] for a given index array."""
     return np.asarray(x, dtype=np.float64) - oracle.decode_mse(idx, nhat, pi, centroids)
+
+
+def f16_bits(v) -> np.ndarray:
+    """fp16 values -> their int16 bit patterns (the library's norm/gamma storage)."""
+    return np.ascontiguousarray(np.asarray(v, dtype=np.float16)).view(np.int16)
+
+
+def oracle_mse(x, pi, bits):
+    """The oracle's Algorithm-1 encoding of x: dict with idx, n_hat (f16), record (u8), centroids, bounds."""
+    d = np.asarray(x).shape[1]
+    c, t = oracle.lloyd_max(d, bits)
+    idx, nh = oracle.encode_mse(x, pi, c, t)
+    return dict(idx=idx, n_hat=nh, record=oracle.mse_record(idx, bits), c=c, t=t)
+
+
+def oracle_prod(x, pi, s, bits):
+    """The oracle's Algorithm-2 encoding of x (b-1 index bits + sign plane)."""
+    d = np.asarray(x).shape[1]
+    c, t = oracle.lloyd_max(d, bits - 1)
+    idx, nh, sb, gh = oracle.encode_prod(x, pi, s, c, t)
+    return dict(idx=idx, n_hat=nh, signs=sb, gamma=gh, record=oracle.prod_record(idx, sb, bits), c=c, t=t)
+
+
+def untile(tiles, T, nplanes, d):
+    """Token-tiled words [ceil(T/32), P, d] (bit i of word = token 32k+i) -> row records [T, P*d/8]."""
+    w = np.asarray(tiles).view(np.uint32).astype(np.uint64)
+    nt = w.shape[0]
+    bits = ((w[..., None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).astype(np.uint8)  # [nt, P, d, 32]
+    bits = bits.transpose(0, 3, 1, 2).reshape(nt * 32, nplanes, d)[:T]
+    return np.packbits(bits, axis=2, bitorder="little").reshape(T, nplanes * d // 8)
+
+
+def check_prod_signs(sb_gpu, idx_gpu, enc, x, pi, s):
+    """Sign bits vs the oracle's, on rows whose index decisions all agree (elsewhere the residual differs)."""
+    same = np.all(idx_gpu == enc["idx"], axis=1)
+    margins = oracle.sign_margins(x, pi, s, enc["c"], enc["t"])
+    nbad, nties = check_codes(sb_gpu[same], enc["signs"][same], margins[same], "sign")
+    return nbad, nties, same
+
+
+def install_oracle_slice(cache, b, g, K, V, kbits=3, vbits=2):
+    """Encode the raw rows of (batch b, kv-head g) with the oracle and write the oracle's records,
+    norms, gammas and token-tiled value words into that slice of a device cache (an AttnCache).
+
+    The attention of that slice then runs on exactly the oracle's codes, so its output can be
+    held to the attention tolerance (a code decision inside the tie zone may move a heavily
+    weighted token's score, which no fixed tolerance on the output covers)."""
+    import torch
+    d = K.shape[1]
+    ke = oracle_mse(K, cache.piK, kbits)
+    ve = oracle_prod(V, cache.piV, cache.sV, vbits)
+    dev = cache.kcodes.device
+
+    def put(dst, arr):
+        dst.copy_(torch.from_numpy(np.ascontiguousarray(arr)).to(dev).view(dst.shape))
+
+    put(cache.kcodes[b, g], ke["record"])
+    put(cache.knorms[b, g], f16_bits(ke["n_hat"]))
+    put(cache.vcodes[b, g], ve["record"])
+    put(cache.vnorms[b, g], f16_bits(ve["n_hat"]))
+    put(cache.vgammas[b, g], f16_bits(ve["gamma"]))
+    put(cache.vtiles[b, g], oracle.tile_records(ve["record"], d, vbits).view(np.int32))
+    return ke, ve
