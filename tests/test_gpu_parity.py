@@ -231,6 +231,16 @@ ATTN_FAST_CASES = [
     (1, 8, 2, 20000, [19999], 128, 3, 2),        # long sequence: many steps per work-group
     (1, 4, 4, 64, [2], 128, 3, 2),               # the largest weight maps to the top int8 digit
     (2, 8, 8, 64, [1, 1], 128, 3, 2),            # one token: output is that token's value
+    # sequence strides that are multiples of 8 take the wave-streaming kernel (head_dim 128, 1-bit values)
+    (2, 8, 2, 1000, [1000, 641], 128, 3, 2),     # ragged tails inside a 64-token step
+    (1, 8, 2, 4096, [4096], 128, 2, 2),
+    (1, 4, 4, 2048, [1999], 128, 1, 2),
+    (1, 4, 4, 2048, [1999], 128, 3, 2),          # one head per kv head
+    (1, 4, 1, 2048, [1999], 128, 1, 2),          # 1-bit keys, four heads
+    (1, 4, 4, 256, [256], 128, 1, 2),
+    (2, 24, 4, 520, [520, 0], 128, 3, 2),        # 6 heads per kv head: a full and a partial head group
+    (1, 4, 1, 192, [130], 128, 3, 2),            # one ring turn, the last step partly valid
+    (1, 32, 8, 30000, [29999], 128, 3, 2),       # many steps per wave
 ]
 
 

@@ -429,6 +429,388 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 }
 
 // ---------------------------------------------------------------------------
+// Wave-streaming variant for head_dim 128 and 1-bit value indices (2-bit prod
+// values): every wave is an independent stream over its own token range, with
+// no work-group barrier anywhere in the loop.
+//
+// * Each 64-token step is staged into a wave-private double-buffered LDS ring
+//   by direct-to-LDS buffer loads issued two steps ahead (keys as 16-byte
+//   plane rows, value tiles as they lie in HBM, the three fp16 arrays), so the
+//   bytes in flight do not occupy registers.
+// * Scores as in attn_fast_kernel (int8 matrix cores on the key Walsh planes).
+// * Value weights p n and p gamma become 24-bit integers split into three
+//   signed byte digits (the integer XOR 0x808080 reads, byte by byte, as the
+//   digit minus 128); row 3 of each head's four MFMA rows is a row of ones
+//   that sums the value operand's bytes, which restores the 128 offsets
+//   exactly.  The digit bytes of a lane's four tokens are gathered with byte
+//   permutes.
+// * The value operand shifts each tile word by the lane's 4-token offset so
+//   every byte holds 1, 2, 4 or 8; the weights carry the inverse factor.
+// * The online softmax reference (maximum, largest value norm and gamma) is
+//   per wave; the int32 accumulators are folded (exactly, in fp64) only when a
+//   step exceeds it.
+// ---------------------------------------------------------------------------
+constexpr int WV_STEP = 64;
+constexpr int WV_RING = 3;                // ring slots: stages s+1 and s+2 are in flight while s is used
+constexpr float WV_WMAX = 8388352.f;      // 2^23 - 256: weights are integers below 2^23 (see wv_weight)
+constexpr float WV_MAGIC = 8388608.f;     // 2^23
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int KB>
+struct WaveStage {
+  static constexpr int KEYS = KB * 1024;   // [plane][64 token slots][16 B]
+  static constexpr int VALS = 2 * 1024;    // [2 tiles][2 planes][128 coords] u32, as stored in HBM
+  static constexpr int NORMS = 3 * 256;    // n_K, n_V, gamma_V: [64] fp16 each (+128 B landing zone)
+  static constexpr int BYTES = KEYS + VALS + NORMS;
+  static constexpr int NLOAD = KB + 2 + 3;  // load instructions per stage
+};
+
+// wait until at most n vector-memory loads of this wave are outstanding (loads complete in order)
+template <int N>
+__device__ __forceinline__ void wv_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// key slot of token t (0..63) in a stage: tokens t and t+32 sit side by side
+__device__ __forceinline__ int wv_key_slot(int t) { return 2 * (t & 31) + (t >> 5); }
+
+// direct-to-LDS loads of one stage: keys as 16-byte plane rows, the two value tiles, and the three
+// fp16 arrays (lanes 0..31 fetch two tokens each; lanes 32..63 aim past every buffer, so they write
+// zeros into the landing zone and fetch nothing).  Reads past the sequence end return zeros and
+// touch no memory.
+template <int KB>
+__device__ __forceinline__ void wv_stage_load(uint8_t *stage, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                              __amdgpu_buffer_rsrc_t rkn, __amdgpu_buffer_rsrc_t rvn,
+                                              __amdgpu_buffer_rsrc_t rvg, int lane, int voff_k, int voff_n,
+                                              int64_t t0) {
+  constexpr int KCB = KB * 16;
+  using S = WaveStage<KB>;
+  const int sk = __builtin_amdgcn_readfirstlane((int)(t0 * KCB));
+#pragma unroll
+  for (int p = 0; p < KB; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(stage + p * 1024), 16, voff_k + p * 16, sk, 0, 0);
+  const int sv = __builtin_amdgcn_readfirstlane((int)((t0 >> 5) * 1024));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(stage + S::KEYS), 16, lane * 16, sv, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(stage + S::KEYS + 1024), 16, lane * 16 + 1024, sv, 0,
+                                           0);
+  const int sn = __builtin_amdgcn_readfirstlane((int)(t0 * 2));
+  uint8_t *nb = stage + S::KEYS + S::VALS;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rkn, (lds_void_t *)(nb), 4, voff_n, sn, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rvn, (lds_void_t *)(nb + 256), 4, voff_n, sn, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rvg, (lds_void_t *)(nb + 512), 4, voff_n, sn, 0, 0);
+}
+
+// w s (0 <= w s < 2^23) rounded to the nearest integer, as the low three bytes of the result, each
+// XOR 0x80: fma(w, s, 2^23) lands in [2^23, 2^24), where the fp32 spacing is 1, so its mantissa is the
+// rounded integer (round to nearest even); the top byte is never read
+__device__ __forceinline__ uint32_t wv_weight(float w, float s) {
+  return __float_as_uint(fmaf(w, s, WV_MAGIC)) ^ 0x808080u;
+}
+
+// value operand: token bits 4c..4c+3 of every byte (c = lane group parity) as bytes 1, 2, 4, 8
+__device__ __forceinline__ intx4 wv_value_bits(uint32_t w, int kofs) {
+  const uint32_t x = w >> kofs;
+  intx4 r;
+  r[0] = (int)(x & 0x01010101u);
+  r[1] = (int)(x & 0x02020202u);
+  r[2] = (int)(x & 0x04040404u);
+  r[3] = (int)(x & 0x08080808u);
+  return r;
+}
+
+// bytes d of four 24-bit words -> one word per digit (byte g = digit of word g)
+__device__ __forceinline__ void wv_digits(const uint32_t (&u)[4], uint32_t (&o)[3]) {
+  const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+  const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+  const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+}
+
+// folded value of one head's four accumulator rows: digits 1, 2^8, 2^16, and the row of ones (the
+// sum of the value operand's bytes) times the digit offset 0x808080
+__device__ __forceinline__ double wv_fold(const intx4 &v) {
+  return (double)v[0] + 256.0 * (double)v[1] + 65536.0 * (double)v[2] + 8421504.0 * (double)v[3];
+}
+
+template <int KB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_wave_kernel(FastAttnArgs a) {
+  constexpr int D = 128;
+  constexpr int KP = walsh_count(KB);
+  constexpr int NINS = KP * 2;
+  constexpr int KCB = KB * D / 8;
+  constexpr int NTC = D / 16;  // value column tiles
+  using S = WaveStage<KB>;
+
+  // one object per ring slot, so the compiler's waits for the direct-to-LDS loads stay per slot
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring0[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring1[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring2[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][16][64];  // weight digits [kind][row][token k]
+
+  const int lane = threadIdx.x;
+  const int hl = lane >> 4, ln = lane & 15;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int sub = unit % a.nsub, bg = unit / a.nsub;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int h0 = g * a.G + sub * FA_GMAX;
+  const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
+  const bool head_ok = hl < gw;
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0), a.Tstride);
+  const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = imin64(T, c0 + a.chunk);
+  // steps, padded to whole ring turns (padding steps hold no valid token and add nothing)
+  const int nvalid = c0 < c1 ? (int)((c1 - c0 + WV_STEP - 1) / WV_STEP) : 0;
+  const int nsteps = (nvalid + WV_RING - 1) / WV_RING * WV_RING;
+
+  intx4 qa[NINS];
+  {
+    const intx4 *img = reinterpret_cast<const intx4 *>(a.qimg) + (int64_t)unit * NINS * 64;
+#pragma unroll
+    for (int i = 0; i < NINS; ++i) qa[i] = img[i * 64 + lane];
+  }
+  const float qinv = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0];
+  const float qconst = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1];
+
+  // digit rows start at zero (rows of absent heads stay so); row 4h+3 of both kinds is all ones
+  for (int i = lane; i < 2 * 16 * 16; i += 64) {
+    const int row = (i >> 4) & 15;
+    reinterpret_cast<uint32_t *>(&s_w[0][0][0])[i] = (row & 3) == 3 ? 0x01010101u : 0u;
+  }
+
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.kcodes + seq * a.Tstride * KCB, c1 * KCB);
+  // the fp16 arrays are fetched a dword (two tokens) at a time: round their ranges up to whole dwords
+  // (the stride is a multiple of 8 tokens, so this stays inside the sequence's row)
+  const int64_t nbytes = (c1 * 2 + 3) & ~(int64_t)3;
+  const __amdgpu_buffer_rsrc_t rkn = uniform_rsrc(a.knorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvn = uniform_rsrc(a.vnorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvg = uniform_rsrc(a.vgammas + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.vtiles + seq * a.ntile * 2 * D, ((c1 + 31) >> 5) * 2 * D * 4);
+  const int voff_k = (32 * (lane & 1) + (lane >> 1)) * KCB;
+  const int voff_n = lane < 32 ? lane * 4 : 0x7FFFFF00;  // past every buffer's end for lanes 32..63
+
+  float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f;
+  float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;
+  float accf[2][NTC];
+  intx4 vacc[2][NTC];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int c = 0; c < NTC; ++c) {
+      accf[k][c] = 0.f;
+      vacc[k][c] = intx4{0, 0, 0, 0};
+    }
+
+  // this lane's tokens in a step: 32 (ln / 8) + (ln % 8) + 8 grp (grp = 0..3)
+  const int tbase = 32 * (ln >> 3) + (ln & 7);
+  const int slot = (2 * (ln >> 3) + ((ln & 7) >> 2)) * 16 + (ln & 3) * 4;  // byte of grp 0 in a digit row
+  const float kscale = 1.f / (float)(1 << (ln & 3));
+  const int kofs = 4 * (hl & 1);
+  int since_fold = 0;
+  float sm_l = 0.f, sq_l = 0.f;  // weight scales WV_WMAX 2^-r / (largest n_V, gamma_V so far)
+
+  // one step over the stage in `st` (a fixed ring slot after inlining)
+  auto body = [&, rk, rkn, rvn, rvg, rv](uint8_t *st, int s) {
+    const int64_t t0 = c0 + (int64_t)s * WV_STEP;
+    const int rem = (int)imax64(imin64(c1 - t0, WV_STEP), 0);  // valid tokens in this step
+    const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
+    // every body issues one stage, so the two stages after this one are the only loads that may
+    // still be in flight: this stage has landed in LDS once no more than theirs are outstanding
+    wv_wait_vm<2 * S::NLOAD>();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- every read of the stage up front: key words, the dwords holding this lane's fp16 values,
+    // value words (four adjacent columns per read; column tile c of this lane is column
+    // 64 (c / 4) + 4 ln + c % 4) ----
+    uint32_t kw[4][KB];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int ks = wv_key_slot(tbase + 8 * grp);
+#pragma unroll
+      for (int p = 0; p < KB; ++p) kw[grp][p] = *reinterpret_cast<const uint32_t *>(st + p * 1024 + ks * 16 + hl * 4);
+    }
+    uint32_t hn[3][4];  // token tbase + 8 grp is the (tbase % 2) half of dword (tbase + 8 grp) / 2
+    {
+      const uint32_t *nd = reinterpret_cast<const uint32_t *>(nrm) + (tbase >> 1);
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nd[64 * k + 4 * grp];
+    }
+    uint4 vw[2][2];  // [plane][column half]
+    {
+      const uint32_t *vt = reinterpret_cast<const uint32_t *>(st + S::KEYS) + (hl >> 1) * 256 + 4 * ln;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) vw[p][h] = *reinterpret_cast<const uint4 *>(vt + 128 * p + 64 * h);
+    }
+    // the optimizer takes a direct-to-LDS load for a write of a few bytes only, and could otherwise
+    // move these reads below the refill of this slot: pin every value that is used after it
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) asm volatile("" : "+v"(hn[k][grp]));
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(vw[p][h].x), "+v"(vw[p][h].y), "+v"(vw[p][h].z), "+v"(vw[p][h].w));
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- key pass: the four 16-token groups interleaved, so consecutive MFMAs are independent ----
+    uint32_t wp[4][KP];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) walsh_planes<KB>(kw[grp], wp[grp]);
+    intx4 cacc[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) cacc[grp] = intx4{0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < KP; ++p)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          intx4 bb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bb[r] = (int)(wp[grp][p] & (0x01010101u << (4 * half + r)));
+          cacc[grp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[p * 2 + half], bb, cacc[grp], 0, 0, 0);
+        }
+    // every read of this slot has returned by now (its words fed the key MFMAs or sit in registers):
+    // refill it with the stage one ring turn ahead
+    __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    wv_stage_load<KB>(st, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, t0 + WV_RING * WV_STEP);
+    __builtin_amdgcn_sched_barrier(0);
+    float sc[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp)
+      sc[grp] = (float)cacc[grp][0] + (float)cacc[grp][1] * (1.f / 128.f) + (float)cacc[grp][2] * (1.f / 16384.f) +
+                (float)cacc[grp][3] * (1.f / 2097152.f);
+    // ---- scores and the reference test ----
+    float fk[4], fvn[4], fvg[4];
+    const int sh = 16 * (tbase & 1);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      fk[grp] = f16_to_f32((uint16_t)(hn[0][grp] >> sh));
+      fvn[grp] = f16_to_f32((uint16_t)(hn[1][grp] >> sh));
+      fvg[grp] = f16_to_f32((uint16_t)(hn[2][grp] >> sh));
+    }
+    bool over = false;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const bool valid = tbase + 8 * grp < rem;
+      const float s_ = (sc[grp] * qinv - qconst) * fk[grp] * a.scale_log2;
+      fvn[grp] = valid ? fvn[grp] : 0.f;
+      fvg[grp] = valid ? fvg[grp] : 0.f;
+      sc[grp] = (head_ok && valid) ? s_ : -INFINITY;
+      over = over || sc[grp] > m_ref || fvn[grp] > vn_ref || fvg[grp] > vg_ref;
+    }
+    ++since_fold;
+    if ((__builtin_amdgcn_ballot_w64(over) != 0ull) || since_fold >= 16384) {
+      // rare: move the reference to this step's maxima and fold the integer accumulators
+      float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      smax = rows16_max(smax);
+      const float vnm = wave_max_f32(fmaxf(fmaxf(fvn[0], fvn[1]), fmaxf(fvn[2], fvn[3])));
+      const float vgm = wave_max_f32(fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3])));
+      const float m_new = fmaxf(m_ref, smax);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      const double im = (double)vn_ref / WV_WMAX, iq = (double)vg_ref / WV_WMAX;
+#pragma unroll
+      for (int c = 0; c < NTC; ++c) {
+        accf[0][c] = (accf[0][c] + (float)(wv_fold(vacc[0][c]) * im)) * alpha;
+        accf[1][c] = (accf[1][c] + (float)(wv_fold(vacc[1][c]) * iq)) * alpha;
+        vacc[0][c] = intx4{0, 0, 0, 0};
+        vacc[1][c] = intx4{0, 0, 0, 0};
+      }
+      l_run *= alpha;
+      ym_run *= alpha;
+      yq_run *= alpha;
+      m_ref = m_new;
+      vn_ref = fmaxf(vn_ref, vnm);
+      vg_ref = fmaxf(vg_ref, vgm);
+      sm_l = vn_ref > 0.f ? WV_WMAX * kscale / vn_ref : 0.f;
+      sq_l = vg_ref > 0.f ? WV_WMAX * kscale / vg_ref : 0.f;
+      since_fold = 0;
+    }
+    // ---- weights: p n and p gamma as integers below 2^23, three signed byte digits per token ----
+    {
+      uint32_t um[4], uq[4];
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        // p = 2^(s - m_ref) <= 1 (hardware exp2: results below 2^-126 flush to zero)
+        const float p = __builtin_amdgcn_exp2f(sc[grp] - m_ref);
+        const float wm = p * fvn[grp], wq = p * fvg[grp];
+        l_run += p;
+        ym_run += wm;
+        yq_run += wq;
+        um[grp] = wv_weight(wm, sm_l);
+        uq[grp] = wv_weight(wq, sq_l);
+      }
+      uint32_t dm[3], dq[3];
+      wv_digits(um, dm);
+      wv_digits(uq, dq);
+      if (head_ok) {
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          *reinterpret_cast<uint32_t *>(&s_w[0][4 * hl + d][slot]) = dm[d];
+          *reinterpret_cast<uint32_t *>(&s_w[1][4 * hl + d][slot]) = dq[d];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- value pass: 64 tokens x 128 columns, both kinds ----
+    {
+      const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_w[0][ln][16 * hl]);
+      const intx4 wa_q = *reinterpret_cast<const intx4 *>(&s_w[1][ln][16 * hl]);
+#pragma unroll
+      for (int c = 0; c < NTC; ++c) {
+        const uint32_t w0 = vw[0][c >> 2][c & 3], w1 = vw[1][c >> 2][c & 3];
+        vacc[0][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m, wv_value_bits(w0, kofs), vacc[0][c], 0, 0, 0);
+        vacc[1][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q, wv_value_bits(w1, kofs), vacc[1][c], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    wv_stage_load<KB>(s_ring0, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0);
+    wv_stage_load<KB>(s_ring1, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0 + WV_STEP);
+    wv_stage_load<KB>(s_ring2, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0 + 2 * WV_STEP);
+    for (int s = 0; s < nsteps; s += WV_RING) {
+      body(s_ring0, s);
+      body(s_ring1, s + 1);
+      body(s_ring2, s + 2);
+    }
+  }
+  // ---- final fold and partial record: m, l, acc_mse[D], acc_qjl[D] ----
+  {
+    const double im = (double)vn_ref / WV_WMAX, iq = (double)vg_ref / WV_WMAX;
+#pragma unroll
+    for (int c = 0; c < NTC; ++c) {
+      accf[0][c] += (float)(wv_fold(vacc[0][c]) * im);
+      accf[1][c] += (float)(wv_fold(vacc[1][c]) * iq);
+    }
+  }
+  l_run = rows16_sum(l_run);
+  ym_run = rows16_sum(ym_run);
+  yq_run = rows16_sum(yq_run);
+  if (head_ok) {
+    float *dst = a.part + (((int64_t)b * a.Hq + h0 + hl) * a.nsplit + split) * (2 + 2 * (int64_t)D);
+    if (ln == 0) { dst[0] = m_ref; dst[1] = l_run; }
+#pragma unroll
+    for (int c = 0; c < NTC; ++c) {
+      const int col = 64 * (c >> 2) + 4 * ln + (c & 3);
+      dst[2 + col] = a.vbeta[0] * (2.f * accf[0][c] - ym_run);
+      dst[2 + D + col] = a.vqjl * (2.f * accf[1][c] - yq_run);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // query operand images: q' = Pi_K q, Walsh-weighted, 2^-k folded, three int8 splits
 // ---------------------------------------------------------------------------
 struct PrepArgs {
@@ -605,6 +987,56 @@ FastPlan fast_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   return p;
 }
 
+// wave-streaming plan: one single-wave work-group per resident slot, each a contiguous token range
+struct WavePlan {
+  int nsplit, chunk;
+  size_t img_off, info_off, part_off, merge_off, total;
+};
+
+bool wave_supported(int D, int KB, int VB) { return D == 128 && VB == 1 && KB >= 1 && KB <= 3; }
+
+// resident single-wave work-groups of attn_wave_kernel<KB> on the current device (cached per device)
+int wave_slots(int KB) {
+  static int cache[64][4] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int &slot = cache[dev][KB];
+  if (slot > 0) return slot;
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  hipError_t e = hipErrorInvalidValue;
+  if (KB == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wave_kernel<1>, 64, 0);
+  if (KB == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wave_kernel<2>, 64, 0);
+  if (KB == 3) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wave_kernel<3>, 64, 0);
+  if (e != hipSuccess || blocks <= 0) blocks = 8;
+  slot = cus * blocks;
+  return slot;
+}
+
+WavePlan wave_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
+  WavePlan p{};
+  const int G = Hq / Hkv;
+  const int nsub = (G + FA_GMAX - 1) / FA_GMAX;
+  const int nins = walsh_count(KB) * (D / 128) * 2;
+  const int64_t units = (int64_t)B * Hkv * nsub;
+  const int64_t want = std::max<int64_t>(1, wave_slots(KB) / std::max<int64_t>(units, 1));
+  int64_t chunk = (T + want - 1) / want;
+  // whole ring turns per wave, so only the last range of a sequence pads
+  const int64_t turn = (int64_t)WV_RING * WV_STEP;
+  chunk = std::max<int64_t>(turn, (chunk + turn - 1) / turn * turn);
+  p.chunk = (int)std::min<int64_t>(chunk, 1 << 30);
+  p.nsplit = (int)std::max<int64_t>(1, (T + p.chunk - 1) / p.chunk);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.img_off = 0;
+  p.info_off = al((size_t)units * nins * 64 * 16);
+  p.part_off = p.info_off + al((size_t)units * FA_GMAX * 2 * 4);
+  p.merge_off = p.part_off + al((size_t)B * Hq * p.nsplit * (2 + 2 * (size_t)D) * 4);
+  p.total = p.merge_off + (size_t)B * Hq * 2 * (size_t)D * 4;
+  return p;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 bool fast_supported(int D, int KB, int VB) {
   if (D != 128 && D != 256) return false;
   if (KB < 1 || KB > 4 || VB < 1 || VB > 3) return false;
@@ -627,7 +1059,9 @@ int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, 
 }  // namespace
 
 size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
-  return fast_plan(D, KB, B, Hq, Hkv, T).total;
+  size_t n = fast_plan(D, KB, B, Hq, Hkv, T).total;
+  if (wave_supported(D, KB, 1)) n = std::max(n, wave_plan(D, KB, B, Hq, Hkv, T).total);
+  return n;
 }
 
 int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *merged,
@@ -640,6 +1074,19 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   const int D = kq->d, KB = kq->bits, VB = vq->bmse;
   if (!fast_supported(D, KB, VB)) return TQ_ERR_UNSUPPORTED;
   FastPlan fp = fast_plan(D, KB, B, Hq, Hkv, Tstride);
+  // the wave-streaming kernel stages 16-byte pieces: sequence rows of the fp16 arrays must stay aligned
+  const bool wave = wave_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) && aligned16(knorms) &&
+                    aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas);
+  if (wave) {
+    const WavePlan wp = wave_plan(D, KB, B, Hq, Hkv, Tstride);
+    fp.nsplit = wp.nsplit;
+    fp.chunk = wp.chunk;
+    fp.img_off = wp.img_off;
+    fp.info_off = wp.info_off;
+    fp.part_off = wp.part_off;
+    fp.merge_off = wp.merge_off;
+    fp.total = wp.total;
+  }
   const int units = B * Hkv * fp.nsub;
   char *w = static_cast<char *>(ws);
   double kb64[8] = {0}, vb64[4] = {0};
@@ -661,6 +1108,25 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   fa.vqjl = vq->qjl_scale;
   for (int i = 0; i < 4; ++i) fa.vbeta[i] = (float)vb64[i];
   int rc = TQ_ERR_UNSUPPORTED;
+  if (wave) {
+    {
+      ProfScope ps("attn_prep", st);
+      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3>), dim3(units), dim3(256), 0, st, pa);
+    }
+    if ((rc = launch_check()) != TQ_OK) return rc;
+    {
+      ProfScope ps("attn_split", st);
+      const dim3 grid((unsigned)units, (unsigned)fp.nsplit);
+      if (KB == 1) hipLaunchKernelGGL(attn_wave_kernel<1>, grid, dim3(64), 0, st, fa);
+      if (KB == 2) hipLaunchKernelGGL(attn_wave_kernel<2>, grid, dim3(64), 0, st, fa);
+      if (KB == 3) hipLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, fa);
+    }
+    if ((rc = launch_check()) != TQ_OK) return rc;
+    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->piT, vq->sT, reinterpret_cast<float *>(w + fp.merge_off),
+                        out, st);
+  }
 #define TQ_FAST(DD, KK, VV) \
   if (D == DD && KB == KK && VB == VV) rc = launch_fast<DD, KK, VV>(fp, fa, pa, units, st);
   TQ_FAST(128, 1, 1) TQ_FAST(128, 2, 1) TQ_FAST(128, 3, 1) TQ_FAST(128, 4, 1)
