@@ -164,43 +164,139 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   }
 }
 
-// merge the sequence splits of one (batch, head) with their log-sum-exp weights:
-// A[bh] = [sum_s 2^(m_s - M) acc_mse_s, sum_s 2^(m_s - M) acc_qjl_s] / sum_s 2^(m_s - M) l_s
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int nsplit, int d, int64_t rows,
+// Finishing a (batch, head) row takes two short, latency-bound kernels with many threads each:
+// (1) merge the row's sequence splits with their log-sum-exp weights,
+//     A = [sum_s 2^(m_s - M) acc_mse_s, sum_s 2^(m_s - M) acc_qjl_s] / sum_s 2^(m_s - M) l_s
+//     (one thread per entry of A; the split loads are issued together, FIN_CHUNK at a time);
+// (2) rotate back once: out = Pi_V^T A_mse + S_V^T A_qjl, i.e. out_j = sum_k Pi[k][j] A_k + S[k][j] A_{d+k}
+//     (a work-group takes 32 output columns of one row; eight k-slices of the 2d terms are summed
+//     through LDS; consecutive threads read consecutive entries of a row of Pi or S).
+constexpr int FIN_CHUNK = 16;
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int64_t BH, int nsplit, int d,
                                                          float *merged) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= rows * 2 * d) return;
+  if (e >= BH * 2 * d) return;
   const int64_t bh = e / (2 * d);
   const int j = (int)(e % (2 * d));
-  const float *pp = part + bh * nsplit * (2 + 2 * (int64_t)d);
+  const int64_t rec = 2 + 2 * (int64_t)d;
+  const float *pp = part + bh * nsplit * rec;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (2 + 2 * (int64_t)d)]);
+  for (int q0 = 0; q0 < nsplit; q0 += FIN_CHUNK) {
+    float m[FIN_CHUNK], l[FIN_CHUNK];
+#pragma unroll
+    for (int i = 0; i < FIN_CHUNK; ++i) {
+      const int q = imin32(q0 + i, nsplit - 1);
+      m[i] = pp[q * rec];
+      l[i] = pp[q * rec + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < FIN_CHUNK; ++i)
+      if (l[i] > 0.f) M = fmaxf(M, m[i]);
+  }
   float L = 0.f, a = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float *q = pp + s * (2 + 2 * (int64_t)d);
-    if (q[1] > 0.f) {
-      const float f = exp2f(q[0] - M);
-      L = fmaf(q[1], f, L);
-      a = fmaf(q[2 + j], f, a);
+  for (int q0 = 0; q0 < nsplit; q0 += FIN_CHUNK) {
+    float m[FIN_CHUNK], l[FIN_CHUNK], v[FIN_CHUNK];
+#pragma unroll
+    for (int i = 0; i < FIN_CHUNK; ++i) {
+      const int q = imin32(q0 + i, nsplit - 1);
+      m[i] = pp[q * rec];
+      l[i] = q0 + i < nsplit ? pp[q * rec + 1] : 0.f;
+      v[i] = pp[q * rec + 2 + j];
+    }
+#pragma unroll
+    for (int i = 0; i < FIN_CHUNK; ++i) {
+      const float f = l[i] > 0.f ? exp2f(m[i] - M) : 0.f;
+      L = fmaf(l[i], f, L);
+      a = fmaf(v[i], f, a);
     }
   }
-  merged[bh * 2 * d + j] = L > 0.f ? a / L : 0.f;
+  merged[e] = L > 0.f ? a / L : 0.f;
 }
 
-// out[bh] = Pi_V^T A_mse + S_V^T A_qjl: one contraction on the fp32 matrix cores
-int rotate_back(const float *merged, int64_t rows, int d, const float *piT, const float *sT, float *out, hipStream_t st);
-
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *merged,
-                 float *out, hipStream_t st) {
-  {
-    ProfScope ps("attn_combine", st);
-    const int64_t n = (int64_t)BH * 2 * d;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, part, nsplit, d,
-                       (int64_t)BH, merged);
+template <int PER>
+__global__ __launch_bounds__(256) void attn_rotate_kernel(const float *merged, int64_t BH, int d, const float *pi,
+                                                          const float *s, float *out) {
+  constexpr int HB = 4;  // rows per work-group: each entry of Pi and S read serves all of them
+  __shared__ float red[HB][8][33];
+  const int64_t bh0 = (int64_t)blockIdx.x * HB;
+  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int j = blockIdx.y * 32 + c;
+  // slice sl covers terms t0 .. t0+PER-1 of the 2d (the first d pair with rows of Pi, the rest with rows of S)
+  const int t0 = sl * PER;
+  const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
+  float m[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) m[i] = mrow[(int64_t)i * d];
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    const float *A = merged + imin64(bh0 + h, BH - 1) * 2 * d + t0;
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v = fmaf(m[i], A[i], v);
+    acc[h] = v;
+    red[h][sl][c] = v;
   }
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      float v = acc[h];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) v += red[h][q][c];
+      if (bh0 + h < BH) out[(bh0 + h) * d + j] = v;
+    }
+  }
+}
+
+// head dims above 256: one row per work-group, eight slices of 2d / 8 terms, partially unrolled
+__global__ __launch_bounds__(256) void attn_rotate_generic_kernel(const float *merged, int d, const float *pi,
+                                                                  const float *s, float *out) {
+  __shared__ float red[8][33];
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int j = blockIdx.y * 32 + c;
+  const float *A = merged + bh * 2 * d;
+  const int per = 2 * d / 8, t0 = sl * per;
+  const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
+  float acc = 0.f;
+#pragma unroll 32
+  for (int i = 0; i < per; ++i) acc = fmaf(mrow[(int64_t)i * d], A[t0 + i], acc);
+  red[sl][c] = acc;
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int q = 1; q < 8; ++q) acc += red[q][c];
+    out[bh * d + j] = acc;
+  }
+}
+
+size_t attn_merge_ws_bytes(int BH, int d) { return (size_t)BH * 2 * d * sizeof(float); }
+
+int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
+                 float *out, hipStream_t st) {
+  if (BH == 0) return TQ_OK;
+  ProfScope ps("attn_combine", st);
+  const int64_t n = (int64_t)BH * 2 * d;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, part, (int64_t)BH, nsplit, d,
+                     merged);
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
-  return rotate_back(merged, BH, d, piT, sT, out, st);
+  // eight slices of the 2d terms: 2d / 8 = d / 4 terms per thread
+  const dim3 grid((unsigned)cdiv64(BH, 4), (unsigned)(d / 32));
+  switch (d) {
+    case 64: hipLaunchKernelGGL(attn_rotate_kernel<16>, grid, dim3(256), 0, st, merged, (int64_t)BH, d, pi, s, out); break;
+    case 128: hipLaunchKernelGGL(attn_rotate_kernel<32>, grid, dim3(256), 0, st, merged, (int64_t)BH, d, pi, s, out); break;
+    case 256: hipLaunchKernelGGL(attn_rotate_kernel<64>, grid, dim3(256), 0, st, merged, (int64_t)BH, d, pi, s, out); break;
+    default: {
+      // larger head dims: slices of 64 terms, launched per 256-term quarter block of... keep one generic form
+      if (d % 256 != 0 && d > 256) return TQ_ERR_UNSUPPORTED;
+      hipLaunchKernelGGL(attn_rotate_generic_kernel, dim3((unsigned)BH, (unsigned)(d / 32)), dim3(256), 0, st, merged,
+                         d, pi, s, out);
+    }
+  }
+  return launch_check();
 }
 
 size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T);
@@ -214,7 +310,8 @@ size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tst
   const int d = kq->d;
   AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
   size_t qb = ((size_t)B * Hq * d * 4 + 255) & ~(size_t)255;
-  return qb + (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255) + (size_t)B * Hq * 2 * d * 4;
+  return qb + (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255) +
+         attn_merge_ws_bytes(B * Hq, d);
 }
 
 template <int CP>
@@ -267,7 +364,7 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   if ((rc = launch_check()) != TQ_OK) return rc;
   float *merged = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
                                             (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255));
-  return attn_combine(part, B * Hq, p.nsplit, d, vq->piT, vq->sT, merged, out, st);
+  return attn_combine(part, B * Hq, p.nsplit, d, vq->pi, vq->s, merged, out, st);
 }
 
 }  // namespace tq

@@ -848,13 +848,37 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   }
   if (threadIdx.x < FA_GMAX * 2) red[threadIdx.x / 2][threadIdx.x % 2] = 0.f;
   __syncthreads();
-  // q'_j = sum_k Pi^T[k][j] q_k: consecutive lanes read consecutive entries of row k of Pi^T
-  for (int e = threadIdx.x; e < FA_GMAX * D; e += 256) {
-    const int h = e / D, j = e % D;
-    float acc = 0.f;
-    if (h < gw)
-      for (int k = 0; k < D; ++k) acc = fmaf(a.piT[(int64_t)k * D + j], qs[h][k], acc);
-    qp[h][j] = acc;
+  // q'_j = sum_k Pi^T[k][j] q_k for the group's heads: thread (slice, j) sums a slice of k for column j
+  // (consecutive threads read consecutive entries of a row of Pi^T; the unrolled loop keeps many
+  // independent loads in flight), and the slices are added through LDS
+  {
+    constexpr int SL = 256 / D;  // k slices (2 for head_dim 128, 1 for 256)
+    const int j = threadIdx.x % D, sl = threadIdx.x / D;
+    float acc[FA_GMAX] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int KS = D / SL, KU = KS < 64 ? KS : 64;
+    for (int k0 = sl * KS; k0 < (sl + 1) * KS; k0 += KU) {
+      float pv[KU];  // a whole batch of loads in flight at once
+#pragma unroll
+      for (int i = 0; i < KU; ++i) pv[i] = a.piT[(int64_t)(k0 + i) * D + j];
+#pragma unroll
+      for (int i = 0; i < KU; ++i)
+#pragma unroll
+        for (int h = 0; h < FA_GMAX; ++h) acc[h] = fmaf(pv[i], qs[h][k0 + i], acc[h]);
+    }
+    if (SL > 1) {
+      if (sl == 1) {
+#pragma unroll
+        for (int h = 0; h < FA_GMAX; ++h) qp[h][j] = acc[h];
+      }
+      __syncthreads();
+      if (sl == 0) {
+#pragma unroll
+        for (int h = 0; h < FA_GMAX; ++h) qp[h][j] += acc[h];
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < FA_GMAX; ++h) qp[h][j] = acc[h];
+    }
   }
   __syncthreads();
   // per head: sum q' and max |q'_j 2^-k_j|
@@ -1064,7 +1088,7 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   return n;
 }
 
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *piT, const float *sT, float *merged,
+int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
                  float *out, hipStream_t st);
 
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
@@ -1124,8 +1148,8 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       if (KB == 3) hipLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
-    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->piT, vq->sT, reinterpret_cast<float *>(w + fp.merge_off),
-                        out, st);
+    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+                        st);
   }
 #define TQ_FAST(DD, KK, VV) \
   if (D == DD && KB == KK && VB == VV) rc = launch_fast<DD, KK, VV>(fp, fa, pa, units, st);
@@ -1137,8 +1161,8 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   TQ_FAST(256, 1, 3) TQ_FAST(256, 2, 3) TQ_FAST(256, 3, 3)
 #undef TQ_FAST
   if (rc != TQ_OK) return rc;
-  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->piT, vq->sT, reinterpret_cast<float *>(w + fp.merge_off), out,
-                      st);
+  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+                        st);
 }
 
 }  // namespace tq

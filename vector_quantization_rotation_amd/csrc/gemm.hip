@@ -388,11 +388,6 @@ int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norm
   return gemm("decode", ld, lb, es, n, d, prod ? 2 * d : d, st);
 }
 
-int rotate_back(const float *merged, int64_t rows, int d, const float *piT, const float *sT, float *out,
-                hipStream_t st) {
-  return gemm("attn_rotate", LoadF32{merged, 2 * (int64_t)d}, LoadCols2{piT, sT, d}, EpiStore{out, d}, rows, d, 2 * d,
-              st);
-}
 
 size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k) {
   const int kq = q->mode == TQ_PROD ? 2 * q->d : q->d;
