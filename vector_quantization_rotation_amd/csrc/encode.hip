@@ -1,0 +1,51 @@
+// Host side of the fused encode (kernels in encode.cuh): the bf16 pieces of the
+// per-shape matrices, the supported shapes and the dispatch.
+#include "encode.cuh"
+
+namespace tq {
+
+// pieces [3][d][d] of a fp32 matrix (piece-major, rows unchanged): exact split as in encode.cuh
+__global__ void split3_kernel(const float *src, int64_t n, uint16_t *dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float p[3];
+  split_exact<3>(src[i], p);
+  dst[i] = (uint16_t)(__float_as_uint(p[0]) >> 16);
+  dst[n + i] = (uint16_t)(__float_as_uint(p[1]) >> 16);
+  dst[2 * n + i] = (uint16_t)(__float_as_uint(p[2]) >> 16);
+}
+
+int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st) {
+  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, src, n, dst);
+  return launch_check();
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+bool encode_fused_supported(const tq_quantizer *q) {
+  return (q->d == 64 || q->d == 128) && q->pi3 && q->bmse >= 1 && q->bmse <= 4 && (q->mode != TQ_PROD || q->m3);
+}
+
+int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
+                     uint16_t *norms, uint16_t *gammas, hipStream_t st) {
+  if (n == 0) return TQ_OK;
+  EncArgs ea{};
+  ea.x = x; ea.ldx = ldx; ea.n = n; ea.pi3 = q->pi3; ea.m3 = q->m3; ea.codes = codes;
+  ea.code_bytes = (int64_t)q->code_bytes; ea.norms = norms; ea.gammas = gammas; ea.cb = q->cb;
+  ProfScope ps("encode_fused", st);
+  if (q->mode == TQ_PROD) launch_encode_prod(xt, q->d, q->bmse, ea, st);
+  else launch_encode_mse(xt, q->d, q->bmse, ea, st);
+  return launch_check();
+}
+
+}  // namespace tq

@@ -344,6 +344,10 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
 
 int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes, uint16_t *norms,
                uint16_t *gammas, hipStream_t st) {
+  // head dims up to 128 with 16-byte aligned rows: one fused kernel on the bf16 matrix cores
+  const size_t esz0 = xt == TQ_F32 ? 4 : 2;
+  if (encode_fused_supported(q) && (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx * esz0) % 16 == 0)
+    return run_encode_fused(q, x, xt, n, ldx, codes, norms, gammas, st);
   const int d = q->d;
   const bool prod = q->mode == TQ_PROD;
   const int64_t chunk = prod ? std::max<int64_t>(64, (int64_t(1) << 27) / d) : (int64_t(1) << 22);

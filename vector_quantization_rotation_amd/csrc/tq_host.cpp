@@ -130,6 +130,8 @@ void free_q(tq_quantizer *q) {
   hipFree(q->s);
   hipFree(q->sT);
   hipFree(q->m);
+  hipFree(q->pi3);
+  hipFree(q->m3);
   if (prev >= 0) hipSetDevice(prev);
   delete q;
 }
@@ -222,10 +224,14 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
     }
     if (rc == TQ_OK) rc = dev_upload<float>(&q->m, nullptr, dd);
     if (rc == TQ_OK) rc = tq::compute_sPiT(d, q->s, q->pi, q->m, nullptr);
-    if (rc == TQ_OK) {
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) rc = tq::hip_fail(e);
-    }
+    if (rc == TQ_OK) rc = dev_upload<uint16_t>(&q->m3, nullptr, 3 * dd);
+    if (rc == TQ_OK) rc = tq::make_pieces(q->m, (int64_t)dd, q->m3, nullptr);
+  }
+  if (rc == TQ_OK) rc = dev_upload<uint16_t>(&q->pi3, nullptr, 3 * dd);
+  if (rc == TQ_OK) rc = tq::make_pieces(q->pi, (int64_t)dd, q->pi3, nullptr);
+  if (rc == TQ_OK) {
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = tq::hip_fail(e);
   }
   if (rc != TQ_OK) { free_q(q); return rc; }
   *out = q;

@@ -38,6 +38,9 @@ struct tq_quantizer {
   float *s = nullptr;    // S            (TQ_PROD)
   float *sT = nullptr;   // S^T          (TQ_PROD)
   float *m = nullptr;    // S Pi^T       (TQ_PROD): S r = M (Pi x - n_hat c[idx]) up to Pi's fp32 orthogonality
+  // bf16 pieces [3][d][d] (hi, mid, lo; exact splits of the fp32 entries) for the bf16 matrix cores
+  uint16_t *pi3 = nullptr;  // of Pi
+  uint16_t *m3 = nullptr;   // of S Pi^T (TQ_PROD)
 };
 
 namespace tq {
@@ -73,6 +76,10 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
                     const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
 int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
                      hipStream_t st);
+int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
+bool encode_fused_supported(const tq_quantizer *q);
+int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
+                     uint16_t *norms, uint16_t *gammas, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
 
 }  // namespace tq
