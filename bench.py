@@ -42,7 +42,32 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=24, help="(batch, kv-head) slices the oracle times")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wave_kernel_traffic.md")
+ATTN_SRC = os.path.join(ROOT, "vector_quantization_rotation_amd", "csrc", "attn_fast.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    kv = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if kv.get("attn_fast.hip sha256") != src or "traffic bytes per launch" not in kv:
+        return None
+    return int(kv["traffic bytes per launch"])
 
 
 def main():
@@ -80,6 +105,16 @@ def main():
     packed = cache.packed_bytes()
 
     step = api.attn_decode_bound(kq, vq, q, kc, kn, vt, vn, vg, seq, scale, out, ws, vlayout=layout)
+
+    if args.copy_calib:
+        # a plain streaming kernel of known size (reads 1 GiB, writes 1 GiB): its FETCH_SIZE and
+        # WRITE_SIZE calibrate the HBM byte counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -130,11 +165,12 @@ def main():
     torch.cuda.synchronize()
     edt = (time.perf_counter() - t0) / esteps
     _lib.profile_enable(False)
-    enc_rot_ms, enc_rot_n = _lib.profile_query("encode_rotate")
-    enc_qjl_ms, enc_qjl_n = _lib.profile_query("encode_qjl")
+    enc_mse_ms, enc_mse_n = _lib.profile_query("encode_mse")
+    enc_prod_ms, enc_prod_n = _lib.profile_query("encode_prod")
     enc_bytes = 2 * nvec * d * 2 + ek[0].numel() + 2 * nvec + ev[0].numel() + 4 * nvec
     enc_vps = 2 * nvec / edt
-    log(f"encode: {edt * 1e3:.3f} ms for {2 * nvec} vectors = {enc_vps:.3e} vectors/s, {enc_bytes / edt / 1e9:.1f} GB/s")
+    log(f"encode: {edt * 1e3:.3f} ms for {2 * nvec} vectors = {enc_vps:.3e} vectors/s, {enc_bytes / edt / 1e9:.1f} GB/s; "
+        f"kernels mse {enc_mse_ms / max(enc_mse_n, 1):.4f} ms, prod {enc_prod_ms / max(enc_prod_n, 1):.4f} ms")
     del Ke, Ve
 
     # ---------------- CPU oracle on a bounded sample ----------------
@@ -214,13 +250,13 @@ def main():
                    "value_layout": "token-tiled (32 tokens per word)",
                    "packed_bytes": int(packed), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_split", "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
         "encode": {"value": round(enc_vps, 1), "unit": "vectors/s", "ms": round(edt * 1e3, 4),
                    "vectors": 2 * nvec, "gbs": round(enc_bytes / edt / 1e9, 2),
-                   "rotate_ms": round(enc_rot_ms / max(enc_rot_n, 1), 5),
-                   "qjl_ms": round(enc_qjl_ms / max(enc_qjl_n, 1), 5),
+                   "mse_kernel_ms": round(enc_mse_ms / max(enc_mse_n, 1), 5),
+                   "prod_kernel_ms": round(enc_prod_ms / max(enc_prod_n, 1), 5),
                    "workload": "one layer: batch 8 x 8 kv heads x 32768 tokens x d128; K mse 3-bit + V prod 3-bit"},
         "parity_sample": parity,
     }

@@ -55,8 +55,10 @@ struct EncIn {
   static constexpr int ESZ = XT == TQ_F32 ? 4 : 2;
 };
 
+// 16-byte alignment lets every fragment access be one ds_read/ds_write_b128 (8 lanes a cycle, conflict-free
+// at the padded strides below) instead of b64 pairs (16 lanes a cycle, two-way conflicts)
 template <int D, int NPA, bool PROD>
-struct EncLds {
+struct __attribute__((aligned(16))) EncLds {
   static constexpr int CW = D / 4;
   uint16_t a[NPA][EB][D + 8];          // row pieces of the tile
   float cw[4][EB][CW + 4];             // per-wave transpose: MFMA layout -> lane = row
@@ -90,28 +92,37 @@ __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// the exact-piece products, smallest terms first
+// the exact-piece products (A piece, B piece), smallest terms first
 template <int NPA>
-__device__ __forceinline__ floatx4 piece_products(const bf16x8 (&af)[3], const bf16x8 (&bf)[3], floatx4 c) {
-  if (NPA == 1) {
-    c = mfma_bf16(af[0], bf[2], c);
-    c = mfma_bf16(af[0], bf[1], c);
-    c = mfma_bf16(af[0], bf[0], c);
-  } else if (NPA == 2) {
-    c = mfma_bf16(af[1], bf[1], c);
-    c = mfma_bf16(af[0], bf[2], c);
-    c = mfma_bf16(af[1], bf[0], c);
-    c = mfma_bf16(af[0], bf[1], c);
-    c = mfma_bf16(af[0], bf[0], c);
-  } else {
-    c = mfma_bf16(af[1], bf[1], c);
-    c = mfma_bf16(af[2], bf[0], c);
-    c = mfma_bf16(af[0], bf[2], c);
-    c = mfma_bf16(af[1], bf[0], c);
-    c = mfma_bf16(af[0], bf[1], c);
-    c = mfma_bf16(af[0], bf[0], c);
-  }
-  return c;
+struct PieceTerms;
+template <>
+struct PieceTerms<1> {
+  static constexpr int N = 3;
+  static constexpr int A[N] = {0, 0, 0}, B[N] = {2, 1, 0};
+};
+template <>
+struct PieceTerms<2> {
+  static constexpr int N = 5;
+  static constexpr int A[N] = {1, 0, 1, 0, 0}, B[N] = {1, 2, 0, 1, 0};
+};
+template <>
+struct PieceTerms<3> {
+  static constexpr int N = 6;
+  static constexpr int A[N] = {1, 2, 0, 1, 0, 0}, B[N] = {1, 0, 2, 0, 1, 0};
+};
+
+// acc[rt][ct] += A rows (16 rt ..) x B columns (16 ct ..) over one 32-deep k-step,
+// term-major so that consecutive MFMAs write different accumulators
+template <int NPA, int NCT>
+__device__ __forceinline__ void contract_kstep(const bf16x8 (&af)[4][3], const bf16x8 (&bf)[NCT][3],
+                                               floatx4 (&acc)[4][NCT]) {
+  using TT = PieceTerms<NPA>;
+#pragma unroll
+  for (int t = 0; t < TT::N; ++t)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mfma_bf16(af[rt][TT::A[t]], bf[ct][TT::B[t]], acc[rt][ct]);
 }
 
 // all of this work-group's LDS traffic done, then the work-group meets (no wait on global loads)
@@ -356,16 +367,15 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 af[4][3];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        bf16x8 af[3];
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          af[p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[0];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = piece_products<NPA>(af, bpi[ks][ct], acc[rt][ct]);
-      }
+          af[rt][p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[rt][0];
+      contract_kstep<NPA, NCT>(af, bpi[ks], acc);
+    }
     lds_barrier();  // row pieces consumed
 
     // ---- to lane = row ----
@@ -441,15 +451,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 af[4][3];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        bf16x8 af[3];
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) af[p] = *reinterpret_cast<const bf16x8 *>(&sh.rp[p][16 * rt + j16][32 * ks + 8 * g4]);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = piece_products<3>(af, bmq[ks][ct], acc[rt][ct]);
-      }
+        for (int p = 0; p < 3; ++p) af[rt][p] = *reinterpret_cast<const bf16x8 *>(&sh.rp[p][16 * rt + j16][32 * ks + 8 * g4]);
+      contract_kstep<3, NCT>(af, bmq[ks], acc);
+    }
     wave_lds_order();
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)

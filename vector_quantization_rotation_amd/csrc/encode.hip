@@ -42,7 +42,7 @@ int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, in
   EncArgs ea{};
   ea.x = x; ea.ldx = ldx; ea.n = n; ea.pi3 = q->pi3; ea.m3 = q->m3; ea.codes = codes;
   ea.code_bytes = (int64_t)q->code_bytes; ea.norms = norms; ea.gammas = gammas; ea.cb = q->cb;
-  ProfScope ps("encode_fused", st);
+  ProfScope ps(q->mode == TQ_PROD ? "encode_prod" : "encode_mse", st);
   if (q->mode == TQ_PROD) launch_encode_prod(xt, q->d, q->bmse, ea, st);
   else launch_encode_mse(xt, q->d, q->bmse, ea, st);
   return launch_check();
