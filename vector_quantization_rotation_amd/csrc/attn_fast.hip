@@ -433,8 +433,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 // values): every wave is an independent stream over its own token range, with
 // no work-group barrier anywhere in the loop.
 //
-// * Each 64-token step is staged into a wave-private double-buffered LDS ring
-//   by direct-to-LDS buffer loads issued two steps ahead (keys as 16-byte
+// * Each 64-token step is staged into a wave-private three-slot LDS ring by
+//   direct-to-LDS buffer loads issued two steps ahead (keys as 16-byte
 //   plane rows, value tiles as they lie in HBM, the three fp16 arrays), so the
 //   bytes in flight do not occupy registers.
 // * Scores as in attn_fast_kernel (int8 matrix cores on the key Walsh planes).
