@@ -173,6 +173,85 @@ def main():
         f"kernels mse {enc_mse_ms / max(enc_mse_n, 1):.4f} ms, prod {enc_prod_ms / max(enc_prod_n, 1):.4f} ms")
     del Ke, Ve
 
+    # ---------------- decode (Algorithm 2 records of the same layer) ----------------
+    dec_out = torch.empty((nvec, d), dtype=torch.float32, device="cuda")
+    evq.decode(ev[0], ev[1], ev[2], out=dec_out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        evq.decode(ev[0], ev[1], ev[2], out=dec_out)
+    torch.cuda.synchronize()
+    ddt = (time.perf_counter() - t0) / 3
+    decode = {"value": round(nvec / ddt, 1), "unit": "vectors/s", "ms": round(ddt * 1e3, 4),
+              "workload": f"{nvec} prod 3-bit records, d{d}, to fp32 rows"}
+    log(f"decode: {ddt * 1e3:.3f} ms for {nvec} vectors = {nvec / ddt:.3e} vectors/s")
+    del dec_out, ek, ev
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps
+
+    # ---------------- heterogeneous layers (local / global), encode + decode attention ----------------
+    het = {}
+    for kind in ("local", "global"):
+        L = workloads.HET_LAYERS[kind]
+        hB, hHq, hHkv, hT, hd = L["B"], L["Hq"], L["Hkv"], L["T"], L["d"]
+        hc = workloads.het_layer_cache(kind)
+        hch = synth.outlier_channels(hHkv, hd, 4, L["seeds"]["chan"])
+        Kr = synth.kv_bf16_torch((hB, hHkv, hT, hd), L["seeds"]["K"], hch, "cuda", student_t_nu=workloads.HET_NU).view(-1, hd)
+        Vr = synth.kv_bf16_torch((hB, hHkv, hT, hd), L["seeds"]["V"], hch, "cuda", student_t_nu=workloads.HET_NU).view(-1, hd)
+        hn = Kr.shape[0]
+        kco, kno = torch.empty_like(hc.kcodes).view(hn, -1), torch.empty_like(hc.knorms).view(-1)
+        vco, vno, vgo = torch.empty_like(hc.vcodes).view(hn, -1), torch.empty_like(hc.vnorms).view(-1), torch.empty_like(hc.vgammas).view(-1)
+        het_enc = timed(lambda: (hc.kq.encode(Kr, codes=kco, norms=kno), hc.vq.encode(Vr, codes=vco, norms=vno, gammas=vgo)))
+        del Kr, Vr, kco, kno, vco, vno, vgo
+        tiled = hc.vtiles.shape[2] > 0
+        hl = api.TQ_LAYOUT_TILE32 if tiled else api.TQ_LAYOUT_ROWS
+        hseq = torch.full((hB,), hT, dtype=torch.int32, device="cuda")
+        hout = torch.empty((hB, hHq, hd), dtype=torch.float32, device="cuda")
+        hws = torch.empty((api.attn_decode_ws_bytes(hc.kq, hB, hHq, hHkv, hT, hl),), dtype=torch.uint8, device="cuda")
+        hstep = api.attn_decode_bound(hc.kq, hc.vq, hc.q, hc.kcodes, hc.knorms, hc.vtiles if tiled else hc.vcodes,
+                                      hc.vnorms, hc.vgammas, hseq, 1 / math.sqrt(hd), hout, hws, vlayout=hl)
+        het_att = timed(hstep, reps=10)
+        hpk = hc.packed_bytes() if tiled else int(hc.kcodes.numel() + hc.vcodes.numel() + 2 * (hc.knorms.numel() + hc.vnorms.numel() + hc.vgammas.numel()))
+        het[kind] = {"shape": {"batch": hB, "q_heads": hHq, "kv_heads": hHkv, "seq_len": hT, "head_dim": hd},
+                     "encode_ms": round(het_enc * 1e3, 4), "encode_vectors_per_s": round(2 * hn / het_enc, 1),
+                     "attn_ms": round(het_att * 1e3, 4), "attn_packed_bytes": hpk,
+                     "attn_gbs": round(hpk / het_att / 1e9, 2),
+                     "attn_kernel": "attn_fast_kernel (token-tiled values)" if tiled else "attn_split_kernel (row records)"}
+        log(f"{kind} layer: encode {het_enc * 1e3:.3f} ms ({2 * hn} vectors), attention {het_att * 1e3:.4f} ms "
+            f"({hpk / het_att / 1e9:.1f} GB/s)")
+        del hc, hout, hws
+        torch.cuda.empty_cache()
+
+    # ---------------- search: encode the database, scan + top-10 ----------------
+    SS = workloads.SEARCH
+    X = workloads.search_database()
+    sq = api.Quantizer(SS["d"], SS["bits"], api.TQ_PROD, synth.haar_rotation(SS["d"], SS["seeds"]["pi"]),
+                       synth.gaussian_projection(SS["d"], SS["seeds"]["s"]))
+    sc = torch.empty((SS["n"], sq.code_bytes), dtype=torch.uint8, device="cuda")
+    sn = torch.empty((SS["n"],), dtype=torch.int16, device="cuda")
+    sg = torch.empty((SS["n"],), dtype=torch.int16, device="cuda")
+    s_enc = timed(lambda: sq.encode(X, codes=sc, norms=sn, gammas=sg))
+    del X
+    torch.cuda.empty_cache()
+    Qs = torch.from_numpy(workloads.search_queries()).cuda()
+    s_scan = timed(lambda: sq.score(Qs, sc, sn, sg, k=SS["k"]))
+    s_bytes = int(sc.numel() + 4 * SS["n"])
+    search = {"workload": f"{SS['n']} x d{SS['d']} clustered, prod {SS['bits']}-bit, {SS['queries']} queries, top-{SS['k']}",
+              "encode_ms": round(s_enc * 1e3, 3), "encode_vectors_per_s": round(SS["n"] / s_enc, 1),
+              "scan_topk_ms": round(s_scan * 1e3, 3), "queries_per_s": round(SS["queries"] / s_scan, 1),
+              "pairs_per_s": round(SS["queries"] * SS["n"] / s_scan, 1), "packed_db_bytes": s_bytes}
+    log(f"search: encode {s_enc * 1e3:.2f} ms ({SS['n'] / s_enc:.3e} vectors/s); scan+top-{SS['k']} "
+        f"{s_scan * 1e3:.2f} ms for {SS['queries']} queries ({SS['queries'] * SS['n'] / s_scan:.3e} pairs/s)")
+    del sc, sn, sg, Qs
+    torch.cuda.empty_cache()
+
     # ---------------- CPU oracle on a bounded sample ----------------
     cpu = None
     parity = None
@@ -258,6 +337,9 @@ def main():
                    "mse_kernel_ms": round(enc_mse_ms / max(enc_mse_n, 1), 5),
                    "prod_kernel_ms": round(enc_prod_ms / max(enc_prod_n, 1), 5),
                    "workload": "one layer: batch 8 x 8 kv heads x 32768 tokens x d128; K mse 3-bit + V prod 3-bit"},
+        "decode": decode,
+        "heterogeneous_layers": het,
+        "search": search,
         "parity_sample": parity,
     }
     print(json.dumps(res), flush=True)

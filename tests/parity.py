@@ -132,5 +132,6 @@ def install_oracle_slice(cache, b, g, K, V, kbits=3, vbits=2):
     put(cache.vcodes[b, g], ve["record"])
     put(cache.vnorms[b, g], f16_bits(ve["n_hat"]))
     put(cache.vgammas[b, g], f16_bits(ve["gamma"]))
-    put(cache.vtiles[b, g], oracle.tile_records(ve["record"], d, vbits).view(np.int32))
+    if cache.vtiles.shape[2] > 0:  # caches read through row records carry no tiles
+        put(cache.vtiles[b, g], oracle.tile_records(ve["record"], d, vbits).view(np.int32))
     return ke, ve

@@ -156,3 +156,22 @@ def kv_bf16_torch(shape, seed: int, channels: np.ndarray | None, device, scale: 
                     xb[h][:, ch] = z / torch.sqrt(v / nu)
         x[b] = xb.to(torch.bfloat16)
     return x
+
+
+def clustered_database_torch(n: int, d: int, n_centers: int, sigma: float, seed_centers: int, seed_assign: int,
+                             seed_noise: int, device, chunk: int = 65536):
+    """Same law as clustered_database (the same centres, drawn on the host) with the assignments and
+    noise drawn by torch's generator on `device`: an [n, d] fp32 tensor."""
+    import torch
+    centers = torch.from_numpy(np.random.default_rng(seed_centers).standard_normal((n_centers, d)).astype(np.float32))
+    centers = centers.to(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_assign)
+    assign = torch.randint(0, n_centers, (n,), generator=g, device=device)
+    g.manual_seed(seed_noise)
+    out = torch.empty((n, d), dtype=torch.float32, device=device)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = centers[assign[s:e]] + sigma * torch.randn((e - s, d), generator=g, device=device, dtype=torch.float32)
+        out[s:e] = v / torch.linalg.vector_norm(v, dim=1, keepdim=True)
+    return out
