@@ -241,6 +241,13 @@ ATTN_FAST_CASES = [
     (2, 24, 4, 520, [520, 0], 128, 3, 2),        # 6 heads per kv head: a full and a partial head group
     (1, 4, 1, 192, [130], 128, 3, 2),            # one ring turn, the last step partly valid
     (1, 32, 8, 30000, [29999], 128, 3, 2),       # many steps per wave
+    # head_dim 512 (global-layer shape): Walsh coefficients applied after the matrix cores
+    (1, 8, 1, 1000, [1000], 512, 3, 2),
+    (2, 16, 2, 700, [700, 333], 512, 2, 2),
+    (1, 32, 4, 1100, [1099], 512, 1, 2),
+    (1, 4, 4, 300, [300], 512, 3, 2),            # one head per kv head
+    (1, 4, 1, 400, [399], 256, 3, 2),            # head_dim 256 folded at 3-bit keys
+    (1, 4, 1, 400, [399], 128, 4, 3),            # 4-bit keys, 3-bit values: folded, one wave per SIMD
 ]
 
 

@@ -47,10 +47,23 @@ struct FastAttnArgs {
   int Hq, Hkv, G, nsub, chunk, nsplit;
   float scale_log2, vqjl;
   float vbeta[4];           // Walsh coefficients of the value codebook (odd subsets)
+  float kbeta[8];           // Walsh coefficients of the key codebook (applied after the MFMA when folded)
 };
+
 
 // Walsh subset masks (odd-size subsets of the index bits), enumeration order shared with the host
 __host__ __device__ constexpr int walsh_count(int b) { return 1 << (b - 1); }
+// With many Walsh planes per 128-coordinate block, keep one query image per block and half and apply
+// the Walsh coefficients to the per-plane integer results instead, so the images fit in registers
+__host__ __device__ constexpr bool fold_beta(int D, int KB) { return walsh_count(KB) * (D / 128) > 4; }
+__host__ __device__ constexpr int key_images(int D, int KB) {
+  return (fold_beta(D, KB) ? 1 : walsh_count(KB)) * (D / 128) * 2;
+}
+// waves per SIMD the 4-wave kernel is compiled for (registers without spills): also its resident
+// work-groups per CU, one wave per SIMD each
+__host__ __device__ constexpr int fa_waves_per_eu(int D, int KB, int VB) {
+  return D > 256 ? 1 : D > 128 ? (VB >= 2 ? 1 : 2) : (KB == 4 && VB >= 2 ? 1 : (KB == 4 || VB >= 2) ? 2 : 3);
+}
 
 template <int B>
 __device__ __forceinline__ void walsh_planes(const uint32_t *w, uint32_t *out) {
@@ -160,13 +173,14 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
 // value norm and gamma) that moves only when a step exceeds it; the int32
 // accumulators are folded into fp32 then.
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attn_fast_kernel(FastAttnArgs a) {
+__global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_waves_per_eu(D, KB, VB)))) void attn_fast_kernel(FastAttnArgs a) {
   constexpr int KP = walsh_count(KB);        // key Walsh planes
   constexpr int VMP = walsh_count(VB);       // value Walsh planes (index part)
   constexpr int VPL = VB + 1;                // stored value planes per tile
   constexpr int KW = D / 32;                 // 32-bit words per key plane
   constexpr int KWL = KB * (D / 128);        // key words per lane per 16-token group
-  constexpr int NINS = KP * (D / 128) * 2;   // key-side MFMAs per 16 tokens
+  constexpr int NINS = key_images(D, KB);    // query operand images
+  constexpr bool FOLD = fold_beta(D, KB);    // Walsh coefficients applied after the MFMA
   constexpr int NTW = D / 64;                // value column tiles per wave
   constexpr int KCB = KB * D / 8;            // key record bytes
   constexpr float WMAX = 268435328.f;        // 2^28 - 128: largest fp32 whose top 7-bit digit is 127
@@ -259,7 +273,9 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     float sc[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      intx4 cacc = {0, 0, 0, 0};
+      intx4 cacc[FOLD ? KP : 1];
+#pragma unroll
+      for (int p = 0; p < (FOLD ? KP : 1); ++p) cacc[p] = intx4{0, 0, 0, 0};
 #pragma unroll
       for (int wb = 0; wb < D / 128; ++wb) {
         uint32_t w[KB];
@@ -274,12 +290,19 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
             intx4 bb;
 #pragma unroll
             for (int r = 0; r < 4; ++r) bb[r] = (int)(wp[p] & (0x01010101u << (4 * half + r)));
-            cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[(p * (D / 128) + wb) * 2 + half], bb, cacc, 0, 0, 0);
+            const int ai = FOLD ? wb * 2 + half : (p * (D / 128) + wb) * 2 + half;
+            cacc[FOLD ? p : 0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ai], bb, cacc[FOLD ? p : 0], 0, 0, 0);
           }
         }
       }
-      sc[grp] = (float)cacc[0] + (float)cacc[1] * (1.f / 128.f) + (float)cacc[2] * (1.f / 16384.f) +
-                (float)cacc[3] * (1.f / 2097152.f);
+      float v = 0.f;
+#pragma unroll
+      for (int p = 0; p < (FOLD ? KP : 1); ++p) {
+        const float x = (float)cacc[p][0] + (float)cacc[p][1] * (1.f / 128.f) + (float)cacc[p][2] * (1.f / 16384.f) +
+                        (float)cacc[p][3] * (1.f / 2097152.f);
+        v = FOLD ? fmaf(2.f * a.kbeta[p], x, v) : x;
+      }
+      sc[grp] = v;
     }
     if (sn < c1) {  // key/norm registers are free now
       fa_load_keys<D, KB>(kw, rk, vo_k, (int)(sn * KCB));
@@ -826,7 +849,8 @@ struct PrepArgs {
 template <int D, int KB>
 __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr int KP = walsh_count(KB);
-  constexpr int NINS = KP * (D / 128) * 2;
+  constexpr int NINS = key_images(D, KB);
+  constexpr bool FOLD = fold_beta(D, KB);
   __shared__ float qs[FA_GMAX][D];
   __shared__ float qp[FA_GMAX][D];
   __shared__ float red[FA_GMAX][2];
@@ -851,9 +875,9 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   // q'_j = sum_k Pi^T[k][j] q_k for the group's heads: thread (slice, j) sums a slice of k for column j
   // (consecutive threads read consecutive entries of a row of Pi^T; the unrolled loop keeps many
   // independent loads in flight), and the slices are added through LDS
-  {
-    constexpr int SL = 256 / D;  // k slices (2 for head_dim 128, 1 for 256)
-    const int j = threadIdx.x % D, sl = threadIdx.x / D;
+  for (int jc = 0; jc < (D > 256 ? D / 256 : 1); ++jc) {
+    constexpr int SL = D >= 256 ? 1 : 256 / D;  // k slices (2 for head_dim 128, else 1)
+    const int j = (threadIdx.x % (D < 256 ? D : 256)) + 256 * jc, sl = D < 256 ? threadIdx.x / D : 0;
     float acc[FA_GMAX] = {0.f, 0.f, 0.f, 0.f};
     constexpr int KS = D / SL, KU = KS < 64 ? KS : 64;
     for (int k0 = sl * KS; k0 < (sl + 1) * KS; k0 += KU) {
@@ -897,6 +921,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   float bmax = 0.f;
 #pragma unroll
   for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
+  if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
   // image
   for (int e = threadIdx.x; e < NINS * 64 * 4; e += 256) {
     const int r = e & 3, lane = (e >> 2) & 63, ins = e >> 8;
@@ -912,7 +937,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
         const int kb = j & 7;
         const float ks = kb == 7 ? -1.f / 128.f : 1.f / (float)(1 << kb);
         int8_t o[4];
-        split4(2.f * a.kbeta[p] * qp[h][j] * ks * sq, o);
+        split4((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * ks * sq, o);
         word |= (uint32_t)(uint8_t)o[sp] << (8 * i);
       }
     }
@@ -991,13 +1016,15 @@ struct FastPlan {
   size_t img_off, info_off, part_off, merge_off, total;
 };
 
-FastPlan fast_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
+FastPlan fast_plan(int D, int KB, int VB, int B, int Hq, int Hkv, int64_t T) {
   FastPlan p{};
   const int G = Hq / Hkv;
   p.nsub = (G + FA_GMAX - 1) / FA_GMAX;
-  p.nins = walsh_count(KB) * (D / 128) * 2;
+  p.nins = key_images(D, KB);
   const int64_t units = (int64_t)B * Hkv * p.nsub;
-  const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(units, 1));
+  // one chunk per resident work-group: long chunks amortise the per-chunk prologue and partials
+  const int64_t slots = (int64_t)device_cus() * fa_waves_per_eu(D, KB, VB);
+  const int64_t want = std::max<int64_t>(1, slots / std::max<int64_t>(units, 1));
   int64_t chunk = (T + want - 1) / want;
   chunk = std::max<int64_t>(4 * FA_SUB, (chunk + FA_SUB - 1) / FA_SUB * FA_SUB);
   p.chunk = (int)std::min<int64_t>(chunk, 1 << 30);
@@ -1041,7 +1068,7 @@ WavePlan wave_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   WavePlan p{};
   const int G = Hq / Hkv;
   const int nsub = (G + FA_GMAX - 1) / FA_GMAX;
-  const int nins = walsh_count(KB) * (D / 128) * 2;
+  const int nins = key_images(D, KB);
   const int64_t units = (int64_t)B * Hkv * nsub;
   const int64_t want = std::max<int64_t>(1, wave_slots(KB) / std::max<int64_t>(units, 1));
   int64_t chunk = (T + want - 1) / want;
@@ -1062,9 +1089,9 @@ WavePlan wave_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 bool fast_supported(int D, int KB, int VB) {
-  if (D != 128 && D != 256) return false;
+  if (D != 128 && D != 256 && D != 512) return false;
   if (KB < 1 || KB > 4 || VB < 1 || VB > 3) return false;
-  return walsh_count(KB) * (D / 128) * 2 <= 16;
+  return key_images(D, KB) <= 16 && (D < 512 || (VB == 1 && KB <= 3));
 }
 
 template <int D, int KB, int VB>
@@ -1083,7 +1110,8 @@ int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, 
 }  // namespace
 
 size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
-  size_t n = fast_plan(D, KB, B, Hq, Hkv, T).total;
+  size_t n = 0;
+  for (int vb = 1; vb <= 3; ++vb) n = std::max(n, fast_plan(D, KB, vb, B, Hq, Hkv, T).total);
   if (wave_supported(D, KB, 1)) n = std::max(n, wave_plan(D, KB, B, Hq, Hkv, T).total);
   return n;
 }
@@ -1097,7 +1125,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
                   void *ws, hipStream_t st) {
   const int D = kq->d, KB = kq->bits, VB = vq->bmse;
   if (!fast_supported(D, KB, VB)) return TQ_ERR_UNSUPPORTED;
-  FastPlan fp = fast_plan(D, KB, B, Hq, Hkv, Tstride);
+  FastPlan fp = fast_plan(D, KB, VB, B, Hq, Hkv, Tstride);
   // the wave-streaming kernel stages 16-byte pieces: sequence rows of the fp16 arrays must stay aligned
   const bool wave = wave_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) && aligned16(knorms) &&
                     aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas);
@@ -1131,6 +1159,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   fa.scale_log2 = scale * 1.4426950408889634f;
   fa.vqjl = vq->qjl_scale;
   for (int i = 0; i < 4; ++i) fa.vbeta[i] = (float)vb64[i];
+  for (int i = 0; i < 8; ++i) fa.kbeta[i] = (float)kb64[i];
   int rc = TQ_ERR_UNSUPPORTED;
   if (wave) {
     {
@@ -1159,6 +1188,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   TQ_FAST(256, 1, 1) TQ_FAST(256, 2, 1) TQ_FAST(256, 3, 1)
   TQ_FAST(256, 1, 2) TQ_FAST(256, 2, 2) TQ_FAST(256, 3, 2)
   TQ_FAST(256, 1, 3) TQ_FAST(256, 2, 3) TQ_FAST(256, 3, 3)
+  TQ_FAST(512, 1, 1) TQ_FAST(512, 2, 1) TQ_FAST(512, 3, 1)
 #undef TQ_FAST
   if (rc != TQ_OK) return rc;
   return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,

@@ -24,8 +24,8 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne_sat(double v) {
   frexp(v, &e);        // v = m 2^e, m in [0.5, 1): unbiased exponent e-1
   int E = e - 1;
   if (E < -14) E = -14;  // subnormal range shares the 2^-24 spacing
-  double ulp = ldexp(1.0, E - 10);
-  double r = rint(v / ulp) * ulp;  // exact scaling, rint rounds half to even
+  // scaling by the power-of-two spacing is exact; rint rounds half to even
+  const double r = ldexp(rint(ldexp(v, 10 - E)), E - 10);
   return __half_as_ushort(__float2half((float)r));  // r is an fp16 value: exact
 }
 

@@ -18,16 +18,19 @@
 //            a_lo b_hi + a_mid b_mid                                    (6 MFMAs)
 // (the dropped cross terms are below 2^-23 of the product).
 //
-// Work split.  A persistent work-group of 4 waves walks 64-row tiles.  Wave w
-// owns output columns [w d/4, (w+1) d/4): its pieces of Pi (and of S Pi^T) stay
-// in registers for the whole launch, so the matrices cross L2 once per
-// work-group.  The row tile is staged whole in LDS (4 threads per row, fp64
-// norm on the way, the next tile's loads in flight behind the contraction).
+// Work split.  A persistent work-group of NW waves (4; 8 for Algorithm 2 at
+// d = 128) walks 64-row tiles.  Wave w owns output columns [w d/NW, (w+1) d/NW):
+// its pieces of Pi (and of S Pi^T) stay in registers for the whole launch, so
+// the matrices cross L2 once per work-group.  The row tile is staged whole in
+// LDS (NW threads per row, fp64 norm on the way, the next tile's loads in
+// flight behind the contraction).
 // The quantizer runs with lane = row over the wave's own columns: the cell index
 // is a binary search over the scaled boundaries, its bits are shifted into one
 // 32-bit word per plane (add-with-carry, no cross-lane traffic), and the words
 // go straight to the record.  The Algorithm 2 residual is split into its pieces
-// once, in LDS, as the operand of the second contraction.
+// once, in LDS, as the operand of the second contraction; its squared norm is
+// accumulated in fp32 (the fp16 gamma tolerates 1e-5 relative), the vector norm
+// in fp64 (the fp16 norm must round exactly as the fp64 value does).
 #pragma once
 
 #include "common.cuh"
@@ -57,13 +60,19 @@ struct EncIn {
 
 // 16-byte alignment lets every fragment access be one ds_read/ds_write_b128 (8 lanes a cycle, conflict-free
 // at the padded strides below) instead of b64 pairs (16 lanes a cycle, two-way conflicts)
+// waves per work-group: Algorithm 2 at d = 128 splits the columns over 8 waves (16 each), which halves
+// the register-resident matrix pieces and lets two waves share each SIMD (one wave's quantizer overlaps
+// the other's matrix-core work); otherwise 4 waves
+__host__ __device__ constexpr int enc_waves(int D, bool PROD) { return PROD && D == 128 ? 8 : 4; }
+
 template <int D, int NPA, bool PROD>
 struct __attribute__((aligned(16))) EncLds {
-  static constexpr int CW = D / 4;
+  static constexpr int NW = enc_waves(D, PROD);
+  static constexpr int CW = D / NW;
   uint16_t a[NPA][EB][D + 8];          // row pieces of the tile
-  float cw[4][EB][CW + 4];             // per-wave transpose: MFMA layout -> lane = row
+  float cw[NW][EB][CW + 4];            // per-wave transpose: MFMA layout -> lane = row
   uint16_t rp[PROD ? 3 : 1][PROD ? EB : 1][D + 8];  // residual pieces (Algorithm 2)
-  double gpart[PROD ? 4 : 1][EB];      // per-wave partial ||r||^2
+  float gpart[PROD ? NW : 1][EB];      // per-wave partial ||r||^2
   float n32[2][EB], nh[2][EB];         // norms by tile parity
 };
 
@@ -246,13 +255,14 @@ __device__ __forceinline__ void quant_coord(float y, const float (&T)[(1 << BM) 
 __device__ __forceinline__ uint32_t shift_in(uint32_t w, bool b) { return (w << 1) | (b ? 1u : 0u); }
 
 template <int XT, int D, bool PROD, int BM>
-__global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs a) {
   constexpr int NPA = EncIn<XT>::NPA, ESZ = EncIn<XT>::ESZ;
-  constexpr int CW = D / 4;        // columns per wave
+  constexpr int NW = enc_waves(D, PROD);
+  constexpr int CW = D / NW;       // columns per wave
   constexpr int NCT = CW / 16;     // 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;      // 32-deep k-steps
   constexpr int L = 1 << BM;
-  constexpr int PER = D / 4;       // staged elements per thread (4 threads per row)
+  constexpr int PER = D / NW;      // staged elements per thread (NW threads per row)
   constexpr int RAW = PER * ESZ / 16;
   static_assert(RAW >= 1, "tile staging");
   __shared__ EncLds<D, NPA, PROD> sh;
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
   for (int k = 0; k < L; ++k) cc[k] = a.cb.c[k];
 
   // ---- staging geometry: row sr, elements [sk, sk + PER) ----
-  const int sr = tid >> 2, sk = (tid & 3) * PER;
+  const int sr = tid / NW, sk = (tid % NW) * PER;
   uint4 raw[RAW];
   auto load_raw = [&](int64_t tile) {
     const int64_t row = tile * EB + sr;
@@ -344,9 +354,9 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
             *reinterpret_cast<uint4 *>(&sh.a[p][sr][sk + i]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
         }
       }
-      ssq += __shfl_xor(ssq, 1, 64);
-      ssq += __shfl_xor(ssq, 2, 64);
-      if ((tid & 3) == 0) {
+#pragma unroll
+      for (int o = 1; o < NW; o <<= 1) ssq += __shfl_xor(ssq, o, 64);
+      if (tid % NW == 0) {
         const double nn = sqrt(ssq);
         const uint16_t h = f64_to_f16_rne_sat(nn);
         sh.n32[buf][sr] = (float)nn;
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
     uint32_t plane[BM];
 #pragma unroll
     for (int p = 0; p < BM; ++p) plane[p] = 0u;
-    double rs = 0.0;
+    float rs = 0.f;  // ||r||^2 over this wave's columns (fp32: gamma is checked to 1e-5 of a midpoint)
 #pragma unroll
     for (int c8 = CW / 8 - 1; c8 >= 0; --c8) {
       const float4 y0 = *reinterpret_cast<const float4 *>(&cw[lane][8 * c8]);
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
         quant_coord<BM, PROD>(ys[e], thr, cc, plane, cv);
         if (PROD) {
           rv[e] = fmaf(-nhat, cv, ys[e]);
-          rs = fma((double)rv[e], (double)rv[e], rs);
+          rs = fmaf(rv[e], rv[e], rs);
         }
       }
       if (PROD) {
@@ -443,9 +453,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncArgs a) {
     // ---- Algorithm 2: gamma, S r = (S Pi^T) r_rot, sign plane ----
     sh.gpart[wave][lane] = rs;
     lds_barrier();  // residual pieces and partial norms complete
-    if (wave == 0 && lane < rows)
-      a.gammas[row0 + lane] =
-          f64_to_f16_rne_sat(sqrt(sh.gpart[0][lane] + sh.gpart[1][lane] + sh.gpart[2][lane] + sh.gpart[3][lane]));
+    if (wave == 0 && lane < rows) {
+      double g2 = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) g2 += (double)sh.gpart[w][lane];
+      a.gammas[row0 + lane] = f64_to_f16_rne_sat(sqrt(g2));
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -489,21 +502,22 @@ int enc_blocks_per_cu() {
   static int cache = 0;
   if (cache > 0) return cache;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, encode_kernel<XT, D, PROD, BM>, 256, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, encode_kernel<XT, D, PROD, BM>, enc_waves(D, PROD) * 64,
+                                                   0) != hipSuccess ||
       blocks <= 0)
     blocks = 1;
   cache = blocks;
   return blocks;
 }
 
-int device_cus();
+
 
 template <int XT, int D, bool PROD, int BM>
 void launch_encode(EncArgs ea, hipStream_t st) {
   ea.ntiles = cdiv64(ea.n, EB);
   const int64_t slots = (int64_t)device_cus() * enc_blocks_per_cu<XT, D, PROD, BM>();
   const unsigned grid = (unsigned)imin64(ea.ntiles, slots);
-  hipLaunchKernelGGL((encode_kernel<XT, D, PROD, BM>), dim3(grid), dim3(256), 0, st, ea);
+  hipLaunchKernelGGL((encode_kernel<XT, D, PROD, BM>), dim3(grid), dim3(enc_waves(D, PROD) * 64), 0, st, ea);
 }
 
 // instantiated per (mode) in the encode translation units

@@ -81,5 +81,6 @@ bool encode_fused_supported(const tq_quantizer *q);
 int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
                      uint16_t *norms, uint16_t *gammas, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
+int device_cus();  // compute units of the current device (cached)
 
 }  // namespace tq

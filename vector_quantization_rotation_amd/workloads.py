@@ -116,7 +116,7 @@ def raw_kv_slice(which: str, b: int, g: int, Hkv: int, T: int, d: int, seeds=ATT
 def het_layer_cache(kind: str, device="cuda") -> AttnCache:
     L = HET_LAYERS[kind]
     return build_attention_cache(L["B"], L["Hq"], L["Hkv"], L["T"], L["d"], 3, 2, seeds=L["seeds"], device=device,
-                                 student_t_nu=HET_NU, tiles=L["d"] <= 256)
+                                 student_t_nu=HET_NU, tiles=True)
 
 
 def search_database(device="cuda") -> torch.Tensor:
