@@ -51,8 +51,6 @@ struct FastAttnArgs {
 };
 
 
-// Walsh subset masks (odd-size subsets of the index bits), enumeration order shared with the host
-__host__ __device__ constexpr int walsh_count(int b) { return 1 << (b - 1); }
 // With many Walsh planes per 128-coordinate block, keep one query image per block and half and apply
 // the Walsh coefficients to the per-plane integer results instead, so the images fit in registers
 __host__ __device__ constexpr bool fold_beta(int D, int KB) { return walsh_count(KB) * (D / 128) > 4; }
@@ -63,21 +61,6 @@ __host__ __device__ constexpr int key_images(int D, int KB) {
 // work-groups per CU, one wave per SIMD each
 __host__ __device__ constexpr int fa_waves_per_eu(int D, int KB, int VB) {
   return D > 256 ? 1 : D > 128 ? (VB >= 2 ? 1 : 2) : (KB == 4 && VB >= 2 ? 1 : (KB == 4 || VB >= 2) ? 2 : 3);
-}
-
-template <int B>
-__device__ __forceinline__ void walsh_planes(const uint32_t *w, uint32_t *out) {
-  if constexpr (B == 1) {
-    out[0] = w[0];
-  } else if constexpr (B == 2) {
-    out[0] = w[0]; out[1] = w[1];
-  } else if constexpr (B == 3) {
-    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[0] ^ w[1] ^ w[2];
-  } else {
-    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[3];
-    out[4] = w[0] ^ w[1] ^ w[2]; out[5] = w[0] ^ w[1] ^ w[3];
-    out[6] = w[0] ^ w[2] ^ w[3]; out[7] = w[1] ^ w[2] ^ w[3];
-  }
 }
 
 // v (|v| <= 127.5) as a1 + a2/2^7 + a3/2^14 + a4/2^21 with int8 terms (|a2..a4| <= 64)
@@ -993,8 +976,6 @@ int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, 
 // ---------------------------------------------------------------------------
 // host dispatch
 // ---------------------------------------------------------------------------
-namespace {
-
 // Walsh coefficients beta_S (odd subsets, enumeration order of walsh_planes) of a symmetric codebook
 void walsh_coeffs(const double *c, int bits, double *beta) {
   static const int subs[4][8] = {{0x1}, {0x1, 0x2}, {0x1, 0x2, 0x4, 0x7}, {0x1, 0x2, 0x4, 0x8, 0x7, 0xB, 0xD, 0xE}};
@@ -1010,6 +991,8 @@ void walsh_coeffs(const double *c, int bits, double *beta) {
     beta[s] = acc / L;
   }
 }
+
+namespace {
 
 struct FastPlan {
   int nsub, nsplit, chunk, nins;

@@ -51,6 +51,26 @@ __device__ __forceinline__ int cell_index(const Codebook &cb, float y, float n) 
   return idx;
 }
 
+// Walsh subset masks (odd-size subsets of the index bits), enumeration order shared with the host
+__host__ __device__ constexpr int walsh_count(int b) { return 1 << (b - 1); }
+
+// Walsh planes of index bit-plane words: the odd-size subsets of the bits, XORed (a symmetric codebook
+// is an odd function of the index bits, so c[idx] = sum_S beta_S prod_{p in S} (2 bit_p - 1))
+template <int B>
+__device__ __forceinline__ void walsh_planes(const uint32_t *w, uint32_t *out) {
+  if constexpr (B == 1) {
+    out[0] = w[0];
+  } else if constexpr (B == 2) {
+    out[0] = w[0]; out[1] = w[1];
+  } else if constexpr (B == 3) {
+    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[0] ^ w[1] ^ w[2];
+  } else {
+    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[3];
+    out[4] = w[0] ^ w[1] ^ w[2]; out[5] = w[0] ^ w[1] ^ w[3];
+    out[6] = w[0] ^ w[2] ^ w[3]; out[7] = w[1] ^ w[2] ^ w[3];
+  }
+}
+
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // integer min/max (the generic device min/max overloads may go through floating point)
 __host__ __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }

@@ -393,11 +393,27 @@ int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norm
 }
 
 
+size_t score_planes_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k);
+bool score_planes_supported(const tq_quantizer *q);
+int run_score_planes(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
+                     const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx,
+                     void *ws, hipStream_t st);
+
 size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k) {
+  if (score_planes_supported(q)) return score_planes_ws_bytes(q, m, n, k);
   const int kq = q->mode == TQ_PROD ? 2 * q->d : q->d;
   size_t b = (((size_t)m * kq * 4) + 255) & ~(size_t)255;
   if (k > 0) b += (size_t)m * n * 4;
   return b;
+}
+
+// rotated queries [Pi q | S q] (the second half for Algorithm 2 only), fp32 [m][kq]
+int rotate_queries(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, float *qrot, hipStream_t st) {
+  const int d = q->d;
+  const bool prod = q->mode == TQ_PROD;
+  const int kq = prod ? 2 * d : d;
+  return gemm("score_qrot", LoadF32{queries, ldq}, LoadRows2{q->pi, prod ? q->s : q->pi, d, d}, EpiStore{qrot, kq}, m,
+              kq, d, st);
 }
 
 int run_topk(const float *scores, int64_t m, int64_t n, int k, float *vals, int64_t *idx, hipStream_t st);
@@ -405,15 +421,15 @@ int run_topk(const float *scores, int64_t m, int64_t n, int k, float *vals, int6
 int run_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, const uint8_t *codes,
               const uint16_t *norms, const uint16_t *gammas, int64_t n, int k, float *scores, int64_t *idx, void *ws,
               size_t ws_bytes, hipStream_t st) {
+  // bit planes on the int8 matrix cores where the shape allows; otherwise dequantizing fp32 GEMMs
+  if (score_planes_supported(q))
+    return run_score_planes(q, queries, m, ldq, codes, norms, gammas, n, k, scores, idx, ws, st);
   const int d = q->d;
   const bool prod = q->mode == TQ_PROD;
   const int kq = prod ? 2 * d : d;
   float *qrot = static_cast<float *>(ws);
   int rc;
-  // rotated queries [Pi q | S q]
-  if ((rc = gemm("score_qrot", LoadF32{queries, ldq}, LoadRows2{q->pi, prod ? q->s : q->pi, d, d}, EpiStore{qrot, kq}, m, kq, d,
-                 st)) != TQ_OK)
-    return rc;
+  if ((rc = rotate_queries(q, queries, m, ldq, qrot, st)) != TQ_OK) return rc;
   if (n == 0) return TQ_OK;
   float *dst = scores;
   if (k > 0) dst = reinterpret_cast<float *>(static_cast<char *>(ws) + ((((size_t)m * kq * 4) + 255) & ~(size_t)255));

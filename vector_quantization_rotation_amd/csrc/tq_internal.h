@@ -82,5 +82,8 @@ int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, in
                      uint16_t *norms, uint16_t *gammas, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
 int device_cus();  // compute units of the current device (cached)
+// Walsh coefficients beta_S of a symmetric 2^bits-level codebook over the odd-size subsets of the index
+// bits (enumeration order of walsh_planes): c[idx] = sum_S beta_S prod_{p in S} (2 bit_p - 1)
+void walsh_coeffs(const double *c, int bits, double *beta);
 
 }  // namespace tq
