@@ -51,7 +51,10 @@ def test_attention_full_size_sampled(cache):
     from vector_quantization_rotation_amd import api
     G = HQ // HKV
     refs = {}
-    for (b, g) in [(0, 0), (7, 3), (15, 7)]:
+    # (7, 1), (9, 4), (11, 4), (13, 1): slices where value weights far below a chunk's maximum round
+    # to zero on the integer weight grid; with the value sums taken from the rounded weights the
+    # error stays ~4e-5 (summing the exact weights instead left a 5.8e-4 bias there)
+    for (b, g) in [(0, 0), (7, 3), (15, 7), (7, 1), (9, 4), (11, 4), (13, 1)]:
         K, V = _raw_slice("K", b, g), _raw_slice("V", b, g)
         ke, ve = parity.install_oracle_slice(cache, b, g, K, V)
         Kt = oracle.decode_mse(ke["idx"], ke["n_hat"], cache.piK, ke["c"])
@@ -66,6 +69,7 @@ def test_attention_full_size_sampled(cache):
         err = parity.rel_rows(out[b, g * G:(g + 1) * G], ref)
         worst = max(worst, float(err.max()))
         assert np.all(err <= parity.RTOL), (b, g, err)
+        assert np.all(err <= 2e-4), (b, g, err)  # the kernel's arithmetic bound, ten times inside the gate
     print(f"full-size attention: max rel err over sampled slices {worst:.2e}")
 
 

@@ -263,6 +263,49 @@ def test_attn_decode_tiled_parity(api, B, Hq, Hkv, T, seq, d, kb, vb):
         print(f"tiled attention case b={b}: max rel err {err.max():.2e}")
 
 
+@pytest.mark.parametrize("T,layout", [(30000, 1), (30000, 0), (4096, 1)])
+def test_attn_peaked_softmax_long_tail(api, T, layout):
+    """One dominant token and a tail of T - 1 tokens with equal keys whose softmax weight relative to
+    the maximum is 3e-8, below the integer weight grid of the token-tiled kernels: the chunk holding
+    the dominant token rounds its tail weights to zero, the other chunks keep them (each chunk has its
+    own maximum).  Held to 2e-4, ten times inside the gate.  (The long-chunk case, where dropped
+    weights could bias the value sums, is held to the same bound in the full-size attention test.)"""
+    d, Hq, Hkv = 128, 4, 1
+    rng = np.random.default_rng(77)
+    xa, xb = rng.standard_normal((2, d)).astype(np.float32)
+    K = np.repeat(xb[None], T, axis=0)
+    K[7] = xa
+    K = synth.round_bf16(K)
+    V = synth.bf16_bits_to_f32(synth.kv_bf16((1, Hkv, T, d), 79)).reshape(-1, d)
+    piK, piV, sV = synth.haar_rotation(d, 80), synth.haar_rotation(d, 81), synth.gaussian_projection(d, 82)
+    ke = parity.oracle_mse(K, piK, 3)
+    ve = parity.oracle_prod(V, piV, sV, 2)
+    Kt = oracle.decode_mse(ke["idx"], ke["n_hat"], piK, ke["c"])
+    Vt = oracle.decode_prod(ve["idx"], ve["n_hat"], ve["signs"], ve["gamma"], piV, sV, ve["c"])
+    # score gap s_7 - s_tail = ln(1 / 3e-8) along the difference of the two decoded keys, per head a
+    # small shift of the common part
+    diff = Kt[7] - Kt[0]
+    lam = math.log(1.0 / 3e-8) * math.sqrt(d) / float(diff @ diff)
+    q = np.stack([lam * diff + 0.01 * h * rng.standard_normal(d) for h in range(Hq)])[None].astype(np.float32)
+    ref = oracle.decode_attention(q, Kt.reshape(1, Hkv, T, d), Vt.reshape(1, Hkv, T, d), np.array([T]),
+                                  1.0 / math.sqrt(d))
+    kq = api.Quantizer(d, 3, api.TQ_MSE, piK)
+    vq = api.Quantizer(d, 2, api.TQ_PROD, piV, sV)
+    if layout == api.TQ_LAYOUT_TILE32:
+        vsrc = _dev(oracle.tile_records(ve["record"], d, 2).view(np.int32)).view(1, Hkv, -1, 2, d)
+    else:
+        vsrc = _dev(ve["record"]).view(1, Hkv, T, -1)
+    out = api.attn_decode(kq, vq, _dev(q), _dev(ke["record"]).view(1, Hkv, T, -1),
+                          _dev(parity.f16_bits(ke["n_hat"])).view(1, Hkv, T), vsrc,
+                          _dev(parity.f16_bits(ve["n_hat"])).view(1, Hkv, T),
+                          _dev(parity.f16_bits(ve["gamma"])).view(1, Hkv, T),
+                          torch.tensor([T], dtype=torch.int32, device="cuda"), 1.0 / math.sqrt(d),
+                          vlayout=layout).cpu().numpy()
+    err = parity.rel_rows(out[0], ref[0])
+    print(f"peaked softmax T={T} layout={layout}: max rel err {err.max():.2e}")
+    assert np.all(err <= 2e-4), err
+
+
 def test_tile_records_matches_oracle(api):
     d, T = 128, 100
     x = synth.unit_test_vectors(3 * T, d, 51, 52)

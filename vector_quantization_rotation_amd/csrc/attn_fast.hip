@@ -343,6 +343,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
     {
       const float sm = vn_ref > 0.f ? WMAX * kscale / vn_ref : 0.f;
       const float sq = vg_ref > 0.f ? WMAX * kscale / vg_ref : 0.f;
+      const float ism = sm > 0.f ? 1.f / sm : 0.f, isq = sq > 0.f ? 1.f / sq : 0.f;
       uint32_t dm[4] = {0u, 0u, 0u, 0u}, dq[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
@@ -350,9 +351,10 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
         const float p = exp2f(sc[grp] - m_ref);
         const float wm = p * s_norm[wave][0][tw], wq = p * s_norm[wave][1][tw];
         l_run += p;
-        ym_run += wm;
-        yq_run += wq;
         const uint32_t um = __float2uint_rn(wm * sm), uq = __float2uint_rn(wq * sq);
+        // value sums from the rounded weights the matrix cores use (see the wave-streaming kernel)
+        ym_run = fmaf((float)um, ism, ym_run);
+        yq_run = fmaf((float)uq, isq, yq_run);
         dm[0] |= (um >> 21) << (8 * grp);
         dm[1] |= ((um >> 14) & 127u) << (8 * grp);
         dm[2] |= ((um >> 7) & 127u) << (8 * grp);
@@ -619,6 +621,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int kofs = 4 * (hl & 1);
   int since_fold = 0;
   float sm_l = 0.f, sq_l = 0.f;  // weight scales WV_WMAX 2^-r / (largest n_V, gamma_V so far)
+  float ism_l = 0.f, isq_l = 0.f;  // their inverses (0 while a scale is 0)
 
   // one step over the stage in `st` (a fixed ring slot after inlining)
   auto body = [&, rk, rkn, rvn, rvg, rv](uint8_t *st, int s) {
@@ -739,6 +742,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       vg_ref = fmaxf(vg_ref, vgm);
       sm_l = vn_ref > 0.f ? WV_WMAX * kscale / vn_ref : 0.f;
       sq_l = vg_ref > 0.f ? WV_WMAX * kscale / vg_ref : 0.f;
+      ism_l = sm_l > 0.f ? 1.f / sm_l : 0.f;
+      isq_l = sq_l > 0.f ? 1.f / sq_l : 0.f;
       since_fold = 0;
     }
     // ---- weights: p n and p gamma as integers below 2^23, three signed byte digits per token ----
@@ -750,10 +755,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         const float p = __builtin_amdgcn_exp2f(sc[grp] - m_ref);
         const float wm = p * fvn[grp], wq = p * fvg[grp];
         l_run += p;
-        ym_run += wm;
-        yq_run += wq;
-        um[grp] = wv_weight(wm, sm_l);
-        uq[grp] = wv_weight(wq, sq_l);
+        // the value sums take the rounded weights the matrix cores use, so a weight that rounds to
+        // zero drops out of both terms of 2 acc - Y (an error of zero mean) instead of biasing every column
+        const float fm = fmaf(wm, sm_l, WV_MAGIC), fq = fmaf(wq, sq_l, WV_MAGIC);
+        ym_run = fmaf(fm - WV_MAGIC, ism_l, ym_run);
+        yq_run = fmaf(fq - WV_MAGIC, isq_l, yq_run);
+        um[grp] = __float_as_uint(fm) ^ 0x808080u;
+        uq[grp] = __float_as_uint(fq) ^ 0x808080u;
       }
       uint32_t dm[3], dq[3];
       wv_digits(um, dm);
