@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-slices", type=int, default=24, help="(batch, kv-head) slices the oracle times")
+    ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()

@@ -11,6 +11,7 @@
 // fp32 operands keep the rotated coordinates within ~1e-7 of their norm scale,
 // far inside the 1e-5 tie zone the codes are checked against.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.cuh"
 
@@ -244,6 +245,161 @@ static int gemm(const char *name, LA la, LB lb, EP ep, int64_t M, int64_t N, int
 }
 
 // ----------------------------------------------------------------------------
+// the tiled contraction on the bf16 matrix cores with exact pieces (encode at d > 128)
+//
+// C = A B^T with the fp32 A values (from a loader) split exactly into NPA bf16
+// pieces on the fly (truncation: hi keeps 8 significant bits, mid the next 8,
+// lo the rest; bf16 inputs are one piece, fp16 two) and B given as its three
+// pre-split pieces [3][N][K].  Products of pieces are exact in fp32; the dropped
+// cross terms are below 2^-23 of the product, so C is fp32-accurate (the codes
+// are checked against the fp64 definition with a 1e-5 tie zone).  A 128 x 128
+// tile per work-group, each wave a 64 x 64 quadrant (4 x 4 MFMA tiles), 32-deep
+// k-steps staged in LDS with the next step's loads in registers; the epilogues
+// of the fp32 kernel run once per quadrant.
+// ----------------------------------------------------------------------------
+constexpr int PBM = 128, PBN = 128, PBK = 32, PKP = 40;
+
+typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
+
+// upper halves of two exact-bf16 floats as one dword (lo element first)
+__device__ __forceinline__ uint32_t g_pack2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+template <int NPA>
+__device__ __forceinline__ void g_split(float x, float (&p)[3]) {
+  p[0] = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
+  const float r1 = x - p[0];
+  p[1] = NPA == 2 ? r1 : __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+  p[2] = r1 - p[1];
+}
+
+template <int NPA>
+__device__ __forceinline__ floatx4 g_terms(const gbf16x8 (&a)[3], const gbf16x8 (&b)[3], floatx4 c) {
+#define TQ_MF(i, j) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], c, 0, 0, 0)
+  if (NPA == 1) {
+    TQ_MF(0, 2); TQ_MF(0, 1); TQ_MF(0, 0);
+  } else if (NPA == 2) {
+    TQ_MF(1, 1); TQ_MF(0, 2); TQ_MF(1, 0); TQ_MF(0, 1); TQ_MF(0, 0);
+  } else {
+    TQ_MF(1, 1); TQ_MF(2, 0); TQ_MF(0, 2); TQ_MF(1, 0); TQ_MF(0, 1); TQ_MF(0, 0);
+  }
+#undef TQ_MF
+  return c;
+}
+
+template <int NPA, class LA, class EP>
+__global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N,
+                                                          int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[NPA][PBM][PKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][PBN][PKP];
+  __shared__ float Cs[GBM][GBN + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t row0 = (int64_t)blockIdx.x * PBM, col0 = (int64_t)blockIdx.y * PBN;
+  const int ar = tid >> 1, ak = (tid & 1) * 16;  // A staging: row ar, k ak..ak+15
+  const bool arow_ok = row0 + ar < M;
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[NPA][2], rb[6];
+  auto gload = [&](int k0) {
+    float v[16];
+    if (arow_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) la(row0 + ar, k0 + ak + 4 * i, v + 4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[3][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float p0[3], p1[3];
+        g_split<NPA>(v[8 * h + 2 * q], p0);
+        g_split<NPA>(v[8 * h + 2 * q + 1], p1);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) w[p][q] = g_pack2(p0[p], p1[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < NPA; ++p) ra[p][h] = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
+      const int64_t col = col0 + br;
+      rb[i] = col < N ? *reinterpret_cast<const uint4 *>(b3 + ((int64_t)p * N + col) * K + k0 + kk)
+                      : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int p = 0; p < NPA; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = ra[p][h];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
+      *reinterpret_cast<uint4 *>(&Bs[p][br][kk]) = rb[i];
+    }
+  };
+
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  gload(0);
+  for (int k0 = 0; k0 < K; k0 += PBK) {
+    __syncthreads();  // the previous step's fragments are consumed
+    lstore();
+    __syncthreads();
+    if (k0 + PBK < K) gload(k0 + PBK);  // in flight during this step's MFMAs
+    gbf16x8 af[4][3];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        af[rt][p] = p < NPA ? *reinterpret_cast<const gbf16x8 *>(&As[p][64 * wm + 16 * rt + fr][fk]) : af[rt][0];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      gbf16x8 bf[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) bf[p] = *reinterpret_cast<const gbf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms<NPA>(af[rt], bf, acc[rt][ct]);
+    }
+  }
+  // one quadrant at a time through the 64 x 64 epilogue tile
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    __syncthreads();
+    if (wave == qd) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Cs[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[rt][ct][e];
+    }
+    __syncthreads();
+    const int64_t qr0 = row0 + 64 * (qd >> 1), qc0 = col0 + 64 * (qd & 1);
+    if (qr0 < M && qc0 < N) ep(Cs, qr0, qc0, M, N);
+  }
+}
+
+template <int NPA, class LA, class EP>
+static int gemm_pieces(const char *name, LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N, int K,
+                       hipStream_t st) {
+  if (M <= 0 || N <= 0) return TQ_OK;
+  dim3 grid((unsigned)cdiv64(M, PBM), (unsigned)cdiv64(N, PBN));
+  ProfScope ps(name, st);
+  hipLaunchKernelGGL((gemm_pieces_kernel<NPA, LA, EP>), grid, dim3(256), 0, st, la, b3, ep, M, N, K);
+  return launch_check();
+}
+
+// ----------------------------------------------------------------------------
 // small kernels: norms, zero fill, gamma finalisation, M = S Pi^T
 // ----------------------------------------------------------------------------
 template <int XT>
@@ -329,13 +485,13 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
   }
   EpiQuant eq{codes, (int64_t)q->code_bytes, d, q->bmse, n32, norms, prod ? resid : nullptr, prod ? rsq : nullptr,
               q->cb};
-  LoadF32 lpi{q->pi, d};
-  if ((rc = gemm("encode_rotate", lx, lpi, eq, cn, d, d, st)) != TQ_OK) return rc;
+  // exact bf16 pieces on the matrix cores: bf16 rows are one piece, fp16 two, fp32 three
+  constexpr int NPA = std::is_same<LX, LoadBF16>::value ? 1 : std::is_same<LX, LoadF16>::value ? 2 : 3;
+  if ((rc = gemm_pieces<NPA>("encode_rotate", lx, q->pi3, eq, cn, d, d, st)) != TQ_OK) return rc;
   if (!prod) return TQ_OK;
   LoadF32 lr{resid, d};
-  LoadF32 lm{q->m, d};
   EpiSign es{codes, (int64_t)q->code_bytes, d, q->planes - 1};
-  if ((rc = gemm("encode_qjl", lr, lm, es, cn, d, d, st)) != TQ_OK) return rc;
+  if ((rc = gemm_pieces<3>("encode_qjl", lr, q->m3, es, cn, d, d, st)) != TQ_OK) return rc;
   hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, cn, gammas);
   return launch_check();
 }
