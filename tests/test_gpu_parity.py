@@ -108,7 +108,10 @@ def test_decode_parity(api, mode, bits):
     out = qz.decode(codes, norms, gammas).cpu().numpy()
     err = parity.rel_rows(out, ref)
     assert np.all(err <= parity.RTOL), err.max()
-    assert err.max() < 1e-5  # fp32 contraction: far inside the gate
+    # the kernel's own arithmetic bound, far inside the gate: each product carries the top 16 significant
+    # bits of both operands (head dims up to 128: two bf16 pieces; three dropped terms of <= 2^-16 each);
+    # the fp32 GEMM path of larger head dims is tighter still
+    assert err.max() < 1e-4
 
 
 @pytest.mark.parametrize("mode,bits", [("mse", 2), ("prod", 3)])

@@ -540,6 +540,9 @@ int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t 
 
 int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas, int64_t n,
                float *out, int64_t ldo, hipStream_t st) {
+  // head dims up to 128: one fused kernel on the bf16 matrix cores
+  if (decode_fused_supported(q) && (reinterpret_cast<uintptr_t>(codes) & 3) == 0)
+    return run_decode_fused(q, codes, norms, gammas, n, out, ldo, st);
   const int d = q->d;
   const bool prod = q->mode == TQ_PROD;
   LoadDequant ld{codes, norms, gammas, (int64_t)q->code_bytes, d, q->bmse, q->qjl_scale, q->cb};

@@ -132,6 +132,8 @@ void free_q(tq_quantizer *q) {
   hipFree(q->m);
   hipFree(q->pi3);
   hipFree(q->m3);
+  hipFree(q->pit3);
+  hipFree(q->st3);
   if (prev >= 0) hipSetDevice(prev);
   delete q;
 }
@@ -229,6 +231,12 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
   }
   if (rc == TQ_OK) rc = dev_upload<uint16_t>(&q->pi3, nullptr, 3 * dd);
   if (rc == TQ_OK) rc = tq::make_pieces(q->pi, (int64_t)dd, q->pi3, nullptr);
+  if (rc == TQ_OK && d <= 128) {  // the fused decode's register-resident matrices
+    rc = dev_upload<uint16_t>(&q->pit3, nullptr, 3 * dd);
+    if (rc == TQ_OK) rc = tq::make_pieces(q->piT, (int64_t)dd, q->pit3, nullptr);
+    if (rc == TQ_OK && mode == TQ_PROD) rc = dev_upload<uint16_t>(&q->st3, nullptr, 3 * dd);
+    if (rc == TQ_OK && mode == TQ_PROD) rc = tq::make_pieces(q->sT, (int64_t)dd, q->st3, nullptr);
+  }
   if (rc == TQ_OK) {
     e = hipDeviceSynchronize();
     if (e != hipSuccess) rc = tq::hip_fail(e);

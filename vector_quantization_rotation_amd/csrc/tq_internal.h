@@ -41,6 +41,8 @@ struct tq_quantizer {
   // bf16 pieces [3][d][d] (hi, mid, lo; exact splits of the fp32 entries) for the bf16 matrix cores
   uint16_t *pi3 = nullptr;  // of Pi
   uint16_t *m3 = nullptr;   // of S Pi^T (TQ_PROD)
+  uint16_t *pit3 = nullptr; // of Pi^T (decode, head dims up to 128)
+  uint16_t *st3 = nullptr;  // of S^T (decode, TQ_PROD, head dims up to 128)
 };
 
 namespace tq {
@@ -82,6 +84,9 @@ int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, in
                      uint16_t *norms, uint16_t *gammas, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
 int device_cus();  // compute units of the current device (cached)
+bool decode_fused_supported(const tq_quantizer *q);
+int run_decode_fused(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas,
+                     int64_t n, float *out, int64_t ldo, hipStream_t st);
 // Walsh coefficients beta_S of a symmetric 2^bits-level codebook over the odd-size subsets of the index
 // bits (enumeration order of walsh_planes): c[idx] = sum_S beta_S prod_{p in S} (2 bit_p - 1)
 void walsh_coeffs(const double *c, int bits, double *beta);
