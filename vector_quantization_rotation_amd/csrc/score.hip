@@ -28,10 +28,12 @@
 //
 // Contraction order: the matrix cores sum over the 64 k-slots of a step in any
 // order as long as both operands agree, so the coordinates are dealt to the
-// slots by super-steps of SPS steps: lane group g of step u in a super-step
-// takes coordinates 16 SPS g + 16 u + (0..15).  A lane then reads its bits of a
-// whole super-step as one contiguous 2 SPS-byte word per plane, prefetched a
-// super-step ahead.
+// slots by super-steps of SPS steps: lane group g owns 16 SPS contiguous
+// coordinates of a super-step, which it reads as one 2 SPS-byte word per plane,
+// prefetched a super-step ahead.  With whole 32-bit words (SPS >= 2) a step
+// takes one nibble half of a word and each B register is that word ANDed with
+// 0x01010101 << r: bytes of value 2^r (r < 4), whose 2^-r the query images
+// carry (1 shift and 4 ANDs per fragment instead of spreading bits to bytes).
 #include <algorithm>
 
 #include "common.cuh"
@@ -75,6 +77,7 @@ struct SuperBits<2> {
   uint32_t w;
   __device__ __forceinline__ void load(const uint8_t *p) { w = *reinterpret_cast<const uint32_t *>(p); }
   __device__ __forceinline__ uint32_t step(int u) const { return (w >> (16 * u)) & 0xFFFFu; }
+  __device__ __forceinline__ uint32_t nib(int u) const { return w >> (4 * u); }
 };
 template <>
 struct SuperBits<4> {
@@ -85,6 +88,7 @@ struct SuperBits<4> {
     w1 = v.y;
   }
   __device__ __forceinline__ uint32_t step(int u) const { return ((u < 2 ? w0 : w1) >> (16 * (u & 1))) & 0xFFFFu; }
+  __device__ __forceinline__ uint32_t nib(int u) const { return (u < 2 ? w0 : w1) >> (4 * (u & 1)); }
 };
 
 template <bool PROD, int BM, int SPS>
@@ -154,7 +158,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int rb = 0; rb < 4; ++rb) {
         uint32_t w[NPL];
 #pragma unroll
-        for (int p = 0; p < NPL; ++p) w[p] = bcur[rb][p].step(u);
+        for (int p = 0; p < NPL; ++p) {
+          if constexpr (SPS == 1) w[p] = bcur[rb][p].step(u);
+          else w[p] = bcur[rb][p].nib(u);
+        }
         walsh_planes<BM>(w, wpl[rb]);
         if (PROD) wpl[rb][KP] = w[BM];
       }
@@ -166,7 +173,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         for (int qb = 0; qb < 4; ++qb) af[qb] = As[buf][s][qb][lane];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const intx4 bf = spread_bits16(wpl[rb][s]);
+          // SPS >= 2: nibble position r of each byte of the lane's word (bytes 2^r; the images carry 2^-r)
+          const uint32_t x = wpl[rb][s];
+          const intx4 bf = SPS == 1 ? spread_bits16(x)
+                                    : intx4{(int)(x & 0x01010101u), (int)(x & 0x02020202u), (int)(x & 0x04040404u),
+                                            (int)(x & 0x08080808u)};
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb) {
             if (PROD && s == KP) accq[qb][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[qb], bf, accq[qb][rb], 0, 0, 0);
@@ -263,10 +274,15 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScorePrepArgs a) {
   const int qb = (int)(q % SC_Q) / 8, qi = (int)(q % 8);
   for (int e = threadIdx.x; e < a.nsteps * nimg * SC_K; e += 256) {
     const int k = e % SC_K, s = (e / SC_K) % nimg, st = e / (SC_K * nimg);
-    // coordinate of slot k of step st (super-step order: lane group k / 16 of step u takes 16 sps g + 16 u + i)
-    const int j = (st / a.sps) * SC_K * a.sps + 16 * a.sps * (k / 16) + 16 * (st % a.sps) + (k % 16);
+    // coordinate of slot k of step st.  sps == 1: lane group g = k / 16 takes coordinates 16 g + (k % 16)
+    // of the step, bytes 0/1.  sps >= 2: lane group g owns 16 sps coordinates of the super-step (sps / 2
+    // words); step u reads nibble half u % 2 of word u / 2, and slot 4 r + j of the group (r, j < 4) holds
+    // bit 8 j + r + 4 (u % 2) of that word as a byte of value 2^r, so its image carries 2^-r
+    const int g = k / 16, i = k % 16, u = st % a.sps, r = a.sps == 1 ? 0 : i / 4;
+    const int j = a.sps == 1 ? st * SC_K + 16 * g + i
+                             : (st / a.sps) * SC_K * a.sps + 16 * a.sps * g + 32 * (u / 2) + 8 * (i % 4) + r + 4 * (u % 2);
     float v = 0.f;
-    if (valid) v = s < a.kp ? 2.f * a.beta[s] * qp[j] * scm : qp[a.d + j] * scq;
+    if (valid) v = (s < a.kp ? 2.f * a.beta[s] * qp[j] * scm : qp[a.d + j] * scq) * (1.f / (float)(1 << r));
     const float a1 = rintf(v), a2 = rintf((v - a1) * 128.f);
     int8_t *frag = a.img + ((((group * a.nsteps + st) * nimg + s) * 4 + qb) * 64) * 16;
     frag[(2 * qi + 0 + 16 * (k / 16)) * 16 + (k % 16)] = (int8_t)(int)a1;
