@@ -145,6 +145,10 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
   }
 }
 
+constexpr float FA_SLACK = 1.f;     // score headroom above the reference maximum (log2 units)
+constexpr float FA_NCAP = 1.25f;   // norm and gamma caps: this times the largest seen
+constexpr float FA_HEADROOM = 2.f;  // 2^FA_SLACK
+
 // D: head dim; KB: key index bits; VB: value index bits (Algorithm-2 records hold VB+1 planes)
 //
 // Work-group = 4 waves over one (batch, kv head, head group, sequence chunk),
@@ -152,9 +156,11 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
 // (all heads), writes their int8 weight digits to LDS, and after a barrier
 // aggregates all 256 tokens for its quarter of the value columns.  The next
 // step's key words, norms and value words are loaded while the current step
-// runs.  Softmax weights are scaled by a reference (running maximum, largest
-// value norm and gamma) that moves only when a step exceeds it; the int32
-// accumulators are folded into fp32 then.
+// runs.  Softmax weights are scaled by a reference (running maximum, value norm
+// and gamma caps) with headroom: scores may exceed the maximum by FA_SLACK
+// (log2 units), the caps are FA_NCAP times the largest norm and gamma seen, and the
+// weight scale is divided by 2^FA_SLACK.  The reference moves only when a step
+// leaves that headroom; the int32 accumulators are folded into fp32 then.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_waves_per_eu(D, KB, VB)))) void attn_fast_kernel(FastAttnArgs a) {
   constexpr int KP = walsh_count(KB);        // key Walsh planes
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       const int tw = tbase + 8 * grp;
       const bool ok = head_ok && (wbase + tw) < c1;
       sc[grp] = ok ? (sc[grp] * qinv - qconst) * s_kn[wave][tw] * a.scale_log2 : -INFINITY;
-      over = over || sc[grp] > m_ref;
+      over = over || sc[grp] > m_ref + FA_SLACK;
     }
     const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0ull;  // every lane votes
     if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       }
       const float m_new = fmaxf(m_ref, step_m);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
-      const float im = vn_ref / WMAX, iq = vg_ref / WMAX;
+      const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
 #pragma unroll
       for (int p = 0; p <= VMP; ++p) {
         const float isc = p < VMP ? im : iq;
@@ -336,13 +342,13 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       ym_run *= alpha;
       yq_run *= alpha;
       m_ref = m_new;
-      vn_ref = fmaxf(vn_ref, step_vn);
-      vg_ref = fmaxf(vg_ref, step_vg);
+      vn_ref = fmaxf(vn_ref, FA_NCAP * step_vn);
+      vg_ref = fmaxf(vg_ref, FA_NCAP * step_vg);
     }
-    // ---- weights: p = 2^(s - m_ref) <= 1; p n and p gamma as four 7-bit digits, one dword per digit row ----
+    // ---- weights: p = 2^(s - m_ref) <= 2^FA_SLACK; p n and p gamma as four 7-bit digits, one dword per digit row ----
     {
-      const float sm = vn_ref > 0.f ? WMAX * kscale / vn_ref : 0.f;
-      const float sq = vg_ref > 0.f ? WMAX * kscale / vg_ref : 0.f;
+      const float sm = vn_ref > 0.f ? WMAX * kscale / (vn_ref * FA_HEADROOM) : 0.f;
+      const float sq = vg_ref > 0.f ? WMAX * kscale / (vg_ref * FA_HEADROOM) : 0.f;
       const float ism = sm > 0.f ? 1.f / sm : 0.f, isq = sq > 0.f ? 1.f / sq : 0.f;
       uint32_t dm[4] = {0u, 0u, 0u, 0u}, dq[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   }
   // ---- final fold, reductions, partial record: m, l, acc_mse[D], acc_qjl[D] ----
   {
-    const float im = vn_ref / WMAX, iq = vg_ref / WMAX;
+    const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
 #pragma unroll
     for (int p = 0; p <= VMP; ++p) {
       const float isc = p < VMP ? im : iq;
@@ -454,11 +460,17 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
 //   permutes.
 // * The value operand shifts each tile word by the lane's 4-token offset so
 //   every byte holds 1, 2, 4 or 8; the weights carry the inverse factor.
-// * The online softmax reference (maximum, largest value norm and gamma) is
-//   per wave; the int32 accumulators are folded (exactly, in fp64) only when a
-//   step exceeds it.
+// * The online softmax reference (maximum, value norm and gamma caps) is per
+//   wave and carries headroom: a score may exceed the reference maximum by
+//   WV_SLACK (log2 units) and the caps are WV_NCAP times the largest norm and
+//   gamma seen, with the weight scale divided by 2^WV_SLACK so the integers stay
+//   below 2^23.  The int32 accumulators are folded (exactly, in fp64) only when
+//   a step leaves that headroom, which after the first step is rare.
 // ---------------------------------------------------------------------------
 constexpr int WV_STEP = 64;
+constexpr float WV_SLACK = 1.f;           // score headroom above the reference maximum (log2 units)
+constexpr float WV_NCAP = 1.25f;          // norm and gamma caps: this times the largest seen
+constexpr float WV_HEADROOM = 2.f;        // 2^WV_SLACK
 constexpr int WV_RING = 3;                // ring slots: stages s+1 and s+2 are in flight while s is used
 constexpr float WV_WMAX = 8388352.f;      // 2^23 - 256: weights are integers below 2^23 (see wv_weight)
 constexpr float WV_MAGIC = 8388608.f;     // 2^23
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       fvn[grp] = valid ? fvn[grp] : 0.f;
       fvg[grp] = valid ? fvg[grp] : 0.f;
       sc[grp] = (head_ok && valid) ? s_ : -INFINITY;
-      over = over || sc[grp] > m_ref || fvn[grp] > vn_ref || fvg[grp] > vg_ref;
+      over = over || sc[grp] > m_ref + WV_SLACK || fvn[grp] > vn_ref || fvg[grp] > vg_ref;
     }
     ++since_fold;
     if ((__builtin_amdgcn_ballot_w64(over) != 0ull) || since_fold >= 16384) {
@@ -726,7 +738,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       const float vgm = wave_max_f32(fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3])));
       const float m_new = fmaxf(m_ref, smax);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
-      const double im = (double)vn_ref / WV_WMAX, iq = (double)vg_ref / WV_WMAX;
+      const double im = (double)vn_ref * WV_HEADROOM / WV_WMAX, iq = (double)vg_ref * WV_HEADROOM / WV_WMAX;
 #pragma unroll
       for (int c = 0; c < NTC; ++c) {
         accf[0][c] = (accf[0][c] + (float)(wv_fold(vacc[0][c]) * im)) * alpha;
@@ -738,10 +750,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       ym_run *= alpha;
       yq_run *= alpha;
       m_ref = m_new;
-      vn_ref = fmaxf(vn_ref, vnm);
-      vg_ref = fmaxf(vg_ref, vgm);
-      sm_l = vn_ref > 0.f ? WV_WMAX * kscale / vn_ref : 0.f;
-      sq_l = vg_ref > 0.f ? WV_WMAX * kscale / vg_ref : 0.f;
+      vn_ref = fmaxf(vn_ref, WV_NCAP * vnm);
+      vg_ref = fmaxf(vg_ref, WV_NCAP * vgm);
+      // p <= 2^WV_SLACK and n <= vn_ref, so p n sm_l <= WV_WMAX
+      sm_l = vn_ref > 0.f ? WV_WMAX * kscale / (vn_ref * WV_HEADROOM) : 0.f;
+      sq_l = vg_ref > 0.f ? WV_WMAX * kscale / (vg_ref * WV_HEADROOM) : 0.f;
       ism_l = sm_l > 0.f ? 1.f / sm_l : 0.f;
       isq_l = sq_l > 0.f ? 1.f / sq_l : 0.f;
       since_fold = 0;
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       uint32_t um[4], uq[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        // p = 2^(s - m_ref) <= 1 (hardware exp2: results below 2^-126 flush to zero)
+        // p = 2^(s - m_ref) <= 2^WV_SLACK (hardware exp2: results below 2^-126 flush to zero)
         const float p = __builtin_amdgcn_exp2f(sc[grp] - m_ref);
         const float wm = p * fvn[grp], wq = p * fvg[grp];
         l_run += p;
@@ -802,7 +815,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   }
   // ---- final fold and partial record: m, l, acc_mse[D], acc_qjl[D] ----
   {
-    const double im = (double)vn_ref / WV_WMAX, iq = (double)vg_ref / WV_WMAX;
+    const double im = (double)vn_ref * WV_HEADROOM / WV_WMAX, iq = (double)vg_ref * WV_HEADROOM / WV_WMAX;
 #pragma unroll
     for (int c = 0; c < NTC; ++c) {
       accf[0][c] += (float)(wv_fold(vacc[0][c]) * im);
