@@ -451,7 +451,13 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
 //   direct-to-LDS buffer loads issued two steps ahead (keys as 16-byte
 //   plane rows, value tiles as they lie in HBM, the three fp16 arrays), so the
 //   bytes in flight do not occupy registers.
-// * Scores as in attn_fast_kernel (int8 matrix cores on the key Walsh planes).
+// * Scores on the key Walsh planes as in attn_fast_kernel, but on the fp8 x fp4
+//   matrix-core form (v_mfma_f32_16x16x128_f8f6f4): the query images are four
+//   fixed-point digits per head held as e4m3 (about 20 bits in all, and the
+//   sums the matrix cores form are exact), a key word of 32 coordinates becomes four
+//   fp4 dwords with one AND each (three for nibble bits 0..2, and one more
+//   after a shift for bit 3), so the key bits cost half the vector operations
+//   of byte operands.
 // * Value weights p n and p gamma become 24-bit integers split into three
 //   signed byte digits (the integer XOR 0x808080 reads, byte by byte, as the
 //   digit minus 128); row 3 of each head's four MFMA rows is a row of ones
@@ -561,7 +567,6 @@ template <int KB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_wave_kernel(FastAttnArgs a) {
   constexpr int D = 128;
   constexpr int KP = walsh_count(KB);
-  constexpr int NINS = KP * 2;
   constexpr int KCB = KB * D / 8;
   constexpr int NTC = D / 16;  // value column tiles
   using S = WaveStage<KB>;
@@ -588,11 +593,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int nvalid = c0 < c1 ? (int)((c1 - c0 + WV_STEP - 1) / WV_STEP) : 0;
   const int nsteps = (nvalid + WV_RING - 1) / WV_RING * WV_RING;
 
-  intx4 qa[NINS];
+  // query operand: per key image, 4 heads x 4 e4m3 digits over the 128 coordinates (32 bytes per lane)
+  intx8 qa[KP];
   {
-    const intx4 *img = reinterpret_cast<const intx4 *>(a.qimg) + (int64_t)unit * NINS * 64;
+    const intx8 *img = reinterpret_cast<const intx8 *>(a.qimg) + (int64_t)unit * KP * 64;
 #pragma unroll
-    for (int i = 0; i < NINS; ++i) qa[i] = img[i * 64 + lane];
+    for (int i = 0; i < KP; ++i) qa[i] = img[i * 64 + lane];
   }
   const float qinv = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0];
   const float qconst = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1];
@@ -681,24 +687,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
       for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(vw[p][h].x), "+v"(vw[p][h].y), "+v"(vw[p][h].z), "+v"(vw[p][h].w));
     __builtin_amdgcn_sched_barrier(0);
-    // ---- key pass: the four 16-token groups interleaved, so consecutive MFMAs are independent ----
+    // ---- key pass (fp8 query digits x fp4 key bits, fp32 accumulation): the four 16-token groups
+    // interleaved, so consecutive MFMAs are independent.  A key word (coordinates 32 hl + 0..31) becomes
+    // four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble bit min(t, 2), i.e. 0.5, 1 or 2 ----
     uint32_t wp[4][KP];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) walsh_planes<KB>(kw[grp], wp[grp]);
-    intx4 cacc[4];
+    floatx4 cacc[4];
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) cacc[grp] = intx4{0, 0, 0, 0};
+    for (int grp = 0; grp < 4; ++grp) cacc[grp] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < KP; ++p)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          intx4 bb;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) bb[r] = (int)(wp[grp][p] & (0x01010101u << (4 * half + r)));
-          cacc[grp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[p * 2 + half], bb, cacc[grp], 0, 0, 0);
-        }
+      for (int grp = 0; grp < 4; ++grp) {
+        const uint32_t x = wp[grp][p];
+        intx8 bb;
+        bb[0] = (int)(x & 0x11111111u);
+        bb[1] = (int)(x & 0x22222222u);
+        bb[2] = (int)(x & 0x44444444u);
+        bb[3] = (int)((x >> 1) & 0x44444444u);
+        bb[4] = bb[5] = bb[6] = bb[7] = 0;  // an fp4 operand reads four registers only
+        cacc[grp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[p], bb, cacc[grp], 0, 4, 0, 0, 0, 0);
+      }
     // every read of this slot has returned by now (its words fed the key MFMAs or sit in registers):
     // refill it with the stage one ring turn ahead
     __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
@@ -707,9 +717,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     __builtin_amdgcn_sched_barrier(0);
     float sc[4];
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
-      sc[grp] = (float)cacc[grp][0] + (float)cacc[grp][1] * (1.f / 128.f) + (float)cacc[grp][2] * (1.f / 16384.f) +
-                (float)cacc[grp][3] * (1.f / 2097152.f);
+    for (int grp = 0; grp < 4; ++grp)  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
+      sc[grp] = cacc[grp][0] + (cacc[grp][1] * 0.0625f + (cacc[grp][2] * (1.f / 512.f) + cacc[grp][3] * (1.f / 16384.f)));
     // ---- scores and the reference test ----
     float fk[4], fvn[4], fvg[4];
     const int sh = 16 * (tbase & 1);
@@ -850,7 +859,27 @@ struct PrepArgs {
   float *qinfo;
 };
 
-template <int D, int KB>
+// four fixed-point digits of u (|u| <= 224) as e4m3 bytes: u = sum_d k_d Q_d + e with Q_d = 2^(4 - 5 d),
+// k_0 in [-14, 14], k_1..k_3 in [-16, 16] and |e| <= 2^-12.  Byte d holds k_d 2^E_d f, E_0 = 4 and E_d = 3
+// after (each matrix-core row is its own output, so rows 1..3 are lifted clear of the e4m3 floor; their
+// sums are scaled back by Q_d 2^-3), f in {2, 1, 0.5} the inverse of the key nibble's value: every such
+// byte is an e4m3 number (at most 4 significant bits, within 4..448 when not 0).  All products of a digit row are
+// multiples of its 2^E_d and at most 16 of them in size, so the fp8 matrix-core sums are exact (they
+// keep only about 12 bits below the largest product of a sum, so floating digits would not be)
+__device__ __forceinline__ void split_fix4_e4m3(float u, float f, uint8_t (&o)[4]) {
+  float r = u;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float q = __builtin_ldexpf(1.f, 4 - 5 * d);
+    const float k = rintf(r / q);
+    r = fmaf(-k, q, r);
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(k * (d == 0 ? 16.f : 8.f) * f, 0.f, 0, false);
+    o[d] = (uint8_t)(pk & 0xFF);
+  }
+}
+
+// F8 (head_dim 128 only): images for the fp8 x fp4 matrix-core key pass of the wave-streaming kernel
+template <int D, int KB, bool F8 = false>
 __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr int KP = walsh_count(KB);
   constexpr int NINS = key_images(D, KB);
@@ -915,7 +944,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
     float sm = 0.f, mx = 0.f;
     for (int j = lane; j < D; j += 64) {
       sm += qp[h][j];
-      mx = fmaxf(mx, fabsf(qp[h][j]) / (float)(1 << (j & 7)));
+      mx = fmaxf(mx, F8 ? fabsf(qp[h][j]) : fabsf(qp[h][j]) / (float)(1 << (j & 7)));
     }
     sm = wave_sum_f32(sm);
     mx = wave_max_f32(mx);
@@ -926,6 +955,42 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
 #pragma unroll
   for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
   if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
+  if constexpr (F8) {
+    static_assert(D == 128, "fp8 images cover one 128-wide contraction");
+    // image p, lane (row m = 4 h + digit, k-group g), byte i of its 32: contraction index
+    // k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key operand holds k as nibble k % 32 of lane
+    // group k / 32, i.e. nibble position n = k % 8 of dword t = (k % 32) / 8, which carries bit 4 n + t of
+    // key word k / 32 as 2^(min(t, 2) - 1): coordinate 32 (k / 32) + 4 n + t, scaled by 2^(1 - min(t, 2))
+    for (int e = threadIdx.x; e < KP * 64 * 8; e += 256) {
+      const int w = e & 7, lane = (e >> 3) & 63, p = e >> 9;
+      const int m = lane & 15, h = m >> 2, dg = m & 3, g = lane >> 4;
+      uint32_t word = 0;
+      if (h < gw) {
+        const float mx = red[h][1] * bmax;
+        const float sq = mx > 0.f ? 224.f / mx : 0.f;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int i = 4 * w + bb;
+          const int k = i < 16 ? 16 * g + i : 64 + 16 * g + (i - 16);
+          const int t = (k & 31) >> 3, n = k & 7;
+          const int j = 32 * (k >> 5) + 4 * n + t;
+          const float f = t == 0 ? 2.f : t == 1 ? 1.f : 0.5f;
+          uint8_t o[4];
+          split_fix4_e4m3(fminf(fmaxf(2.f * a.kbeta[p] * qp[h][j] * sq, -224.f), 224.f), f, o);
+          word |= (uint32_t)o[dg] << (8 * bb);
+        }
+      }
+      a.qimg[(((int64_t)unit * KP + p) * 64 + lane) * 8 + w] = (int)word;
+    }
+    if (threadIdx.x < FA_GMAX) {
+      const int h = threadIdx.x;
+      const float mx = red[h][1] * bmax;
+      const float sq = mx > 0.f ? 224.f / mx : 0.f;
+      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
+      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] : 0.f;
+    }
+    return;
+  }
   // image
   for (int e = threadIdx.x; e < NINS * 64 * 4; e += 256) {
     const int r = e & 3, lane = (e >> 2) & 63, ins = e >> 8;
@@ -1168,9 +1233,9 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   if (wave) {
     {
       ProfScope ps("attn_prep", st);
-      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1, true>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2, true>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3, true>), dim3(units), dim3(256), 0, st, pa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {
