@@ -600,8 +600,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
     for (int i = 0; i < KP; ++i) qa[i] = img[i * 64 + lane];
   }
-  const float qinv = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0];
-  const float qconst = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1];
+  // score in log2 units = (image sum * qinv - qconst) * n_K * scale_log2
+  const float qinv2 = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0] * a.scale_log2;
+  const float qconst2 = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1] * a.scale_log2;
 
   // digit rows start at zero (rows of absent heads stay so); row 4h+3 of both kinds is all ones
   for (int i = lane; i < 2 * 16 * 16; i += 64) {
@@ -660,14 +661,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
       for (int p = 0; p < KB; ++p) kw[grp][p] = *reinterpret_cast<const uint32_t *>(st + p * 1024 + ks * 16 + hl * 4);
     }
-    uint32_t hn[3][4];  // token tbase + 8 grp is the (tbase % 2) half of dword (tbase + 8 grp) / 2
-    {
-      const uint32_t *nd = reinterpret_cast<const uint32_t *>(nrm) + (tbase >> 1);
+    uint32_t hn[3][4];  // fp16 of token tbase + 8 grp in the three arrays (128 halves apart)
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nd[64 * k + 4 * grp];
-    }
+      for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nrm[128 * k + tbase + 8 * grp];
     uint4 vw[2][2];  // [plane][column half]
     {
       const uint32_t *vt = reinterpret_cast<const uint32_t *>(st + S::KEYS) + (hl >> 1) * 256 + 4 * ln;
@@ -677,15 +675,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         for (int h = 0; h < 2; ++h) vw[p][h] = *reinterpret_cast<const uint4 *>(vt + 128 * p + 64 * h);
     }
     // the optimizer takes a direct-to-LDS load for a write of a few bytes only, and could otherwise
-    // move these reads below the refill of this slot: pin every value that is used after it
+    // move these reads below the refill of this slot: every value used after it is an input of a
+    // volatile statement here, so its read has returned before the refill is issued
 #pragma unroll
     for (int k = 0; k < 3; ++k)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) asm volatile("" : "+v"(hn[k][grp]));
+      for (int grp = 0; grp < 4; ++grp) asm volatile("" ::"v"(hn[k][grp]));
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(vw[p][h].x), "+v"(vw[p][h].y), "+v"(vw[p][h].z), "+v"(vw[p][h].w));
+      for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(vw[p][h].x), "v"(vw[p][h].y), "v"(vw[p][h].z), "v"(vw[p][h].w));
     __builtin_amdgcn_sched_barrier(0);
     // ---- key pass (fp8 query digits x fp4 key bits, fp32 accumulation): the four 16-token groups
     // interleaved, so consecutive MFMAs are independent.  A key word (coordinates 32 hl + 0..31) becomes
@@ -721,30 +720,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       sc[grp] = cacc[grp][0] + (cacc[grp][1] * 0.0625f + (cacc[grp][2] * (1.f / 512.f) + cacc[grp][3] * (1.f / 16384.f)));
     // ---- scores and the reference test ----
     float fk[4], fvn[4], fvg[4];
-    const int sh = 16 * (tbase & 1);
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      fk[grp] = f16_to_f32((uint16_t)(hn[0][grp] >> sh));
-      fvn[grp] = f16_to_f32((uint16_t)(hn[1][grp] >> sh));
-      fvg[grp] = f16_to_f32((uint16_t)(hn[2][grp] >> sh));
+      fk[grp] = f16_to_f32((uint16_t)hn[0][grp]);
+      fvn[grp] = f16_to_f32((uint16_t)hn[1][grp]);
+      fvg[grp] = f16_to_f32((uint16_t)hn[2][grp]);
     }
-    bool over = false;
+    if (rem == WV_STEP && gw == FA_GMAX) {  // a whole step of valid tokens for every head (wave-uniform)
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const bool valid = tbase + 8 * grp < rem;
-      const float s_ = (sc[grp] * qinv - qconst) * fk[grp] * a.scale_log2;
-      fvn[grp] = valid ? fvn[grp] : 0.f;
-      fvg[grp] = valid ? fvg[grp] : 0.f;
-      sc[grp] = (head_ok && valid) ? s_ : -INFINITY;
-      over = over || sc[grp] > m_ref + WV_SLACK || fvn[grp] > vn_ref || fvg[grp] > vg_ref;
+      for (int grp = 0; grp < 4; ++grp) sc[grp] = fmaf(sc[grp], qinv2, -qconst2) * fk[grp];
+    } else {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const bool valid = tbase + 8 * grp < rem;
+        const float s_ = fmaf(sc[grp], qinv2, -qconst2) * fk[grp];
+        fvn[grp] = valid ? fvn[grp] : 0.f;
+        fvg[grp] = valid ? fvg[grp] : 0.f;
+        sc[grp] = (head_ok && valid) ? s_ : -INFINITY;
+      }
     }
+    const float ms = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float mn = fmaxf(fmaxf(fvn[0], fvn[1]), fmaxf(fvn[2], fvn[3]));
+    const float mg = fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3]));
+    const bool over = ms > m_ref + WV_SLACK || mn > vn_ref || mg > vg_ref;
     ++since_fold;
     if ((__builtin_amdgcn_ballot_w64(over) != 0ull) || since_fold >= 16384) {
       // rare: move the reference to this step's maxima and fold the integer accumulators
-      float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      smax = rows16_max(smax);
-      const float vnm = wave_max_f32(fmaxf(fmaxf(fvn[0], fvn[1]), fmaxf(fvn[2], fvn[3])));
-      const float vgm = wave_max_f32(fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3])));
+      const float smax = rows16_max(ms);
+      const float vnm = wave_max_f32(mn);
+      const float vgm = wave_max_f32(mg);
       const float m_new = fmaxf(m_ref, smax);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const double im = (double)vn_ref * WV_HEADROOM / WV_WMAX, iq = (double)vg_ref * WV_HEADROOM / WV_WMAX;
