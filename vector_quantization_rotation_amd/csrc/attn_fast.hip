@@ -470,8 +470,13 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
 //   wave and carries headroom: a score may exceed the reference maximum by
 //   WV_SLACK (log2 units) and the caps are WV_NCAP times the largest norm and
 //   gamma seen, with the weight scale divided by 2^WV_SLACK so the integers stay
-//   below 2^23.  The int32 accumulators are folded (exactly, in fp64) only when
-//   a step leaves that headroom, which after the first step is rare.
+//   below 2^23.  The int32 accumulators are folded into fp32 (as non-negative
+//   unsigned digit sums, so without cancellation) only when a step leaves that
+//   headroom, which after the first step is rare.
+// * Software pipelining: a step's key pass (matrix-core work) is issued for the
+//   next step before this step's softmax, so its MFMAs do not hold up the
+//   vector work that follows; the stage ring refills a slot after its value
+//   words are read.
 // ---------------------------------------------------------------------------
 constexpr int WV_STEP = 64;
 constexpr float WV_SLACK = 1.f;           // score headroom above the reference maximum (log2 units)
@@ -558,9 +563,13 @@ __device__ __forceinline__ void wv_digits(const uint32_t (&u)[4], uint32_t (&o)[
 }
 
 // folded value of one head's four accumulator rows: digits 1, 2^8, 2^16, and the row of ones (the
-// sum of the value operand's bytes) times the digit offset 0x808080
-__device__ __forceinline__ double wv_fold(const intx4 &v) {
-  return (double)v[0] + 256.0 * (double)v[1] + 65536.0 * (double)v[2] + 8421504.0 * (double)v[3];
+// sum of the value operand's bytes) times the digit offset 0x808080.  Each digit row plus 128 times the
+// row of ones is the sum of that digit's unsigned bytes (exact as a 32-bit unsigned integer, at most
+// 2^31 within a fold), so the three terms added in fp32 are all non-negative: no cancellation
+__device__ __forceinline__ float wv_fold(const intx4 &v) {
+  const uint32_t o = (uint32_t)v[3] * 128u;
+  const float u0 = (float)((uint32_t)v[0] + o), u1 = (float)((uint32_t)v[1] + o), u2 = (float)((uint32_t)v[2] + o);
+  return fmaf(65536.f, u2, fmaf(256.f, u1, u0));
 }
 
 template <int KB>
@@ -642,57 +651,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   float sm_l = 0.f, sq_l = 0.f;  // weight scales WV_WMAX 2^-r / (largest n_V, gamma_V so far)
   float ism_l = 0.f, isq_l = 0.f;  // their inverses (0 while a scale is 0)
 
-  // one step over the stage in `st` (a fixed ring slot after inlining)
-  auto body = [&, rk, rkn, rvn, rvg, rv](uint8_t *st, int s) {
-    const int64_t t0 = c0 + (int64_t)s * WV_STEP;
-    const int rem = (int)imax64(imin64(c1 - t0, WV_STEP), 0);  // valid tokens in this step
-    const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
-    // every body issues one stage, so the two stages after this one are the only loads that may
-    // still be in flight: this stage has landed in LDS once no more than theirs are outstanding
-    wv_wait_vm<2 * S::NLOAD>();
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- every read of the stage up front: key words, the dwords holding this lane's fp16 values,
-    // value words (four adjacent columns per read; column tile c of this lane is column
-    // 64 (c / 4) + 4 ln + c % 4) ----
+  // key pass of one step on the stage in `stk`: its key words as fp4 operands against the query digits,
+  // the digit-row sums in cacc (fp32, exact)
+  auto key_mfma = [&](const uint8_t *stk, floatx4 (&cacc)[4]) {
     uint32_t kw[4][KB];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int ks = wv_key_slot(tbase + 8 * grp);
 #pragma unroll
-      for (int p = 0; p < KB; ++p) kw[grp][p] = *reinterpret_cast<const uint32_t *>(st + p * 1024 + ks * 16 + hl * 4);
+      for (int p = 0; p < KB; ++p) kw[grp][p] = *reinterpret_cast<const uint32_t *>(stk + p * 1024 + ks * 16 + hl * 4);
     }
-    uint32_t hn[3][4];  // fp16 of token tbase + 8 grp in the three arrays (128 halves apart)
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nrm[128 * k + tbase + 8 * grp];
-    uint4 vw[2][2];  // [plane][column half]
-    {
-      const uint32_t *vt = reinterpret_cast<const uint32_t *>(st + S::KEYS) + (hl >> 1) * 256 + 4 * ln;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) vw[p][h] = *reinterpret_cast<const uint4 *>(vt + 128 * p + 64 * h);
-    }
-    // the optimizer takes a direct-to-LDS load for a write of a few bytes only, and could otherwise
-    // move these reads below the refill of this slot: every value used after it is an input of a
-    // volatile statement here, so its read has returned before the refill is issued
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) asm volatile("" ::"v"(hn[k][grp]));
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(vw[p][h].x), "v"(vw[p][h].y), "v"(vw[p][h].z), "v"(vw[p][h].w));
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- key pass (fp8 query digits x fp4 key bits, fp32 accumulation): the four 16-token groups
-    // interleaved, so consecutive MFMAs are independent.  A key word (coordinates 32 hl + 0..31) becomes
-    // four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble bit min(t, 2), i.e. 0.5, 1 or 2 ----
+    // (the four 16-token groups interleaved, so consecutive MFMAs are independent.  A key word,
+    // coordinates 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble
+    // bit min(t, 2), i.e. 0.5, 1 or 2)
     uint32_t wp[4][KP];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) walsh_planes<KB>(kw[grp], wp[grp]);
-    floatx4 cacc[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) cacc[grp] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -708,16 +682,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         bb[4] = bb[5] = bb[6] = bb[7] = 0;  // an fp4 operand reads four registers only
         cacc[grp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[p], bb, cacc[grp], 0, 4, 0, 0, 0, 0);
       }
-    // every read of this slot has returned by now (its words fed the key MFMAs or sit in registers):
-    // refill it with the stage one ring turn ahead
-    __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-    wv_stage_load<KB>(st, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, t0 + WV_RING * WV_STEP);
-    __builtin_amdgcn_sched_barrier(0);
-    float sc[4];
+  };
+  float sc_next[4] = {0.f, 0.f, 0.f, 0.f};  // image sums of the next step's tokens
+  auto digit_sum = [&](const floatx4 (&cacc)[4]) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp)  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
-      sc[grp] = cacc[grp][0] + (cacc[grp][1] * 0.0625f + (cacc[grp][2] * (1.f / 512.f) + cacc[grp][3] * (1.f / 16384.f)));
+      sc_next[grp] =
+          cacc[grp][0] + (cacc[grp][1] * 0.0625f + (cacc[grp][2] * (1.f / 512.f) + cacc[grp][3] * (1.f / 16384.f)));
+  };
+
+  // step s on the stage in `st` (a fixed ring slot after inlining): its softmax and value pass, with the
+  // key pass of step s + 1 (stage in `stn`) issued first, so the matrix cores run it under this step's
+  // vector work
+  auto body = [&, rk, rkn, rvn, rvg, rv](uint8_t *st, const uint8_t *stn, int s) {
+    const int64_t t0 = c0 + (int64_t)s * WV_STEP;
+    const int rem = (int)imax64(imin64(c1 - t0, WV_STEP), 0);  // valid tokens in this step
+    const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
+    // every body issues one stage, so stages s + 1 and s + 2 are the only loads that may still be in
+    // flight: stage s + 1 (the next key pass) has landed once no more than one stage is outstanding
+    wv_wait_vm<S::NLOAD>();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- key pass of step s + 1 (fp8 query digits x fp4 key bits) ----
+    floatx4 cacc[4];
+    key_mfma(stn, cacc);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t hn[3][4];  // fp16 of token tbase + 8 grp in the three arrays (128 halves apart)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nrm[128 * k + tbase + 8 * grp];
+    float sc[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) sc[grp] = sc_next[grp];
     // ---- scores and the reference test ----
     float fk[4], fvn[4], fvg[4];
 #pragma unroll
@@ -751,11 +747,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       const float vgm = wave_max_f32(mg);
       const float m_new = fmaxf(m_ref, smax);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
-      const double im = (double)vn_ref * WV_HEADROOM / WV_WMAX, iq = (double)vg_ref * WV_HEADROOM / WV_WMAX;
+      const float im = vn_ref * (WV_HEADROOM / WV_WMAX), iq = vg_ref * (WV_HEADROOM / WV_WMAX);
 #pragma unroll
       for (int c = 0; c < NTC; ++c) {
-        accf[0][c] = (accf[0][c] + (float)(wv_fold(vacc[0][c]) * im)) * alpha;
-        accf[1][c] = (accf[1][c] + (float)(wv_fold(vacc[1][c]) * iq)) * alpha;
+        accf[0][c] = fmaf(wv_fold(vacc[0][c]), im, accf[0][c]) * alpha;
+        accf[1][c] = fmaf(wv_fold(vacc[1][c]), iq, accf[1][c]) * alpha;
         vacc[0][c] = intx4{0, 0, 0, 0};
         vacc[1][c] = intx4{0, 0, 0, 0};
       }
@@ -800,9 +796,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         }
       }
     }
+    // the next step's image sums (its key pass has run under this step's softmax)
+    digit_sum(cacc);
+    // ---- the value words (four adjacent columns per read; column tile c of this lane is column
+    // 64 (c / 4) + 4 ln + c % 4), the last reads of this slot: then refill it one ring turn ahead ----
+    uint4 vw[2][2];  // [plane][column half]
+    {
+      const uint32_t *vt = reinterpret_cast<const uint32_t *>(st + S::KEYS) + (hl >> 1) * 256 + 4 * ln;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) vw[p][h] = *reinterpret_cast<const uint4 *>(vt + 128 * p + 64 * h);
+    }
+    // the optimizer takes a direct-to-LDS load for a write of a few bytes only, and could otherwise
+    // move these reads below the refill of this slot: every value used after it is an input of a
+    // volatile statement here, so its read has returned before the refill is issued (the slot's key
+    // words were read, and used, by the previous step's key pass; its fp16 values above)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(vw[p][h].x), "v"(vw[p][h].y), "v"(vw[p][h].z), "v"(vw[p][h].w));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    wv_stage_load<KB>(st, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, t0 + WV_RING * WV_STEP);
+    __builtin_amdgcn_sched_barrier(0);
     // ---- value pass: 64 tokens x 128 columns, both kinds ----
     {
       const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_w[0][ln][16 * hl]);
@@ -820,19 +840,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     wv_stage_load<KB>(s_ring0, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0);
     wv_stage_load<KB>(s_ring1, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0 + WV_STEP);
     wv_stage_load<KB>(s_ring2, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, c0 + 2 * WV_STEP);
+    {  // the key pass of step 0, once stage 0 has landed
+      wv_wait_vm<2 * S::NLOAD>();
+      __builtin_amdgcn_sched_barrier(0);
+      floatx4 cacc[4];
+      key_mfma(s_ring0, cacc);
+      digit_sum(cacc);
+    }
+    // (the last step's key pass reads the stage after the chunk: zeros, never used)
     for (int s = 0; s < nsteps; s += WV_RING) {
-      body(s_ring0, s);
-      body(s_ring1, s + 1);
-      body(s_ring2, s + 2);
+      body(s_ring0, s_ring1, s);
+      body(s_ring1, s_ring2, s + 1);
+      body(s_ring2, s_ring0, s + 2);
     }
   }
   // ---- final fold and partial record: m, l, acc_mse[D], acc_qjl[D] ----
   {
-    const double im = (double)vn_ref * WV_HEADROOM / WV_WMAX, iq = (double)vg_ref * WV_HEADROOM / WV_WMAX;
+    const float im = vn_ref * (WV_HEADROOM / WV_WMAX), iq = vg_ref * (WV_HEADROOM / WV_WMAX);
 #pragma unroll
     for (int c = 0; c < NTC; ++c) {
-      accf[0][c] += (float)(wv_fold(vacc[0][c]) * im);
-      accf[1][c] += (float)(wv_fold(vacc[1][c]) * iq);
+      accf[0][c] = fmaf(wv_fold(vacc[0][c]), im, accf[0][c]);
+      accf[1][c] = fmaf(wv_fold(vacc[1][c]), iq, accf[1][c]);
     }
   }
   l_run = rows16_sum(l_run);
