@@ -770,21 +770,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     // ---- weights: p n and p gamma as integers below 2^23, three signed byte digits per token ----
     {
-      uint32_t um[4], uq[4];
+      uint32_t um[4], uq[4], bm[4], bq[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         // p = 2^(s - m_ref) <= 2^WV_SLACK (hardware exp2: results below 2^-126 flush to zero)
         const float p = __builtin_amdgcn_exp2f(sc[grp] - m_ref);
         const float wm = p * fvn[grp], wq = p * fvg[grp];
         l_run += p;
-        // the value sums take the rounded weights the matrix cores use, so a weight that rounds to
-        // zero drops out of both terms of 2 acc - Y (an error of zero mean) instead of biasing every column
-        const float fm = fmaf(wm, sm_l, WV_MAGIC), fq = fmaf(wq, sq_l, WV_MAGIC);
-        ym_run = fmaf(fm - WV_MAGIC, ism_l, ym_run);
-        yq_run = fmaf(fq - WV_MAGIC, isq_l, yq_run);
-        um[grp] = __float_as_uint(fm) ^ 0x808080u;
-        uq[grp] = __float_as_uint(fq) ^ 0x808080u;
+        bm[grp] = __float_as_uint(fmaf(wm, sm_l, WV_MAGIC));
+        bq[grp] = __float_as_uint(fmaf(wq, sq_l, WV_MAGIC));
+        um[grp] = bm[grp] ^ 0x808080u;
+        uq[grp] = bq[grp] ^ 0x808080u;
       }
+      // the value sums take the rounded weights the matrix cores use, so a weight that rounds to zero
+      // drops out of both terms of 2 acc - Y (an error of zero mean) instead of biasing every column:
+      // the four integers (the low 23 bits of 2^23 + w) summed as integers, below 2^25
+      ym_run = fmaf((float)(bm[0] + bm[1] + bm[2] + bm[3] - 4u * 0x4B000000u), ism_l, ym_run);
+      yq_run = fmaf((float)(bq[0] + bq[1] + bq[2] + bq[3] - 4u * 0x4B000000u), isq_l, yq_run);
       uint32_t dm[3], dq[3];
       wv_digits(um, dm);
       wv_digits(uq, dq);
