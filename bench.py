@@ -321,7 +321,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8 matrix cores on bit planes, i32 accumulate, f32 softmax",
+        "dtype": "fp8 x fp4 (keys, exact fixed-point digits) and i8 (values) matrix cores on bit planes, f32 softmax",
         "data": "synthetic",
         "config": {"workload": "decode attention over a TurboQuant-packed KV cache",
                    "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "seq_len": T,
