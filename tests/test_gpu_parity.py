@@ -175,17 +175,18 @@ def test_score_topk_ties_to_lower_index(api):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
-def _attn_case(api, B, Hq, Hkv, T, d, seq, qdtype, seed=0, layout=0, kbits=3, vbits=2):
+def _attn_case(api, B, Hq, Hkv, T, d, seq, qdtype, seed=0, layout=0, kbits=3, vbits=2, qfn=None):
     """Oracle-encoded K/V records (rows, or token-tiled by the oracle) fed to the GPU; the oracle's
-    two-pass attention over its own decoded caches is the expected value."""
+    two-pass attention over its own decoded caches is the expected value.  qfn(rng, piK) -> [B, Hq, d]
+    replaces the N(0, 1) queries."""
     rng = np.random.default_rng(seed)
     chans = synth.outlier_channels(Hkv, d, 4, seed + 1)
     K = synth.bf16_bits_to_f32(synth.kv_bf16((B, Hkv, T, d), seed + 2, chans)).reshape(-1, d)
     V = synth.bf16_bits_to_f32(synth.kv_bf16((B, Hkv, T, d), seed + 3, chans)).reshape(-1, d)
-    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    piK, piV, sV = synth.haar_rotation(d, seed + 4), synth.haar_rotation(d, seed + 5), synth.gaussian_projection(d, seed + 6)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32) if qfn is None else qfn(rng, piK).astype(np.float32)
     if qdtype == "bf16":
         q = synth.round_bf16(q)
-    piK, piV, sV = synth.haar_rotation(d, seed + 4), synth.haar_rotation(d, seed + 5), synth.gaussian_projection(d, seed + 6)
     kq = api.Quantizer(d, kbits, api.TQ_MSE, piK)
     vq = api.Quantizer(d, vbits, api.TQ_PROD, piV, sV)
     ke = parity.oracle_mse(K, piK, kbits)
@@ -264,6 +265,36 @@ def test_attn_decode_tiled_parity(api, B, Hq, Hkv, T, seq, d, kb, vb):
         err = parity.rel_rows(out[b], ref[b])
         assert np.all(err <= parity.RTOL), (b, err.max())
         print(f"tiled attention case b={b}: max rel err {err.max():.2e}")
+
+
+def _q_spike(rng, piK):
+    """Queries whose rotated image q' = Pi_K q is one coordinate of size 40 over N(0, 1e-3) noise: the
+    key operand's fixed-point query digits resolve the small coordinates only to their absolute grid."""
+    d = piK.shape[0]
+    qr = 1e-3 * rng.standard_normal((2, 8, d))
+    qr[:, :, 5] = 40.0
+    qr[:, 3:, 77] = -25.0
+    return qr @ np.asarray(piK, dtype=np.float64)  # q = Pi^T q'
+
+
+def _q_sharp(rng, piK):
+    """N(0, 1) queries scaled by 12: scores spread over hundreds of log2 units (a near one-hot softmax
+    whose runner-up tokens still carry weight in some heads)."""
+    return 12.0 * rng.standard_normal((2, 8, piK.shape[0]))
+
+
+@pytest.mark.parametrize("kind", ["spike", "sharp"])
+@pytest.mark.parametrize("kb", [3, 1, 4])
+def test_attn_query_extremes(api, kind, kb):
+    """The score paths on queries far from N(0, 1): the wave kernel (head_dim 128, 2-bit values, token-tiled)
+    and, at 4-bit keys, the 4-wave kernel, against the oracle's attention within the gate."""
+    qfn = _q_spike if kind == "spike" else _q_sharp
+    out, ref = _attn_case(api, 2, 8, 2, 3000, 128, [3000, 1777], "f32", seed=31, layout=api.TQ_LAYOUT_TILE32,
+                          kbits=kb, vbits=2, qfn=qfn)
+    for b in range(2):
+        err = parity.rel_rows(out[b], ref[b])
+        print(f"{kind} queries, {kb}-bit keys, b={b}: max rel err {err.max():.2e}")
+        assert np.all(err <= parity.RTOL), (b, err.max())
 
 
 @pytest.mark.parametrize("T,layout", [(30000, 1), (30000, 0), (4096, 1)])
