@@ -1,4 +1,4 @@
-// Fast decode attention on a TurboQuant cache: int8 matrix cores on bit planes.
+// Fast decode attention on a TurboQuant cache: matrix cores on bit planes.
 //
 // Method (ai-navigate-news Gemma 4 post, section "仕組み（技術的）"): keys are
 // Algorithm-1 records, values Algorithm-2 records; scores use the rotated query
@@ -11,12 +11,15 @@
 //   the bit planes:  c[idx] = sum_S beta_S prod_{p in S} s_p  (2^(b-1) terms;
 //   for b = 3: planes b0, b1, b2 and the parity b0^b1^b2).  Each term is a 0/1
 //   bit plane, so <q', c[idx]> = 2 sum_S beta_S <q', bits_S> - c[L-1] sum_j q'_j.
-// * A 0/1 plane word w feeds v_mfma_i32_16x16x64_i8 directly: (w & 0x01010101 << k)
-//   holds four bits as bytes of value 2^k (k = 7 reads as -128); the 2^-k (and
-//   the sign for k = 7) is folded into the other operand.
-// * The other operand (query or softmax weights) is split into four int8
-//   digits of 7 bits each, one per MFMA row of a head, so integer
-//   accumulation is exact and the only rounding is the split itself.
+// * Keys: a plane word (32 coordinates) feeds v_mfma_f32_16x16x128_f8f6f4 as
+//   four fp4 dwords (x & 0x11111111, x & 0x22222222, x & 0x44444444,
+//   (x >> 1) & 0x44444444: nibble values 0.5, 1, 2); the query images are four
+//   fixed-point e4m3 digits per head (one MFMA row each) carrying the inverse
+//   nibble factor, and every digit row's sum is exact (see split_fix4_e4m3).
+// * Values: a 0/1 plane word feeds v_mfma_i32_16x16x64_i8 directly:
+//   (w & 0x01010101 << k) holds four bits as bytes of value 2^k; the 2^-k is
+//   folded into the softmax weights, which are split into signed byte digits,
+//   one per MFMA row of a head, so integer accumulation is exact.
 // * Keys stay in per-token records (their bits run along the contraction).
 //   Values are read from the token-tiled layout (32 tokens per word) so that
 //   the contraction over tokens also runs along the word bits.
@@ -51,9 +54,10 @@ struct FastAttnArgs {
 };
 
 
-// With many Walsh planes per 128-coordinate block, keep one query image per block and half and apply
-// the Walsh coefficients to the per-plane integer results instead, so the images fit in registers
+// With many Walsh planes per 128-coordinate block, keep one query image per block and apply the Walsh
+// coefficients to the per-plane results instead, so the images fit in registers
 __host__ __device__ constexpr bool fold_beta(int D, int KB) { return walsh_count(KB) * (D / 128) > 4; }
+// workspace of the query images in KiB per unit (an fp8 image is 64 lanes x 32 B)
 __host__ __device__ constexpr int key_images(int D, int KB) {
   return (fold_beta(D, KB) ? 1 : walsh_count(KB)) * (D / 128) * 2;
 }
@@ -61,16 +65,6 @@ __host__ __device__ constexpr int key_images(int D, int KB) {
 // work-groups per CU, one wave per SIMD each
 __host__ __device__ constexpr int fa_waves_per_eu(int D, int KB, int VB) {
   return D > 256 ? 1 : D > 128 ? (VB >= 2 ? 1 : 2) : (KB == 4 && VB >= 2 ? 1 : (KB == 4 || VB >= 2) ? 2 : 3);
-}
-
-// v (|v| <= 127.5) as a1 + a2/2^7 + a3/2^14 + a4/2^21 with int8 terms (|a2..a4| <= 64)
-__device__ __forceinline__ void split4(float v, int8_t *o) {
-  const float a1 = rintf(v), r1 = (v - a1) * 128.f, a2 = rintf(r1), r2 = (r1 - a2) * 128.f, a3 = rintf(r2);
-  const float a4 = rintf((r2 - a3) * 128.f);
-  o[0] = (int8_t)(int)a1;
-  o[1] = (int8_t)(int)a2;
-  o[2] = (int8_t)(int)a3;
-  o[3] = (int8_t)(int)a4;
 }
 
 __device__ __forceinline__ float rows16_max(float v) {
@@ -153,7 +147,8 @@ constexpr float FA_HEADROOM = 2.f;  // 2^FA_SLACK
 //
 // Work-group = 4 waves over one (batch, kv head, head group, sequence chunk),
 // walked in steps of 256 tokens.  In a step wave w scores tokens 64w..64w+63
-// (all heads), writes their int8 weight digits to LDS, and after a barrier
+// (all heads; fp8 x fp4 matrix cores as in the wave-streaming kernel), writes
+// their int8 weight digits to LDS, and after a barrier
 // aggregates all 256 tokens for its quarter of the value columns.  The next
 // step's key words, norms and value words are loaded while the current step
 // runs.  Softmax weights are scaled by a reference (running maximum, value norm
@@ -168,7 +163,6 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   constexpr int VPL = VB + 1;                // stored value planes per tile
   constexpr int KW = D / 32;                 // 32-bit words per key plane
   constexpr int KWL = KB * (D / 128);        // key words per lane per 16-token group
-  constexpr int NINS = key_images(D, KB);    // query operand images
   constexpr bool FOLD = fold_beta(D, KB);    // Walsh coefficients applied after the MFMA
   constexpr int NTW = D / 64;                // value column tiles per wave
   constexpr int KCB = KB * D / 8;            // key record bytes
@@ -198,11 +192,14 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   const int kofs = (hl & 1) * 4; // value operand: token-bit offset of this lane group
   const bool head_ok = hl < gw;
 
-  intx4 qa[NINS];
+  // query operand: e4m3 fixed-point digit images (4 heads x 4 digit rows), one per 128-coordinate block
+  // (FOLD) or per (Walsh plane, block)
+  constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
+  intx8 qa[NI8];
   {
-    const intx4 *img = reinterpret_cast<const intx4 *>(a.qimg) + (int64_t)unit * NINS * 64;
+    const intx8 *img = reinterpret_cast<const intx8 *>(a.qimg) + (int64_t)unit * NI8 * 64;
 #pragma unroll
-    for (int i = 0; i < NINS; ++i) qa[i] = img[i * 64 + lane];
+    for (int i = 0; i < NI8; ++i) qa[i] = img[i * 64 + lane];
   }
   const float qinv = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0];
   const float qconst = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1];
@@ -258,13 +255,15 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- key pass: 4 groups of 16 tokens ----
+    // ---- key pass: 4 groups of 16 tokens, fp8 query digits x fp4 key bits (a key word, coordinates
+    // 128 wb + 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble
+    // bit min(t, 2)); exact fp32 sums per digit row ----
     float sc[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      intx4 cacc[FOLD ? KP : 1];
+      floatx4 cacc[FOLD ? KP : 1];
 #pragma unroll
-      for (int p = 0; p < (FOLD ? KP : 1); ++p) cacc[p] = intx4{0, 0, 0, 0};
+      for (int p = 0; p < (FOLD ? KP : 1); ++p) cacc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int wb = 0; wb < D / 128; ++wb) {
         uint32_t w[KB];
@@ -274,21 +273,22 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
         walsh_planes<KB>(w, wp);
 #pragma unroll
         for (int p = 0; p < KP; ++p) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            intx4 bb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bb[r] = (int)(wp[p] & (0x01010101u << (4 * half + r)));
-            const int ai = FOLD ? wb * 2 + half : (p * (D / 128) + wb) * 2 + half;
-            cacc[FOLD ? p : 0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ai], bb, cacc[FOLD ? p : 0], 0, 0, 0);
-          }
+          const uint32_t x = wp[p];
+          intx8 bb;
+          bb[0] = (int)(x & 0x11111111u);
+          bb[1] = (int)(x & 0x22222222u);
+          bb[2] = (int)(x & 0x44444444u);
+          bb[3] = (int)((x >> 1) & 0x44444444u);
+          bb[4] = bb[5] = bb[6] = bb[7] = 0;  // an fp4 operand reads four registers only
+          const int ai = FOLD ? wb : p * (D / 128) + wb;
+          cacc[FOLD ? p : 0] =
+              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ai], bb, cacc[FOLD ? p : 0], 0, 4, 0, 0, 0, 0);
         }
       }
       float v = 0.f;
 #pragma unroll
-      for (int p = 0; p < (FOLD ? KP : 1); ++p) {
-        const float x = (float)cacc[p][0] + (float)cacc[p][1] * (1.f / 128.f) + (float)cacc[p][2] * (1.f / 16384.f) +
-                        (float)cacc[p][3] * (1.f / 2097152.f);
+      for (int p = 0; p < (FOLD ? KP : 1); ++p) {  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
+        const float x = cacc[p][0] + (cacc[p][1] * 0.0625f + (cacc[p][2] * (1.f / 512.f) + cacc[p][3] * (1.f / 16384.f)));
         v = FOLD ? fmaf(2.f * a.kbeta[p], x, v) : x;
       }
       sc[grp] = v;
@@ -881,7 +881,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 }
 
 // ---------------------------------------------------------------------------
-// query operand images: q' = Pi_K q, Walsh-weighted, 2^-k folded, three int8 splits
+// query operand images: q' = Pi_K q, Walsh-weighted, as four fixed-point e4m3 digits in the fp8
+// operand order, with the inverse of each key nibble's value folded in
 // ---------------------------------------------------------------------------
 struct PrepArgs {
   const void *q;
@@ -912,11 +913,10 @@ __device__ __forceinline__ void split_fix4_e4m3(float u, float f, uint8_t (&o)[4
   }
 }
 
-// F8 (head_dim 128 only): images for the fp8 x fp4 matrix-core key pass of the wave-streaming kernel
-template <int D, int KB, bool F8 = false>
+// images for the fp8 x fp4 matrix-core key passes
+template <int D, int KB>
 __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr int KP = walsh_count(KB);
-  constexpr int NINS = key_images(D, KB);
   constexpr bool FOLD = fold_beta(D, KB);
   __shared__ float qs[FA_GMAX][D];
   __shared__ float qp[FA_GMAX][D];
@@ -978,7 +978,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
     float sm = 0.f, mx = 0.f;
     for (int j = lane; j < D; j += 64) {
       sm += qp[h][j];
-      mx = fmaxf(mx, F8 ? fabsf(qp[h][j]) : fabsf(qp[h][j]) / (float)(1 << (j & 7)));
+      mx = fmaxf(mx, fabsf(qp[h][j]));
     }
     sm = wave_sum_f32(sm);
     mx = wave_max_f32(mx);
@@ -989,14 +989,17 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
 #pragma unroll
   for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
   if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
-  if constexpr (F8) {
-    static_assert(D == 128, "fp8 images cover one 128-wide contraction");
-    // image p, lane (row m = 4 h + digit, k-group g), byte i of its 32: contraction index
-    // k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key operand holds k as nibble k % 32 of lane
-    // group k / 32, i.e. nibble position n = k % 8 of dword t = (k % 32) / 8, which carries bit 4 n + t of
-    // key word k / 32 as 2^(min(t, 2) - 1): coordinate 32 (k / 32) + 4 n + t, scaled by 2^(1 - min(t, 2))
-    for (int e = threadIdx.x; e < KP * 64 * 8; e += 256) {
-      const int w = e & 7, lane = (e >> 3) & 63, p = e >> 9;
+  {
+    // image ii (FOLD: the 128-coordinate block ii, coefficients applied after the matrix cores; else
+    // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
+    // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
+    // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
+    // t = (k % 32) / 8, which carries bit 4 n + t of the block's key word k / 32 as 2^(min(t, 2) - 1):
+    // coordinate 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - min(t, 2))
+    constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
+    for (int e = threadIdx.x; e < NI8 * 64 * 8; e += 256) {
+      const int w = e & 7, lane = (e >> 3) & 63, ii = e >> 9;
+      const int wb = ii % (D / 128), p = ii / (D / 128);
       const int m = lane & 15, h = m >> 2, dg = m & 3, g = lane >> 4;
       uint32_t word = 0;
       if (h < gw) {
@@ -1007,14 +1010,14 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
           const int i = 4 * w + bb;
           const int k = i < 16 ? 16 * g + i : 64 + 16 * g + (i - 16);
           const int t = (k & 31) >> 3, n = k & 7;
-          const int j = 32 * (k >> 5) + 4 * n + t;
+          const int j = 128 * wb + 32 * (k >> 5) + 4 * n + t;
           const float f = t == 0 ? 2.f : t == 1 ? 1.f : 0.5f;
           uint8_t o[4];
-          split_fix4_e4m3(fminf(fmaxf(2.f * a.kbeta[p] * qp[h][j] * sq, -224.f), 224.f), f, o);
+          split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * sq, -224.f), 224.f), f, o);
           word |= (uint32_t)o[dg] << (8 * bb);
         }
       }
-      a.qimg[(((int64_t)unit * KP + p) * 64 + lane) * 8 + w] = (int)word;
+      a.qimg[(((int64_t)unit * NI8 + ii) * 64 + lane) * 8 + w] = (int)word;
     }
     if (threadIdx.x < FA_GMAX) {
       const int h = threadIdx.x;
@@ -1023,35 +1026,6 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
       a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
       a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] : 0.f;
     }
-    return;
-  }
-  // image
-  for (int e = threadIdx.x; e < NINS * 64 * 4; e += 256) {
-    const int r = e & 3, lane = (e >> 2) & 63, ins = e >> 8;
-    const int half = ins & 1, pw = ins >> 1, wb = pw % (D / 128), p = pw / (D / 128);
-    const int m = lane & 15, h = m >> 2, sp = m & 3, gq = lane >> 4;
-    uint32_t word = 0;
-    if (h < gw) {
-      const float mx = red[h][1] * bmax;
-      const float sq = mx > 0.f ? 127.f / mx : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 32 * (4 * wb + gq) + 8 * i + 4 * half + r;
-        const int kb = j & 7;
-        const float ks = kb == 7 ? -1.f / 128.f : 1.f / (float)(1 << kb);
-        int8_t o[4];
-        split4((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * ks * sq, o);
-        word |= (uint32_t)(uint8_t)o[sp] << (8 * i);
-      }
-    }
-    a.qimg[(((int64_t)unit * NINS + ins) * 64 + lane) * 4 + r] = (int)word;
-  }
-  if (threadIdx.x < FA_GMAX) {
-    const int h = threadIdx.x;
-    const float mx = red[h][1] * bmax;
-    const float sq = mx > 0.f ? 127.f / mx : 0.f;
-    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
-    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] : 0.f;
   }
 }
 
@@ -1267,9 +1241,9 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   if (wave) {
     {
       ProfScope ps("attn_prep", st);
-      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1, true>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2, true>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3, true>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3>), dim3(units), dim3(256), 0, st, pa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {
