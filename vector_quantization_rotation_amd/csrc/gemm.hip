@@ -22,37 +22,43 @@ constexpr int GBM = 64, GBN = 64, GBK = 16, GPAD = 16;
 // ----------------------------------------------------------------------------
 // operand loaders: fill v[0..3] with elements k..k+3 of row r (k % 4 == 0)
 // ----------------------------------------------------------------------------
+// Loaders: operator() gives four consecutive elements of row r from k as fp32; fetch / unpack split
+// the same into the load (issued early, kept in registers) and the conversion.
 struct LoadF32 {
   const float *p;
   int64_t ld;
-  __device__ void operator()(int64_t r, int k, float *v) const {
-    float4 t = *reinterpret_cast<const float4 *>(p + r * ld + k);
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-  }
+  using Raw = float4;
+  __device__ Raw fetch(int64_t r, int k) const { return *reinterpret_cast<const float4 *>(p + r * ld + k); }
+  __device__ void unpack(const Raw &t, float *v) const { v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w; }
+  __device__ void operator()(int64_t r, int k, float *v) const { unpack(fetch(r, k), v); }
 };
 
 struct LoadBF16 {
   const uint16_t *p;
   int64_t ld;
-  __device__ void operator()(int64_t r, int k, float *v) const {
-    uint2 t = *reinterpret_cast<const uint2 *>(p + r * ld + k);
+  using Raw = uint2;
+  __device__ Raw fetch(int64_t r, int k) const { return *reinterpret_cast<const uint2 *>(p + r * ld + k); }
+  __device__ void unpack(const Raw &t, float *v) const {
     v[0] = __uint_as_float(t.x << 16);
     v[1] = __uint_as_float(t.x & 0xFFFF0000u);
     v[2] = __uint_as_float(t.y << 16);
     v[3] = __uint_as_float(t.y & 0xFFFF0000u);
   }
+  __device__ void operator()(int64_t r, int k, float *v) const { unpack(fetch(r, k), v); }
 };
 
 struct LoadF16 {
   const uint16_t *p;
   int64_t ld;
-  __device__ void operator()(int64_t r, int k, float *v) const {
-    uint2 t = *reinterpret_cast<const uint2 *>(p + r * ld + k);
+  using Raw = uint2;
+  __device__ Raw fetch(int64_t r, int k) const { return *reinterpret_cast<const uint2 *>(p + r * ld + k); }
+  __device__ void unpack(const Raw &t, float *v) const {
     v[0] = f16_to_f32(t.x & 0xFFFF);
     v[1] = f16_to_f32(t.x >> 16);
     v[2] = f16_to_f32(t.y & 0xFFFF);
     v[3] = f16_to_f32(t.y >> 16);
   }
+  __device__ void operator()(int64_t r, int k, float *v) const { unpack(fetch(r, k), v); }
 };
 
 // rows [0, split) from a, rows [split, ...) from b (same row length ld)
@@ -126,38 +132,81 @@ struct EpiStore {
 };
 
 // Algorithm-1 index planes for 64 coordinates (one tile column block) per row.
-// For Algorithm 2 also the rotated residual y - n_hat c[idx] and its squared norm.
+// For Algorithm 2 also the rotated residual y - n_hat c[idx] and its squared norm over the block (fp32:
+// the fp16 gamma tolerates 1e-5 relative), one partial per (row, block) so no atomics are needed.
+// BM index bits; the cell index is a binary search over the row's scaled boundaries t_k n.
+template <int BM>
 struct EpiQuant {
   uint8_t *codes;
   int64_t code_bytes;
-  int d, bmse;
+  int d;
   const float *n32;        // fp32 norms of the rows (chunk-relative)
   const uint16_t *nhat;    // fp16 norms (chunk-relative)
   float *resid;            // [rows, d] rotated residual, or null (Algorithm 1)
-  double *rsq;             // [rows] accumulated ||r||^2, or null
+  float *rsq;              // [rows, d / 64] partial ||r||^2, or null
   Codebook cb;
   __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    constexpr int L = 1 << BM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // this wave's 16 rows: one load per lane, then uniform per row
+    float nl = 0.f, hl = 0.f;
+    if (lane < 16 && row0 + wave * 16 + lane < M) {
+      nl = n32[row0 + wave * 16 + lane];
+      hl = f16_to_f32(nhat[row0 + wave * 16 + lane]);
+    }
+    float tb[L - 1], cc[L];
+#pragma unroll
+    for (int k = 0; k < L - 1; ++k) tb[k] = cb.t[k];
+#pragma unroll
+    for (int k = 0; k < L; ++k) cc[k] = cb.c[k];
+    const int nblk = d >> 6;
+    float sq[16];  // r^2 of this lane's column, per row (summed over the block below)
+#pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
+      sq[rr] = 0.f;
       const int r = wave * 16 + rr;
       const int64_t row = row0 + r;
-      if (row >= M) break;
-      float y = Cs[r][lane];
-      float n = n32[row];
-      float yq = y, nq = n;
-      if (n == 0.0f) { yq = 0.0f; nq = 1.0f; }
-      int idx = cell_index(cb, yq, nq);
+      if (row >= M) continue;
+      const float y = Cs[r][lane];
+      const float n = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nl), rr));
+      const float yq = n == 0.0f ? 0.0f : y, nq = n == 0.0f ? 1.0f : n;
+      // binary search: bit s of idx decided against the one boundary the higher bits leave
+      int idx = 0;
+#pragma unroll
+      for (int sbit = BM - 1; sbit >= 0; --sbit) {
+        const int s = 1 << sbit;
+        float t = tb[s - 1];
+#pragma unroll
+        for (int c = 1; c < L / (2 * s); ++c)
+          if (idx == 2 * s * c) t = tb[2 * s * c + s - 1];
+        idx += (yq > t * nq) ? s : 0;
+      }
       uint8_t *dst = codes + row * code_bytes + (col0 >> 3);
-      for (int p = 0; p < bmse; ++p) {
-        unsigned long long m = __ballot(((idx >> p) & 1) != 0);
+#pragma unroll
+      for (int p = 0; p < BM; ++p) {
+        const unsigned long long m = __ballot(((idx >> p) & 1) != 0);
         if (lane == 0) *reinterpret_cast<unsigned long long *>(dst + p * (d >> 3)) = m;
       }
       if (resid) {
-        float rv = y - f16_to_f32(nhat[row]) * cb.c[idx];
+        float cv = cc[0];
+#pragma unroll
+        for (int k = 1; k < L; ++k) cv = idx == k ? cc[k] : cv;
+        const float nh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), rr));
+        const float rv = y - nh * cv;
         resid[row * d + col0 + lane] = rv;
-        double s = wave_sum_f64((double)rv * (double)rv);
-        if (lane == 0) atomicAdd(rsq + row, s);
+        sq[rr] = rv * rv;
       }
+    }
+    if (resid) {
+      // the 16 row sums over the lanes at once (independent shuffles in flight together)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sq[rr] += __shfl_xor(sq[rr], o, 64);
+      float mine = sq[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mine = (lane == rr) ? sq[rr] : mine;
+      if (lane < 16 && row0 + wave * 16 + lane < M) rsq[(row0 + wave * 16 + lane) * nblk + (col0 >> 6)] = mine;
     }
   }
 };
@@ -305,12 +354,28 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[NPA][2], rb[6];
+  // the next step's A and B elements are loaded into registers before this step's MFMAs and converted
+  // to pieces only when they are stored, so the loads are in flight under the MFMAs
+  typename LA::Raw rr[4];
+  uint4 rb[6];
   auto gload = [&](int k0) {
+    if (arow_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rr[i] = la.fetch(row0 + ar, k0 + ak + 4 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
+      const int64_t col = col0 + br;
+      rb[i] = col < N ? *reinterpret_cast<const uint4 *>(b3 + ((int64_t)p * N + col) * K + k0 + kk)
+                      : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&]() {
     float v[16];
     if (arow_ok) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) la(row0 + ar, k0 + ak + 4 * i, v + 4 * i);
+      for (int i = 0; i < 4; ++i) la.unpack(rr[i], v + 4 * i);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0.f;
@@ -327,21 +392,8 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
         for (int p = 0; p < 3; ++p) w[p][q] = g_pack2(p0[p], p1[p]);
       }
 #pragma unroll
-      for (int p = 0; p < NPA; ++p) ra[p][h] = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
+      for (int p = 0; p < NPA; ++p) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
     }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
-      const int64_t col = col0 + br;
-      rb[i] = col < N ? *reinterpret_cast<const uint4 *>(b3 + ((int64_t)p * N + col) * K + k0 + kk)
-                      : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int p = 0; p < NPA; ++p)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = ra[p][h];
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
@@ -424,14 +476,13 @@ __global__ __launch_bounds__(256) void norm_kernel(const void *x, int64_t ldx, i
   }
 }
 
-__global__ void zero_f64_kernel(double *p, int64_t n) {
+// gamma = ||r|| from the rows' per-block partial squares (summed in fp64)
+__global__ void gamma_kernel(const float *rsq, int nblk, int64_t n, uint16_t *gam) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0;
-}
-
-__global__ void gamma_kernel(const double *rsq, int64_t n, uint16_t *gam) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) gam[i] = f64_to_f16_rne_sat(sqrt(rsq[i]));
+  if (i >= n) return;
+  double s = 0.0;
+  for (int b = 0; b < nblk; ++b) s += (double)rsq[i * nblk + b];
+  gam[i] = f64_to_f16_rne_sat(sqrt(s));
 }
 
 // m[i][j] = sum_k s[i][k] pi[j][k] in fp64, rounded to fp32
@@ -467,7 +518,7 @@ struct Scratch {
 
 template <class LX>
 int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ldx, int64_t cn, uint8_t *codes,
-                 uint16_t *norms, uint16_t *gammas, float *n32, float *resid, double *rsq, hipStream_t st) {
+                 uint16_t *norms, uint16_t *gammas, float *n32, float *resid, float *rsq, hipStream_t st) {
   const int d = q->d;
   int rc;
   dim3 ng((unsigned)cdiv64(cn, 4));
@@ -479,20 +530,24 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
   }
   if ((rc = launch_check()) != TQ_OK) return rc;
   const bool prod = q->mode == TQ_PROD;
-  if (prod) {
-    hipLaunchKernelGGL(zero_f64_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, cn);
-    if ((rc = launch_check()) != TQ_OK) return rc;
-  }
-  EpiQuant eq{codes, (int64_t)q->code_bytes, d, q->bmse, n32, norms, prod ? resid : nullptr, prod ? rsq : nullptr,
-              q->cb};
   // exact bf16 pieces on the matrix cores: bf16 rows are one piece, fp16 two, fp32 three
   constexpr int NPA = std::is_same<LX, LoadBF16>::value ? 1 : std::is_same<LX, LoadF16>::value ? 2 : 3;
-  if ((rc = gemm_pieces<NPA>("encode_rotate", lx, q->pi3, eq, cn, d, d, st)) != TQ_OK) return rc;
+  auto rotate = [&](auto eq) { return gemm_pieces<NPA>("encode_rotate", lx, q->pi3, eq, cn, d, d, st); };
+  float *rs = prod ? resid : nullptr, *rq = prod ? rsq : nullptr;
+  const int64_t cbytes = (int64_t)q->code_bytes;
+  switch (q->bmse) {
+    case 1: rc = rotate(EpiQuant<1>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
+    case 2: rc = rotate(EpiQuant<2>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
+    case 3: rc = rotate(EpiQuant<3>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
+    case 4: rc = rotate(EpiQuant<4>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
+    default: rc = TQ_ERR_UNSUPPORTED;
+  }
+  if (rc != TQ_OK) return rc;
   if (!prod) return TQ_OK;
   LoadF32 lr{resid, d};
   EpiSign es{codes, (int64_t)q->code_bytes, d, q->planes - 1};
   if ((rc = gemm_pieces<3>("encode_qjl", lr, q->m3, es, cn, d, d, st)) != TQ_OK) return rc;
-  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, cn, gammas);
+  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)cdiv64(cn, 256)), dim3(256), 0, st, rsq, d / 64, cn, gammas);
   return launch_check();
 }
 
@@ -509,19 +564,18 @@ int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t 
   const int64_t chunk = prod ? std::max<int64_t>(64, (int64_t(1) << 27) / d) : (int64_t(1) << 22);
   const int64_t cmax = std::min(n, chunk);
   size_t bytes = (size_t)cmax * 4 + 256;
-  if (prod) bytes += (size_t)cmax * d * 4 + (size_t)cmax * 8 + 256;
+  if (prod) bytes += (size_t)cmax * d * 4 + (size_t)cmax * (d / 64) * 4 + 256;
   Scratch sc(st);
   int rc = sc.alloc(bytes);
   if (rc != TQ_OK) return rc;
   char *base = static_cast<char *>(sc.p);
   float *n32 = reinterpret_cast<float *>(base);
-  float *resid = nullptr;
-  double *rsq = nullptr;
+  float *resid = nullptr, *rsq = nullptr;
   if (prod) {
     size_t off = ((size_t)cmax * 4 + 255) & ~(size_t)255;
     resid = reinterpret_cast<float *>(base + off);
     off += ((size_t)cmax * d * 4 + 255) & ~(size_t)255;
-    rsq = reinterpret_cast<double *>(base + off);
+    rsq = reinterpret_cast<float *>(base + off);
   }
   const size_t esz = xt == TQ_F32 ? 4 : 2;
   for (int64_t r0 = 0; r0 < n; r0 += chunk) {
