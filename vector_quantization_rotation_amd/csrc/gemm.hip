@@ -454,23 +454,43 @@ static int gemm_pieces(const char *name, LA la, const uint16_t *b3, EP ep, int64
 // ----------------------------------------------------------------------------
 // small kernels: norms, zero fill, gamma finalisation, M = S Pi^T
 // ----------------------------------------------------------------------------
+// one row per 16 lanes (16 rows per work-group): each lane sums the squares of 4 consecutive elements
+// every 64, in fp64 (the fp16 norm must round as the exact value does), loads kept in flight together
 template <int XT>
 __global__ __launch_bounds__(256) void norm_kernel(const void *x, int64_t ldx, int d, int64_t n, uint16_t *nhat,
                                                    float *n32) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
+  const int l16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   double s = 0.0;
-  for (int j = lane; j < d; j += 64) {
-    double v;
-    if (XT == TQ_F32) v = static_cast<const float *>(x)[row * ldx + j];
-    else if (XT == TQ_BF16) v = bf16_to_f32(static_cast<const uint16_t *>(x)[row * ldx + j]);
-    else v = f16_to_f32(static_cast<const uint16_t *>(x)[row * ldx + j]);
-    s += v * v;
+  if (row < n) {
+    for (int j0 = 4 * l16; j0 < d; j0 += 256) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 64 * u;
+        if (j >= d) {
+          v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.f;
+        } else if (XT == TQ_F32) {
+          const float4 t = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row * ldx + j);
+          v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + row * ldx + j);
+          const uint16_t h[4] = {(uint16_t)(t.x & 0xFFFF), (uint16_t)(t.x >> 16), (uint16_t)(t.y & 0xFFFF),
+                                 (uint16_t)(t.y >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[u][e] = XT == TQ_BF16 ? bf16_to_f32(h[e]) : f16_to_f32(h[e]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fma((double)v[u][e], (double)v[u][e], s);
+    }
   }
-  s = wave_sum_f64(s);
-  if (lane == 0) {
-    double nn = sqrt(s);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (l16 == 0 && row < n) {
+    const double nn = sqrt(s);
     nhat[row] = f64_to_f16_rne_sat(nn);
     n32[row] = (float)nn;
   }
@@ -521,7 +541,7 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
                  uint16_t *norms, uint16_t *gammas, float *n32, float *resid, float *rsq, hipStream_t st) {
   const int d = q->d;
   int rc;
-  dim3 ng((unsigned)cdiv64(cn, 4));
+  dim3 ng((unsigned)cdiv64(cn, 16));
   {
   ProfScope ps("encode_norm", st);
   if (xt == TQ_F32) hipLaunchKernelGGL(norm_kernel<TQ_F32>, ng, dim3(256), 0, st, x, ldx, d, cn, norms, n32);
