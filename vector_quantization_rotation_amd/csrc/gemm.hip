@@ -145,14 +145,15 @@ struct EpiQuant {
   float *resid;            // [rows, d] rotated residual, or null (Algorithm 1)
   float *rsq;              // [rows, d / 64] partial ||r||^2, or null
   Codebook cb;
-  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+  // rows rb..rb+15 of the tile by the calling wave (lane = column)
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
     constexpr int L = 1 << BM;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // this wave's 16 rows: one load per lane, then uniform per row
+    const int lane = threadIdx.x & 63;
+    // the 16 rows' norms: one load per lane, then uniform per row
     float nl = 0.f, hl = 0.f;
-    if (lane < 16 && row0 + wave * 16 + lane < M) {
-      nl = n32[row0 + wave * 16 + lane];
-      hl = f16_to_f32(nhat[row0 + wave * 16 + lane]);
+    if (lane < 16 && row0 + rb + lane < M) {
+      nl = n32[row0 + rb + lane];
+      hl = f16_to_f32(nhat[row0 + rb + lane]);
     }
     float tb[L - 1], cc[L];
 #pragma unroll
@@ -164,7 +165,7 @@ struct EpiQuant {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       sq[rr] = 0.f;
-      const int r = wave * 16 + rr;
+      const int r = rb + rr;
       const int64_t row = row0 + r;
       if (row >= M) continue;
       const float y = Cs[r][lane];
@@ -206,7 +207,7 @@ struct EpiQuant {
       float mine = sq[0];
 #pragma unroll
       for (int rr = 1; rr < 16; ++rr) mine = (lane == rr) ? sq[rr] : mine;
-      if (lane < 16 && row0 + wave * 16 + lane < M) rsq[(row0 + wave * 16 + lane) * nblk + (col0 >> 6)] = mine;
+      if (lane < 16 && row0 + rb + lane < M) rsq[(row0 + rb + lane) * nblk + (col0 >> 6)] = mine;
     }
   }
 };
@@ -216,10 +217,11 @@ struct EpiSign {
   uint8_t *codes;
   int64_t code_bytes;
   int d, plane;
-  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // rows rb..rb+15 of the tile by the calling wave (lane = column)
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
+    const int lane = threadIdx.x & 63;
     for (int rr = 0; rr < 16; ++rr) {
-      const int r = wave * 16 + rr;
+      const int r = rb + rr;
       const int64_t row = row0 + r;
       if (row >= M) break;
       unsigned long long m = __ballot(Cs[r][lane] >= 0.0f);
@@ -340,9 +342,11 @@ __device__ __forceinline__ floatx4 g_terms(const gbf16x8 (&a)[3], const gbf16x8 
 template <int NPA, class LA, class EP>
 __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N,
                                                           int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[NPA][PBM][PKP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][PBN][PKP];
-  __shared__ float Cs[GBM][GBN + 1];
+  // one buffer: the staged pieces during the contraction, then each wave's 64 x 64 result tile
+  constexpr size_t AB = (size_t)(NPA + 3) * PBM * PKP * 2, CT = (size_t)4 * GBM * (GBN + 1) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[AB > CT ? AB : CT];
+  uint16_t(*As)[PBM][PKP] = reinterpret_cast<uint16_t(*)[PBM][PKP]>(lds);
+  uint16_t(*Bs)[PBN][PKP] = reinterpret_cast<uint16_t(*)[PBN][PKP]>(lds + (size_t)NPA * PBM * PKP * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row0 = (int64_t)blockIdx.x * PBM, col0 = (int64_t)blockIdx.y * PBN;
@@ -423,21 +427,23 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
       for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms<NPA>(af[rt], bf, acc[rt][ct]);
     }
   }
-  // one quadrant at a time through the 64 x 64 epilogue tile
+  // every wave turns its own 64 x 64 quadrant to row-major in its part of the buffer and runs the
+  // epilogue on it, 16 rows at a time (no work-group barrier after the first)
+  __syncthreads();  // every read of the staged pieces done
+  CTile *Cw = reinterpret_cast<CTile *>(lds + (size_t)wave * GBM * (GBN + 1) * 4);
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    __syncthreads();
-    if (wave == qd) {
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Cs[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[rt][ct][e];
-    }
-    __syncthreads();
-    const int64_t qr0 = row0 + 64 * (qd >> 1), qc0 = col0 + 64 * (qd & 1);
-    if (qr0 < M && qc0 < N) ep(Cs, qr0, qc0, M, N);
+      for (int e = 0; e < 4; ++e) Cw[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[rt][ct][e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int64_t qr0 = row0 + 64 * wm, qc0 = col0 + 64 * wn;
+  if (qr0 < M && qc0 < N) {
+#pragma unroll 1
+    for (int rb = 0; rb < GBM; rb += 16) ep(Cw, qr0, qc0, M, N, rb);
   }
 }
 
