@@ -28,6 +28,7 @@
 //   weight digits in LDS, aggregate (value pass); online softmax with a
 //   rarely-moving reference maximum.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.cuh"
 
@@ -74,6 +75,18 @@ __device__ __forceinline__ float rows16_max(float v) {
 __device__ __forceinline__ float rows16_sum(float v) {
   for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// fp4 dword of the sign-form key nibbles: bit 3 of every nibble of x kept as the sign of 0.5, so each
+// nibble is worth 0.5 - bit.  With the 0.5 pattern `ones` (0x11111111) in a vector register this is one
+// AND-OR (the instruction takes one scalar operand only, here the mask); written in C so that the
+// compiler sees a vector instruction and keeps the wait states the matrix core needs before reading it
+__device__ __forceinline__ int f4_sign_half(uint32_t x, uint32_t ones) { return (int)((x & 0x88888888u) | ones); }
+// 0x11111111 in a vector register, opaque to the compiler so that it stays one
+__device__ __forceinline__ uint32_t f4_ones_reg() {
+  uint32_t c = 0x11111111u;
+  asm volatile("" : "+v"(c));
+  return c;
 }
 
 // ---------------------------------------------------------------------------
@@ -243,6 +256,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   const int tbase = 32 * (ln >> 3) + (ln & 7);
   const int slot = (2 * (ln >> 3) + ((ln & 7) >> 2)) * 16 + (ln & 3) * 4;  // byte offset of grp 0
   const float kscale = __builtin_amdgcn_ldexpf(1.f, -value_kexp(ln & 7));
+  const uint32_t f4_ones = f4_ones_reg();
   for (int64_t s0 = c0; s0 < c1; s0 += FA_SUB) {
     const int64_t sn = s0 + FA_SUB;
     const int64_t wbase = s0 + 64 * wave;
@@ -256,8 +270,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- key pass: 4 groups of 16 tokens, fp8 query digits x fp4 key bits (a key word, coordinates
-    // 128 wb + 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble
-    // bit min(t, 2)); exact fp32 sums per digit row ----
+    // 128 wb + 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit b = bit 4 n + t,
+    // at nibble bit t for t < 3 and as the sign of 0.5 for t = 3); exact fp32 sums per digit row ----
     float sc[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
           bb[0] = (int)(x & 0x11111111u);
           bb[1] = (int)(x & 0x22222222u);
           bb[2] = (int)(x & 0x44444444u);
-          bb[3] = (int)((x >> 1) & 0x44444444u);
+          bb[3] = f4_sign_half(x, f4_ones);  // +-0.5: 0.5 - bit
           bb[4] = bb[5] = bb[6] = bb[7] = 0;  // an fp4 operand reads four registers only
           const int ai = FOLD ? wb : p * (D / 128) + wb;
           cacc[FOLD ? p : 0] =
@@ -646,6 +660,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int tbase = 32 * (ln >> 3) + (ln & 7);
   const int slot = (2 * (ln >> 3) + ((ln & 7) >> 2)) * 16 + (ln & 3) * 4;  // byte of grp 0 in a digit row
   const float kscale = 1.f / (float)(1 << (ln & 3));
+  const uint32_t f4_ones = f4_ones_reg();
   const int kofs = 4 * (hl & 1);
   int since_fold = 0;
   float sm_l = 0.f, sq_l = 0.f;  // weight scales WV_WMAX 2^-r / (largest n_V, gamma_V so far)
@@ -662,8 +677,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       for (int p = 0; p < KB; ++p) kw[grp][p] = *reinterpret_cast<const uint32_t *>(stk + p * 1024 + ks * 16 + hl * 4);
     }
     // (the four 16-token groups interleaved, so consecutive MFMAs are independent.  A key word,
-    // coordinates 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit 4 n + t at nibble
-    // bit min(t, 2), i.e. 0.5, 1 or 2)
+    // coordinates 32 hl + 0..31, becomes four fp4 dwords: nibble n of dword t holds bit b = bit 4 n + t,
+    // as 0.5 b, b, 2 b for t = 0, 1, 2 (one AND each) and as 0.5 - b for t = 3 (b in the sign, 0.5 set))
     uint32_t wp[4][KP];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) walsh_planes<KB>(kw[grp], wp[grp]);
@@ -678,7 +693,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         bb[0] = (int)(x & 0x11111111u);
         bb[1] = (int)(x & 0x22222222u);
         bb[2] = (int)(x & 0x44444444u);
-        bb[3] = (int)((x >> 1) & 0x44444444u);
+        bb[3] = f4_sign_half(x, f4_ones);  // +-0.5: 0.5 - bit
         bb[4] = bb[5] = bb[6] = bb[7] = 0;  // an fp4 operand reads four registers only
         cacc[grp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[p], bb, cacc[grp], 0, 4, 0, 0, 0, 0);
       }
@@ -687,16 +702,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   auto digit_sum = [&](const floatx4 (&cacc)[4]) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp)  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
-      sc_next[grp] =
-          cacc[grp][0] + (cacc[grp][1] * 0.0625f + (cacc[grp][2] * (1.f / 512.f) + cacc[grp][3] * (1.f / 16384.f)));
+      sc_next[grp] = fmaf(fmaf(fmaf(cacc[grp][3], 1.f / 32.f, cacc[grp][2]), 1.f / 32.f, cacc[grp][1]), 0.0625f,
+                          cacc[grp][0]);
   };
 
   // step s on the stage in `st` (a fixed ring slot after inlining): its softmax and value pass, with the
   // key pass of step s + 1 (stage in `stn`) issued first, so the matrix cores run it under this step's
-  // vector work
-  auto body = [&, rk, rkn, rvn, rvg, rv](uint8_t *st, const uint8_t *stn, int s) {
+  // vector work.  `whole` (a compile-time flag): all 64 tokens of the step are valid and every head of the
+  // group is present, so no token or head is masked
+  auto body = [&, rk, rkn, rvn, rvg, rv](auto whole, uint8_t *st, const uint8_t *stn, int s) {
+    constexpr bool WHOLE = decltype(whole)::value;
     const int64_t t0 = c0 + (int64_t)s * WV_STEP;
-    const int rem = (int)imax64(imin64(c1 - t0, WV_STEP), 0);  // valid tokens in this step
     const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
     // every body issues one stage, so stages s + 1 and s + 2 are the only loads that may still be in
     // flight: stage s + 1 (the next key pass) has landed once no more than one stage is outstanding
@@ -711,38 +727,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     for (int k = 0; k < 3; ++k)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) hn[k][grp] = nrm[128 * k + tbase + 8 * grp];
-    float sc[4];
+    // ---- scores relative to the reference, d = s - m_ref, and the reference test ----
+    float d[4], fvn[4], fvg[4], mn, mg;
+    if constexpr (WHOLE) {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) sc[grp] = sc_next[grp];
-    // ---- scores and the reference test ----
-    float fk[4], fvn[4], fvg[4];
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      fk[grp] = f16_to_f32((uint16_t)hn[0][grp]);
-      fvn[grp] = f16_to_f32((uint16_t)hn[1][grp]);
-      fvg[grp] = f16_to_f32((uint16_t)hn[2][grp]);
-    }
-    if (rem == WV_STEP && gw == FA_GMAX) {  // a whole step of valid tokens for every head (wave-uniform)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) sc[grp] = fmaf(sc[grp], qinv2, -qconst2) * fk[grp];
+      for (int grp = 0; grp < 4; ++grp)
+        d[grp] = fmaf(fmaf(sc_next[grp], qinv2, -qconst2), f16_to_f32((uint16_t)hn[0][grp]), -m_ref);
+      // the norms are non-negative fp16 numbers, ordered as their bit patterns
+      auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+      mn = f16_to_f32((uint16_t)umax(umax(hn[1][0], hn[1][1]), umax(hn[1][2], hn[1][3])));
+      mg = f16_to_f32((uint16_t)umax(umax(hn[2][0], hn[2][1]), umax(hn[2][2], hn[2][3])));
     } else {
+      const int rem = (int)imax64(imin64(c1 - t0, WV_STEP), 0);  // valid tokens in this step
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const bool valid = tbase + 8 * grp < rem;
-        const float s_ = fmaf(sc[grp], qinv2, -qconst2) * fk[grp];
-        fvn[grp] = valid ? fvn[grp] : 0.f;
-        fvg[grp] = valid ? fvg[grp] : 0.f;
-        sc[grp] = (head_ok && valid) ? s_ : -INFINITY;
+        const float dv = fmaf(fmaf(sc_next[grp], qinv2, -qconst2), f16_to_f32((uint16_t)hn[0][grp]), -m_ref);
+        d[grp] = (head_ok && valid) ? dv : -INFINITY;
+        fvn[grp] = valid ? f16_to_f32((uint16_t)hn[1][grp]) : 0.f;
+        fvg[grp] = valid ? f16_to_f32((uint16_t)hn[2][grp]) : 0.f;
       }
+      mn = fmaxf(fmaxf(fvn[0], fvn[1]), fmaxf(fvn[2], fvn[3]));
+      mg = fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3]));
     }
-    const float ms = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    const float mn = fmaxf(fmaxf(fvn[0], fvn[1]), fmaxf(fvn[2], fvn[3]));
-    const float mg = fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3]));
-    const bool over = ms > m_ref + WV_SLACK || mn > vn_ref || mg > vg_ref;
+    const float dmax = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
+    const uint64_t over = __builtin_amdgcn_ballot_w64(dmax > WV_SLACK) | __builtin_amdgcn_ballot_w64(mn > vn_ref) |
+                          __builtin_amdgcn_ballot_w64(mg > vg_ref);
     ++since_fold;
-    if ((__builtin_amdgcn_ballot_w64(over) != 0ull) || since_fold >= 16384) {
-      // rare: move the reference to this step's maxima and fold the integer accumulators
-      const float smax = rows16_max(ms);
+    if (over != 0ull || since_fold >= 16384) {
+      // rare: move the reference to this step's maxima and fold the integer accumulators (the scores
+      // are formed again from their parts, n_K read again: d holds +inf while the reference is -inf)
+      float sct[4];
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        sct[grp] = d[grp] == -INFINITY ? -INFINITY
+                                       : fmaf(sc_next[grp], qinv2, -qconst2) * f16_to_f32(nrm[tbase + 8 * grp]);
+      const float smax = rows16_max(fmaxf(fmaxf(sct[0], sct[1]), fmaxf(sct[2], sct[3])));
       const float vnm = wave_max_f32(mn);
       const float vgm = wave_max_f32(mg);
       const float m_new = fmaxf(m_ref, smax);
@@ -759,6 +779,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       ym_run *= alpha;
       yq_run *= alpha;
       m_ref = m_new;
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) d[grp] = sct[grp] - m_new;
       vn_ref = fmaxf(vn_ref, WV_NCAP * vnm);
       vg_ref = fmaxf(vg_ref, WV_NCAP * vgm);
       // p <= 2^WV_SLACK and n <= vn_ref, so p n sm_l <= WV_WMAX
@@ -770,31 +792,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     // ---- weights: p n and p gamma as integers below 2^23, three signed byte digits per token ----
     {
-      uint32_t um[4], uq[4], bm[4], bq[4];
+      uint32_t bm[4], bq[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         // p = 2^(s - m_ref) <= 2^WV_SLACK (hardware exp2: results below 2^-126 flush to zero)
-        const float p = __builtin_amdgcn_exp2f(sc[grp] - m_ref);
-        const float wm = p * fvn[grp], wq = p * fvg[grp];
+        const float p = __builtin_amdgcn_exp2f(d[grp]);
         l_run += p;
+        // (whole steps: the fp16 norms enter the products as they are, in mixed-precision FMAs)
+        float wm, wq;
+        if constexpr (WHOLE) {
+          wm = fmaf(p, f16_to_f32((uint16_t)hn[1][grp]), 0.f);
+          wq = fmaf(p, f16_to_f32((uint16_t)hn[2][grp]), 0.f);
+        } else {
+          wm = p * fvn[grp];
+          wq = p * fvg[grp];
+        }
         bm[grp] = __float_as_uint(fmaf(wm, sm_l, WV_MAGIC));
         bq[grp] = __float_as_uint(fmaf(wq, sq_l, WV_MAGIC));
-        um[grp] = bm[grp] ^ 0x808080u;
-        uq[grp] = bq[grp] ^ 0x808080u;
       }
       // the value sums take the rounded weights the matrix cores use, so a weight that rounds to zero
       // drops out of both terms of 2 acc - Y (an error of zero mean) instead of biasing every column:
       // the four integers (the low 23 bits of 2^23 + w) summed as integers, below 2^25
       ym_run = fmaf((float)(bm[0] + bm[1] + bm[2] + bm[3] - 4u * 0x4B000000u), ism_l, ym_run);
       yq_run = fmaf((float)(bq[0] + bq[1] + bq[2] + bq[3] - 4u * 0x4B000000u), isq_l, yq_run);
-      uint32_t dm[3], dq[3];
-      wv_digits(um, dm);
-      wv_digits(uq, dq);
-      if (head_ok) {
+      // digit words (byte g = digit of token grp g), each byte XOR 0x80: the signed digit minus 128
+      uint32_t dgm[3], dgq[3];
+      wv_digits(bm, dgm);
+      wv_digits(bq, dgq);
+      if (WHOLE || head_ok) {
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          *reinterpret_cast<uint32_t *>(&s_w[0][4 * hl + d][slot]) = dm[d];
-          *reinterpret_cast<uint32_t *>(&s_w[1][4 * hl + d][slot]) = dq[d];
+        for (int dd = 0; dd < 3; ++dd) {
+          *reinterpret_cast<uint32_t *>(&s_w[0][4 * hl + dd][slot]) = dgm[dd] ^ 0x80808080u;
+          *reinterpret_cast<uint32_t *>(&s_w[1][4 * hl + dd][slot]) = dgq[dd] ^ 0x80808080u;
         }
       }
     }
@@ -849,11 +878,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       key_mfma(s_ring0, cacc);
       digit_sum(cacc);
     }
-    // (the last step's key pass reads the stage after the chunk: zeros, never used)
-    for (int s = 0; s < nsteps; s += WV_RING) {
-      body(s_ring0, s_ring1, s);
-      body(s_ring1, s_ring2, s + 1);
-      body(s_ring2, s_ring0, s + 2);
+    // (the last step's key pass reads the stage after the chunk: zeros, never used).  Whole ring turns
+    // of whole steps first, then the rest with masking
+    const int nwhole = gw == FA_GMAX && c1 > c0 ? (int)((c1 - c0) / WV_STEP) : 0;
+    int s = 0;
+    for (; s + WV_RING <= nwhole; s += WV_RING) {
+      body(std::true_type{}, s_ring0, s_ring1, s);
+      body(std::true_type{}, s_ring1, s_ring2, s + 1);
+      body(std::true_type{}, s_ring2, s_ring0, s + 2);
+    }
+    for (; s < nsteps; s += WV_RING) {
+      body(std::false_type{}, s_ring0, s_ring1, s);
+      body(std::false_type{}, s_ring1, s_ring2, s + 1);
+      body(std::false_type{}, s_ring2, s_ring0, s + 2);
     }
   }
   // ---- final fold and partial record: m, l, acc_mse[D], acc_qjl[D] ----
@@ -897,20 +934,23 @@ struct PrepArgs {
 // four fixed-point digits of u (|u| <= 224) as e4m3 bytes: u = sum_d k_d Q_d + e with Q_d = 2^(4 - 5 d),
 // k_0 in [-14, 14], k_1..k_3 in [-16, 16] and |e| <= 2^-12.  Byte d holds k_d 2^E_d f, E_0 = 4 and E_d = 3
 // after (each matrix-core row is its own output, so rows 1..3 are lifted clear of the e4m3 floor; their
-// sums are scaled back by Q_d 2^-3), f in {2, 1, 0.5} the inverse of the key nibble's value: every such
-// byte is an e4m3 number (at most 4 significant bits, within 4..448 when not 0).  All products of a digit row are
-// multiples of its 2^E_d and at most 16 of them in size, so the fp8 matrix-core sums are exact (they
-// keep only about 12 bits below the largest product of a sum, so floating digits would not be)
-__device__ __forceinline__ void split_fix4_e4m3(float u, float f, uint8_t (&o)[4]) {
-  float r = u;
+// sums are scaled back by Q_d 2^-3), f in {2, 1, 0.5, -1} set by the key nibble's form: every such byte
+// is an e4m3 number (at most 4 significant bits, within 4..448 when not 0).  All products of a digit row
+// are multiples of half its 2^E_d and at most 16 of them in size, so the fp8 matrix-core sums are exact
+// (they keep only about 12 bits below the largest product of a sum, so floating digits would not be).
+// Returns the digits' value sum_d k_d Q_d (exact in fp32).
+__device__ __forceinline__ float split_fix4_e4m3(float u, float f, uint8_t (&o)[4]) {
+  float r = u, v = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const float q = __builtin_ldexpf(1.f, 4 - 5 * d);
     const float k = rintf(r / q);
     r = fmaf(-k, q, r);
+    v = fmaf(k, q, v);
     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(k * (d == 0 ? 16.f : 8.f) * f, 0.f, 0, false);
     o[d] = (uint8_t)(pk & 0xFF);
   }
+  return v;
 }
 
 // images for the fp8 x fp4 matrix-core key passes
@@ -920,7 +960,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr bool FOLD = fold_beta(D, KB);
   __shared__ float qs[FA_GMAX][D];
   __shared__ float qp[FA_GMAX][D];
-  __shared__ float red[FA_GMAX][2];
+  __shared__ float red[FA_GMAX][3];
   const int unit = blockIdx.x;
   const int sub = unit % a.nsub, bg = unit / a.nsub;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -994,8 +1034,11 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
     // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
     // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
     // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
-    // t = (k % 32) / 8, which carries bit 4 n + t of the block's key word k / 32 as 2^(min(t, 2) - 1):
-    // coordinate 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - min(t, 2))
+    // t = (k % 32) / 8, which carries bit b = bit 4 n + t of the block's key word k / 32 as the value
+    // 2^(t - 1) b for t < 3 and 0.5 - b for t = 3 (bit b in the nibble's sign, 0.5 always set): coordinate
+    // 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - t), or by -1 for t = 3, whose sums then fall
+    // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
+    // taken off the score's offset below)
     constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
     for (int e = threadIdx.x; e < NI8 * 64 * 8; e += 256) {
       const int w = e & 7, lane = (e >> 3) & 63, ii = e >> 9;
@@ -1011,7 +1054,7 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
           const int k = i < 16 ? 16 * g + i : 64 + 16 * g + (i - 16);
           const int t = (k & 31) >> 3, n = k & 7;
           const int j = 128 * wb + 32 * (k >> 5) + 4 * n + t;
-          const float f = t == 0 ? 2.f : t == 1 ? 1.f : 0.5f;
+          const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
           uint8_t o[4];
           split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * sq, -224.f), 224.f), f, o);
           word |= (uint32_t)o[dg] << (8 * bb);
@@ -1019,12 +1062,36 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
       }
       a.qimg[(((int64_t)unit * NI8 + ii) * 64 + lane) * 8 + w] = (int)word;
     }
+    // per head: half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
+    {
+      const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      const float mx = red[h][1] * bmax;
+      const float sq = mx > 0.f ? 224.f / mx : 0.f;
+      float cs = 0.f;
+      if (h < gw) {
+        for (int e = lane; e < (FOLD ? 1 : KP) * (D / 4); e += 64) {
+          const int p = e / (D / 4), j = 4 * (e % (D / 4)) + 3;
+          uint8_t o[4];
+          cs += split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * sq, -224.f), 224.f), -1.f, o);
+        }
+      }
+      cs = wave_sum_f32(cs);
+      if (FOLD) {
+        float bs = 0.f;
+#pragma unroll
+        for (int p = 0; p < KP; ++p) bs += 2.f * a.kbeta[p];
+        cs *= bs;
+      }
+      if (lane == 0) red[h][2] = 0.5f * cs;
+    }
+    __syncthreads();
     if (threadIdx.x < FA_GMAX) {
       const int h = threadIdx.x;
       const float mx = red[h][1] * bmax;
       const float sq = mx > 0.f ? 224.f / mx : 0.f;
-      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
-      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] : 0.f;
+      const float qinv = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
+      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = qinv;
+      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] - red[h][2] * qinv : 0.f;
     }
   }
 }
