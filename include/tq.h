@@ -186,9 +186,13 @@ size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, i
  *     returns the summed elapsed time and number of launches of kernels whose
  *     name contains `name` (NULL or "" = all).  Kernel names are listed in the
  *     design notes (e.g. "attn_split", "attn_combine", "encode").
+ *   tq_profile_select(name): while enabled, records only the launches whose
+ *     kernel name contains `name` (NULL or "" = all, the default), so a timed
+ *     loop can bracket one kernel without events around its neighbours.
  *   tq_profile_reset(): drops all recorded launches.
  * Thread-safe; events are shared by all streams of the process. */
 int tq_profile_enable(int on);
+int tq_profile_select(const char *name);
 int tq_profile_query(const char *name, double *total_ms, int64_t *count);
 int tq_profile_reset(void);
 

@@ -35,6 +35,7 @@ SIGNATURES = [
     ("tq_attn_decode", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ, _P]),
     ("tq_attn_decode_ws_bytes", _SZ, [_P, _I, _I, _I, _I64, _I]),
     ("tq_profile_enable", _I, [_I]),
+    ("tq_profile_select", _I, [C.c_char_p]),
     ("tq_profile_query", _I, [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     ("tq_profile_reset", _I, []),
     ("tq_status_str", C.c_char_p, [_I]),
@@ -88,6 +89,11 @@ def codebook_build(d: int, bits: int):
 
 def profile_enable(on: bool = True):
     _check("tq_profile_enable", load().tq_profile_enable(1 if on else 0))
+
+
+def profile_select(name: str = ""):
+    """Record only launches whose kernel name contains `name` ("" = all)."""
+    _check("tq_profile_select", load().tq_profile_select(name.encode()))
 
 
 def profile_reset():

@@ -953,146 +953,132 @@ __device__ __forceinline__ float split_fix4_e4m3(float u, float f, uint8_t (&o)[
   return v;
 }
 
-// images for the fp8 x fp4 matrix-core key passes
+// images for the fp8 x fp4 matrix-core key passes: one work-group per (unit, head of its group), so the
+// four heads' images are made in parallel
 template <int D, int KB>
 __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr int KP = walsh_count(KB);
   constexpr bool FOLD = fold_beta(D, KB);
-  __shared__ float qs[FA_GMAX][D];
-  __shared__ float qp[FA_GMAX][D];
-  __shared__ float red[FA_GMAX][3];
-  const int unit = blockIdx.x;
+  __shared__ float qs[D];
+  __shared__ float qp[D];
+  __shared__ float red[4][2];
+  const int unit = blockIdx.x, h = blockIdx.y;
   const int sub = unit % a.nsub, bg = unit / a.nsub;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
-  for (int e = threadIdx.x; e < FA_GMAX * D; e += 256) {
-    const int h = e / D, j = e % D;
+  const bool present = h < gw;  // a head past the group's end gets zero images and offsets
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  for (int j = tid; j < D; j += 256) {
     float v = 0.f;
-    if (h < gw) {
+    if (present) {
       const int64_t off = ((int64_t)b * a.Hq + h0 + h) * D + j;
       if (a.qt == TQ_F32) v = static_cast<const float *>(a.q)[off];
       else if (a.qt == TQ_BF16) v = bf16_to_f32(static_cast<const uint16_t *>(a.q)[off]);
       else v = f16_to_f32(static_cast<const uint16_t *>(a.q)[off]);
     }
-    qs[h][j] = v;
+    qs[j] = v;
   }
-  if (threadIdx.x < FA_GMAX * 2) red[threadIdx.x / 2][threadIdx.x % 2] = 0.f;
   __syncthreads();
-  // q'_j = sum_k Pi^T[k][j] q_k for the group's heads: thread (slice, j) sums a slice of k for column j
-  // (consecutive threads read consecutive entries of a row of Pi^T; the unrolled loop keeps many
-  // independent loads in flight), and the slices are added through LDS
+  // q'_j = sum_k Pi^T[k][j] q_k: thread (slice, j) sums a slice of k for column j (consecutive threads
+  // read consecutive entries of a row of Pi^T; the unrolled loop keeps many independent loads in
+  // flight), and the slices are added through LDS
   for (int jc = 0; jc < (D > 256 ? D / 256 : 1); ++jc) {
     constexpr int SL = D >= 256 ? 1 : 256 / D;  // k slices (2 for head_dim 128, else 1)
-    const int j = (threadIdx.x % (D < 256 ? D : 256)) + 256 * jc, sl = D < 256 ? threadIdx.x / D : 0;
-    float acc[FA_GMAX] = {0.f, 0.f, 0.f, 0.f};
+    const int j = (tid % (D < 256 ? D : 256)) + 256 * jc, sl = D < 256 ? tid / D : 0;
+    float acc = 0.f;
     constexpr int KS = D / SL, KU = KS < 64 ? KS : 64;
     for (int k0 = sl * KS; k0 < (sl + 1) * KS; k0 += KU) {
       float pv[KU];  // a whole batch of loads in flight at once
 #pragma unroll
       for (int i = 0; i < KU; ++i) pv[i] = a.piT[(int64_t)(k0 + i) * D + j];
 #pragma unroll
-      for (int i = 0; i < KU; ++i)
-#pragma unroll
-        for (int h = 0; h < FA_GMAX; ++h) acc[h] = fmaf(pv[i], qs[h][k0 + i], acc[h]);
+      for (int i = 0; i < KU; ++i) acc = fmaf(pv[i], qs[k0 + i], acc);
     }
     if (SL > 1) {
-      if (sl == 1) {
-#pragma unroll
-        for (int h = 0; h < FA_GMAX; ++h) qp[h][j] = acc[h];
-      }
+      if (sl == 1) qp[j] = acc;
       __syncthreads();
-      if (sl == 0) {
-#pragma unroll
-        for (int h = 0; h < FA_GMAX; ++h) qp[h][j] += acc[h];
-      }
+      if (sl == 0) qp[j] += acc;
     } else {
-#pragma unroll
-      for (int h = 0; h < FA_GMAX; ++h) qp[h][j] = acc[h];
+      qp[j] = acc;
     }
   }
   __syncthreads();
-  // per head: sum q' and max |q'_j 2^-k_j|
+  // sum q' and max |q'_j|
   {
-    const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float sm = 0.f, mx = 0.f;
-    for (int j = lane; j < D; j += 64) {
-      sm += qp[h][j];
-      mx = fmaxf(mx, fabsf(qp[h][j]));
+    for (int j = tid; j < D; j += 256) {
+      sm += qp[j];
+      mx = fmaxf(mx, fabsf(qp[j]));
     }
     sm = wave_sum_f32(sm);
     mx = wave_max_f32(mx);
-    if (lane == 0) { red[h][0] = sm; red[h][1] = mx; }
+    if (lane == 0) { red[wv][0] = sm; red[wv][1] = mx; }
   }
   __syncthreads();
+  const float qsum = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
   float bmax = 0.f;
 #pragma unroll
   for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
   if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
-  {
-    // image ii (FOLD: the 128-coordinate block ii, coefficients applied after the matrix cores; else
-    // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
-    // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
-    // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
-    // t = (k % 32) / 8, which carries bit b = bit 4 n + t of the block's key word k / 32 as the value
-    // 2^(t - 1) b for t < 3 and 0.5 - b for t = 3 (bit b in the nibble's sign, 0.5 always set): coordinate
-    // 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - t), or by -1 for t = 3, whose sums then fall
-    // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
-    // taken off the score's offset below)
-    constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
-    for (int e = threadIdx.x; e < NI8 * 64 * 8; e += 256) {
-      const int w = e & 7, lane = (e >> 3) & 63, ii = e >> 9;
-      const int wb = ii % (D / 128), p = ii / (D / 128);
-      const int m = lane & 15, h = m >> 2, dg = m & 3, g = lane >> 4;
-      uint32_t word = 0;
-      if (h < gw) {
-        const float mx = red[h][1] * bmax;
-        const float sq = mx > 0.f ? 224.f / mx : 0.f;
+  const float mxs = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1])) * bmax;
+  const float sq = mxs > 0.f ? 224.f / mxs : 0.f;
+  // image ii (FOLD: the 128-coordinate block ii, coefficients applied after the matrix cores; else
+  // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
+  // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
+  // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
+  // t = (k % 32) / 8, which carries bit b = bit 4 n + t of the block's key word k / 32 as the value
+  // 2^(t - 1) b for t < 3 and 0.5 - b for t = 3 (bit b in the nibble's sign, 0.5 always set): coordinate
+  // 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - t), or by -1 for t = 3, whose sums then fall
+  // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
+  // taken off the score's offset below).  This work-group writes the 16 lanes of its head (rows 4 h ..
+  // 4 h + 3 of the four lane groups) in every image.
+  constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
+  for (int e = tid; e < NI8 * 16 * 8; e += 256) {
+    const int w = e & 7, r = (e >> 3) & 15, ii = e >> 7;
+    const int wb = ii % (D / 128), p = ii / (D / 128);
+    const int dg = r & 3, gg = r >> 2, il = 16 * gg + 4 * h + dg;
+    uint32_t word = 0;
+    if (present) {
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int i = 4 * w + bb;
-          const int k = i < 16 ? 16 * g + i : 64 + 16 * g + (i - 16);
-          const int t = (k & 31) >> 3, n = k & 7;
-          const int j = 128 * wb + 32 * (k >> 5) + 4 * n + t;
-          const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
-          uint8_t o[4];
-          split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * sq, -224.f), 224.f), f, o);
-          word |= (uint32_t)o[dg] << (8 * bb);
-        }
+      for (int bb = 0; bb < 4; ++bb) {
+        const int i = 4 * w + bb;
+        const int k = i < 16 ? 16 * gg + i : 64 + 16 * gg + (i - 16);
+        const int t = (k & 31) >> 3, n = k & 7;
+        const int j = 128 * wb + 32 * (k >> 5) + 4 * n + t;
+        const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
+        uint8_t o[4];
+        split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), f, o);
+        word |= (uint32_t)o[dg] << (8 * bb);
       }
-      a.qimg[(((int64_t)unit * NI8 + ii) * 64 + lane) * 8 + w] = (int)word;
     }
-    // per head: half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
-    {
-      const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
-      const float mx = red[h][1] * bmax;
-      const float sq = mx > 0.f ? 224.f / mx : 0.f;
-      float cs = 0.f;
-      if (h < gw) {
-        for (int e = lane; e < (FOLD ? 1 : KP) * (D / 4); e += 64) {
-          const int p = e / (D / 4), j = 4 * (e % (D / 4)) + 3;
-          uint8_t o[4];
-          cs += split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[h][j] * sq, -224.f), 224.f), -1.f, o);
-        }
-      }
-      cs = wave_sum_f32(cs);
-      if (FOLD) {
-        float bs = 0.f;
+    a.qimg[(((int64_t)unit * NI8 + ii) * 64 + il) * 8 + w] = (int)word;
+  }
+  // half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
+  float cs = 0.f;
+  if (present) {
+    for (int e = tid; e < (FOLD ? 1 : KP) * (D / 4); e += 256) {
+      const int p = e / (D / 4), j = 4 * (e % (D / 4)) + 3;
+      uint8_t o[4];
+      cs += split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), -1.f, o);
+    }
+  }
+  cs = wave_sum_f32(cs);
+  __syncthreads();  // every read of red above is done
+  if (lane == 0) red[wv][0] = cs;
+  __syncthreads();
+  if (tid == 0) {
+    float c = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+    if (FOLD) {
+      float bs = 0.f;
 #pragma unroll
-        for (int p = 0; p < KP; ++p) bs += 2.f * a.kbeta[p];
-        cs *= bs;
-      }
-      if (lane == 0) red[h][2] = 0.5f * cs;
+      for (int p = 0; p < KP; ++p) bs += 2.f * a.kbeta[p];
+      c *= bs;
     }
-    __syncthreads();
-    if (threadIdx.x < FA_GMAX) {
-      const int h = threadIdx.x;
-      const float mx = red[h][1] * bmax;
-      const float sq = mx > 0.f ? 224.f / mx : 0.f;
-      const float qinv = (h < gw && sq > 0.f) ? 1.f / sq : 0.f;
-      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = qinv;
-      a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = h < gw ? a.ctop * red[h][0] - red[h][2] * qinv : 0.f;
-    }
+    c *= 0.5f;
+    const float qinv = (present && sq > 0.f) ? 1.f / sq : 0.f;
+    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = qinv;
+    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = present ? a.ctop * qsum - c * qinv : 0.f;
   }
 }
 
@@ -1242,7 +1228,7 @@ template <int D, int KB, int VB>
 int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, int units, hipStream_t st) {
   {
     ProfScope ps("attn_prep", st);
-    hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units), dim3(256), 0, st, pa);
+    hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
   }
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
@@ -1308,9 +1294,9 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   if (wave) {
     {
       ProfScope ps("attn_prep", st);
-      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2>), dim3(units), dim3(256), 0, st, pa);
-      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3>), dim3(units), dim3(256), 0, st, pa);
+      if (KB == 1) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 1>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+      if (KB == 2) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 2>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+      if (KB == 3) hipLaunchKernelGGL((attn_fast_prep_kernel<128, 3>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {

@@ -19,6 +19,7 @@ struct Rec {
 
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
+std::string g_select;  // record only launches whose name contains this (empty: all)
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -41,6 +42,7 @@ bool profiling() { return g_on.load(std::memory_order_relaxed); }
 void *prof_begin(const char *name, hipStream_t st) {
   if (!profiling()) return nullptr;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_select.empty() && std::strstr(name, g_select.c_str()) == nullptr) return nullptr;
   hipEvent_t a = get_event(), b = get_event();
   if (!a || !b) return nullptr;
   hipEventRecord(a, st);
@@ -61,6 +63,12 @@ extern "C" {
 
 int tq_profile_enable(int on) {
   tq::g_on.store(on != 0);
+  return TQ_OK;
+}
+
+int tq_profile_select(const char *name) {
+  std::lock_guard<std::mutex> lk(tq::g_mu);
+  tq::g_select = name ? name : "";
   return TQ_OK;
 }
 
