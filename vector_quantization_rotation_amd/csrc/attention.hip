@@ -272,12 +272,122 @@ __global__ __launch_bounds__(256) void attn_rotate_generic_kernel(const float *m
   }
 }
 
+// Head dims up to 256: both steps in one kernel.  A work-group takes four rows and 32 output columns;
+// its matrix entries are loaded first (in flight during the merge), each wave merges the splits' weights
+// of one row (the largest split maximum M and the total weight L, then each split's factor
+// 2^(m_s - M) / L into LDS), the four rows' entries of A are merged into LDS, and the rotation reads them
+// there.  The merge is repeated by the d / 32 work-groups of a row group (its inputs are few kilobytes).
+constexpr int CMB_SPLITS = 256;  // splits whose factors fit in LDS; beyond, the separate kernels run
+template <int PER>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float *part, int64_t BH, int nsplit, int d,
+                                                           const float *pi, const float *s, float *out) {
+  constexpr int HB = 4;
+  __shared__ float sf[HB][CMB_SPLITS];  // 2^(m_s - M) / L per row and split (0 for empty splits)
+  __shared__ float sa[HB][8 * PER];     // the rows' A (2d = 8 PER entries)
+  __shared__ float red[HB][8][33];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int64_t bh0 = (int64_t)blockIdx.x * HB;
+  const int c = tid & 31, sl = tid >> 5;
+  const int j = blockIdx.y * 32 + c;
+  const int t0 = sl * PER;
+  const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
+  float m[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) m[i] = mrow[(int64_t)i * d];
+  const int64_t rec = 2 + 2 * (int64_t)d;
+  {  // wave wv: the split factors of row bh0 + wv (each lane keeps its splits' m and l: 4 per lane here)
+    const float *pp = part + imin64(bh0 + wv, BH - 1) * nsplit * rec;
+    constexpr int QL = CMB_SPLITS / 64;
+    float mq[QL], lq[QL];
+#pragma unroll
+    for (int k = 0; k < QL; ++k) {
+      const int q = lane + 64 * k;
+      mq[k] = q < nsplit ? pp[q * rec] : 0.f;
+      lq[k] = q < nsplit ? pp[q * rec + 1] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < QL; ++k)
+      if (lq[k] > 0.f) M = fmaxf(M, mq[k]);
+    M = wave_max_f32(M);
+    float fq[QL], L = 0.f;
+#pragma unroll
+    for (int k = 0; k < QL; ++k) {
+      fq[k] = lq[k] > 0.f ? exp2f(mq[k] - M) : 0.f;
+      L = fmaf(lq[k], fq[k], L);
+    }
+    L = wave_sum_f32(L);
+    const float il = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int k = 0; k < QL; ++k) sf[wv][lane + 64 * k] = fq[k] * il;
+  }
+  __syncthreads();
+  {  // this thread's entries of A: e = tid + 256 i, every split's value loaded in one batch per chunk
+    constexpr int EPT = HB * 8 * PER / 256;
+    constexpr int QC = 64 / EPT < FIN_CHUNK ? 64 / EPT : FIN_CHUNK;
+    float a[EPT];
+    const float *pe[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i, h = e / (8 * PER), t = e % (8 * PER);
+      pe[i] = part + imin64(bh0 + h, BH - 1) * nsplit * rec + 2 + t;
+      a[i] = 0.f;
+    }
+    for (int q0 = 0; q0 < nsplit; q0 += QC) {
+      float v[EPT][QC];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+#pragma unroll
+        for (int k = 0; k < QC; ++k) v[i][k] = pe[i][imin32(q0 + k, nsplit - 1) * rec];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int h = (tid + 256 * i) / (8 * PER);
+#pragma unroll
+        for (int k = 0; k < QC; ++k)
+          if (q0 + k < nsplit) a[i] = fmaf(v[i][k], sf[h][q0 + k], a[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i;
+      sa[e / (8 * PER)][e % (8 * PER)] = a[i];
+    }
+  }
+  __syncthreads();
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v = fmaf(m[i], sa[h][t0 + i], v);
+    acc[h] = v;
+    red[h][sl][c] = v;
+  }
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      float v = acc[h];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) v += red[h][q][c];
+      if (bh0 + h < BH) out[(bh0 + h) * d + j] = v;
+    }
+  }
+}
+
 size_t attn_merge_ws_bytes(int BH, int d) { return (size_t)BH * 2 * d * sizeof(float); }
 
 int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
                  float *out, hipStream_t st) {
   if (BH == 0) return TQ_OK;
   ProfScope ps("attn_combine", st);
+  if (nsplit <= CMB_SPLITS && (d == 64 || d == 128 || d == 256)) {
+    const dim3 grid((unsigned)cdiv64(BH, 4), (unsigned)(d / 32));
+    if (d == 64) hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);
+    if (d == 128) hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);
+    if (d == 256) hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);
+    return launch_check();
+  }
   const int64_t n = (int64_t)BH * 2 * d;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, part, (int64_t)BH, nsplit, d,
                      merged);
