@@ -12,10 +12,12 @@
 //   for b = 3: planes b0, b1, b2 and the parity b0^b1^b2).  Each term is a 0/1
 //   bit plane, so <q', c[idx]> = 2 sum_S beta_S <q', bits_S> - c[L-1] sum_j q'_j.
 // * Keys: a plane word (32 coordinates) feeds v_mfma_f32_16x16x128_f8f6f4 as
-//   four fp4 dwords (x & 0x11111111, x & 0x22222222, x & 0x44444444,
-//   (x >> 1) & 0x44444444: nibble values 0.5, 1, 2); the query images are four
-//   fixed-point e4m3 digits per head (one MFMA row each) carrying the inverse
-//   nibble factor, and every digit row's sum is exact (see split_fix4_e4m3).
+//   four fp4 dwords (x & 0x11111111, x & 0x22222222, x & 0x44444444: nibble
+//   values 0.5, 1, 2 times the bit; (x & 0x88888888) | 0x11111111: 0.5 - bit);
+//   the query images are four fixed-point e4m3 digits per head (one MFMA row
+//   each) carrying the inverse nibble factor (-1 for the sign form, whose
+//   constant the prep kernel takes off the score offset), and every digit row's
+//   sum is exact (see split_fix4_e4m3).
 // * Values: a 0/1 plane word feeds v_mfma_i32_16x16x64_i8 directly:
 //   (w & 0x01010101 << k) holds four bits as bytes of value 2^k; the 2^-k is
 //   folded into the softmax weights, which are split into signed byte digits,
@@ -23,10 +25,12 @@
 // * Keys stay in per-token records (their bits run along the contraction).
 //   Values are read from the token-tiled layout (32 tokens per word) so that
 //   the contraction over tokens also runs along the word bits.
-// * Each work-group owns a (batch, kv-head, head group, sequence chunk) and
-//   walks it in 256-token steps: score (key pass), turn the scores into int8
-//   weight digits in LDS, aggregate (value pass); online softmax with a
-//   rarely-moving reference maximum.
+// * attn_fast_kernel: each work-group of 4 waves owns a (batch, kv-head, head
+//   group, sequence chunk) and walks it in 256-token steps: score (key pass),
+//   turn the scores into int8 weight digits in LDS, aggregate (value pass);
+//   online softmax with a rarely-moving reference maximum.  attn_wave_kernel
+//   (head_dim 128, 1-bit value indices): one wave per work-group streams its
+//   chunk in 64-token steps through a three-slot LDS ring.
 #include <algorithm>
 #include <type_traits>
 
