@@ -244,6 +244,7 @@ ATTN_FAST_CASES = [
     (1, 4, 4, 256, [256], 128, 1, 2),
     (2, 24, 4, 520, [520, 0], 128, 3, 2),        # 6 heads per kv head: a full and a partial head group
     (1, 4, 1, 192, [130], 128, 3, 2),            # one ring turn, the last step partly valid
+    (1, 4, 1, 65536, [65000], 128, 3, 2),        # more than 256 sequence splits: separate merge and rotation
     (1, 32, 8, 30000, [29999], 128, 3, 2),       # many steps per wave
     # head_dim 512 (global-layer shape): Walsh coefficients applied after the matrix cores
     (1, 8, 1, 1000, [1000], 512, 3, 2),
