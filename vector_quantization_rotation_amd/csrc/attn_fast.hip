@@ -710,9 +710,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
                           cacc[grp][0]);
   };
 
-  // step s on the stage in `st` (a fixed ring slot after inlining): its softmax and value pass, with the
-  // key pass of step s + 1 (stage in `stn`) issued first, so the matrix cores run it under this step's
-  // vector work.  `whole` (a compile-time flag): all 64 tokens of the step are valid and every head of the
+  // step s on the stage in `st` (a fixed ring slot after inlining): its softmax, then the key pass of step
+  // s + 1 (stage in `stn`) and its own value pass back to back on the matrix cores, the next step's scores
+  // formed from the key-pass sums at the end.  `whole` (a compile-time flag): all 64 tokens of the step are valid and every head of the
   // group is present, so no token or head is masked
   auto body = [&, rk, rkn, rvn, rvg, rv](auto whole, uint8_t *st, const uint8_t *stn, int s) {
     constexpr bool WHOLE = decltype(whole)::value;
@@ -721,10 +721,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     // every body issues one stage, so stages s + 1 and s + 2 are the only loads that may still be in
     // flight: stage s + 1 (the next key pass) has landed once no more than one stage is outstanding
     wv_wait_vm<S::NLOAD>();
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- key pass of step s + 1 (fp8 query digits x fp4 key bits) ----
-    floatx4 cacc[4];
-    key_mfma(stn, cacc);
     __builtin_amdgcn_sched_barrier(0);
     uint32_t hn[3][4];  // fp16 of token tbase + 8 grp in the three arrays (128 halves apart)
 #pragma unroll
@@ -831,8 +827,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         }
       }
     }
-    // the next step's image sums (its key pass has run under this step's softmax)
-    digit_sum(cacc);
     // ---- the value words (four adjacent columns per read; column tile c of this lane is column
     // 64 (c / 4) + 4 ln + c % 4), the last reads of this slot: then refill it one ring turn ahead ----
     uint4 vw[2][2];  // [plane][column half]
@@ -858,6 +852,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     __builtin_amdgcn_sched_barrier(0);
     wv_stage_load<KB>(st, rk, rv, rkn, rvn, rvg, lane, voff_k, voff_n, t0 + WV_RING * WV_STEP);
     __builtin_amdgcn_sched_barrier(0);
+    // ---- key pass of step s + 1 (fp8 query digits x fp4 key bits), then the value pass of step s: the
+    // matrix cores take both in turn while the vector units expand their bits ----
+    floatx4 cacc[4];
+    key_mfma(stn, cacc);
     // ---- value pass: 64 tokens x 128 columns, both kinds ----
     {
       const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_w[0][ln][16 * hl]);
@@ -869,6 +867,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         vacc[1][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q, wv_value_bits(w1, kofs), vacc[1][c], 0, 0, 0);
       }
     }
+    // the next step's image sums
+    digit_sum(cacc);
   };
 
   if (nsteps > 0) {
