@@ -194,7 +194,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, split = blockIdx.y;
-  const int sub = unit % a.nsub, bg = unit / a.nsub;
+  const int nbg = (int)gridDim.x / a.nsub;  // (batch, kv-head) pairs; units = nbg x head subgroups
+  const int sub = unit / nbg, bg = unit % nbg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
@@ -607,7 +608,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int lane = threadIdx.x;
   const int hl = lane >> 4, ln = lane & 15;
   const int unit = blockIdx.x, split = blockIdx.y;
-  const int sub = unit % a.nsub, bg = unit / a.nsub;
+  const int nbg = (int)gridDim.x / a.nsub;  // (batch, kv-head) pairs; units = nbg x head subgroups
+  const int sub = unit / nbg, bg = unit % nbg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
@@ -967,7 +969,8 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   __shared__ float qp[D];
   __shared__ float red[4][2];
   const int unit = blockIdx.x, h = blockIdx.y;
-  const int sub = unit % a.nsub, bg = unit / a.nsub;
+  const int nbg = (int)gridDim.x / a.nsub;  // (batch, kv-head) pairs; units = nbg x head subgroups
+  const int sub = unit / nbg, bg = unit % nbg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
