@@ -382,3 +382,35 @@ def test_bf16_and_f16_inputs_match_f32(api):
     c32, n32, _ = qz.encode(_dev(x16))
     c16, n16, _ = qz.encode(_dev(x16).to(torch.float16))
     assert torch.equal(c32, c16) and torch.equal(n32, n16)
+
+
+def test_profile_select_brackets_named_kernels(api):
+    """tq_profile_select: while a name is selected only the matching launches record events; "" selects
+    every launch again (the attention step launches prep, the wave kernel and the finish)."""
+    from vector_quantization_rotation_amd import _lib, workloads
+    d, T = 128, 256
+    c = workloads.build_attention_cache(1, 4, 1, T, d)
+    seq = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 4, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty((api.attn_decode_ws_bytes(c.kq, 1, 4, 1, T, api.TQ_LAYOUT_TILE32),), dtype=torch.uint8,
+                     device="cuda")
+    step = api.attn_decode_bound(c.kq, c.vq, c.q, c.kcodes, c.knorms, c.vtiles, c.vnorms, c.vgammas, seq,
+                                 1 / math.sqrt(d), out, ws, vlayout=api.TQ_LAYOUT_TILE32)
+    try:
+        for sel, expect in (("attn_split", {"attn_split": 2, "attn_prep": 0, "attn_combine": 0}),
+                            ("", {"attn_split": 2, "attn_prep": 2, "attn_combine": 2})):
+            _lib.profile_reset()
+            _lib.profile_select(sel)
+            _lib.profile_enable(True)
+            step()
+            step()
+            torch.cuda.synchronize()
+            _lib.profile_enable(False)
+            for name, n in expect.items():
+                ms, cnt = _lib.profile_query(name)
+                assert cnt == n, (sel, name, cnt)
+                assert (ms > 0) == (n > 0), (sel, name, ms)
+    finally:
+        _lib.profile_enable(False)
+        _lib.profile_select("")
+        _lib.profile_reset()
