@@ -21,13 +21,21 @@ i.e. (u+1)/2 ~ Beta((d-1)/2, (d-1)/2).  Its limit for large d is N(0, 1/d).
 """
 from __future__ import annotations
 
+import mpmath
 import numpy as np
-from scipy.special import betainc, gammaln, ndtri
+from scipy.special import betainc, ndtri
 from scipy.stats import norm as _norm
 
 
 def _log_norm_const(d: int) -> float:
-    return float(gammaln(d / 2.0) - 0.5 * np.log(np.pi) - gammaln((d - 1) / 2.0))
+    """log of Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)), the density's normalising constant.
+
+    Evaluated with 50-digit log-gammas: in fp64 the difference of the two
+    log-gammas loses up to 4e-11 of relative precision at d = 65536.
+    """
+    with mpmath.workdps(50):
+        v = mpmath.loggamma(mpmath.mpf(d) / 2) - mpmath.loggamma(mpmath.mpf(d - 1) / 2) - mpmath.log(mpmath.pi) / 2
+        return float(v)
 
 
 def coord_density(u, d: int):

@@ -46,12 +46,35 @@ def test_status_strings():
 @pytest.mark.parametrize("d", [3, 64, 128, 256, 512, 1536])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_codebook_matches_oracle(d, bits):
+    # the library integrates cell masses by Gauss-Legendre quadrature in the angle u = sin(th);
+    # the oracle uses the regularized incomplete beta function: two independent routes to one
+    # fixed point, which agree to 1e-12 relative
     c, t = _lib.codebook_build(d, bits)
     co, to = oracle.lloyd_max(d, bits)
-    # the two builders normalise the law differently; they agree far below fp32 resolution
-    assert np.allclose(c, co, rtol=5e-11, atol=0)
-    assert np.allclose(t, to, rtol=5e-11, atol=1e-300)
+    assert np.allclose(c, co, rtol=1e-12, atol=0)
+    assert np.allclose(t, to, rtol=1e-12, atol=1e-300)
     assert np.array_equal(c, -c[::-1])
+
+
+@pytest.mark.parametrize("d", [3, 4, 5, 64, 128, 1536, 65536])
+def test_codebook_one_bit_closed_form(d):
+    # b = 1: boundary 0 and centroid E[U | U > 0] = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+    import mpmath
+    c, t = _lib.codebook_build(d, 1)
+    with mpmath.workdps(40):
+        expect = float(mpmath.gamma(mpmath.mpf(d) / 2) / (mpmath.sqrt(mpmath.pi) * mpmath.gamma(mpmath.mpf(d + 1) / 2)))
+    assert t[0] == 0.0
+    assert c[1] == pytest.approx(expect, rel=2e-15)
+    assert c[0] == -c[1]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_d3_is_uniform_quantizer(bits):
+    # d = 3: the coordinate law is uniform on [-1, 1] (Archimedes), so Lloyd-Max is the uniform quantizer
+    L = 1 << bits
+    c, t = _lib.codebook_build(3, bits)
+    assert np.allclose(c, -1 + (2 * np.arange(L) + 1) / L, rtol=0, atol=1e-14)
+    assert np.allclose(t, -1 + 2 * np.arange(1, L) / L, rtol=0, atol=1e-14)
 
 
 def test_codebook_invalid_arguments():

@@ -11,8 +11,8 @@ import os
 
 import numpy as np
 import pytest
+import mpmath
 from scipy.integrate import quad
-from scipy.special import gammaln
 
 import oracle
 from oracle.codebook import distortion
@@ -63,9 +63,10 @@ def test_d3_lloyd_max_is_uniform_quantizer(bits):
 def test_one_bit_centroid_closed_form(d):
     # b = 1: boundary 0, centroid E[U | U > 0] = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
     c, t = oracle.lloyd_max(d, 1)
-    expect = math.exp(gammaln(d / 2) - 0.5 * math.log(math.pi) - gammaln((d + 1) / 2))
+    with mpmath.workdps(40):
+        expect = float(mpmath.gamma(mpmath.mpf(d) / 2) / (mpmath.sqrt(mpmath.pi) * mpmath.gamma(mpmath.mpf(d + 1) / 2)))
     assert t[0] == 0.0
-    assert c[1] == pytest.approx(expect, rel=1e-13)
+    assert c[1] == pytest.approx(expect, rel=2e-15)
     assert c[0] == -c[1]
 
 

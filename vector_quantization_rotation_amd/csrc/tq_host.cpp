@@ -2,6 +2,7 @@
 // quantizer lifecycle and dispatch to the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -16,62 +17,98 @@ thread_local int g_last_hip_error = 0;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
-// Coordinate law of a uniform point on S^{d-1}: density C_d (1-u^2)^((d-3)/2)
-// on [-1, 1] (the Beta-shaped law of the AiBoss overview, section
-// "TurboQuantの技術原理").  Cell masses come from the continued fraction of the
-// incomplete beta function (DLMF 8.17.22), evaluated by the modified Lentz
-// method.
+// Coordinate law of a uniform point on S^{d-1}: density proportional to
+// (1-u^2)^((d-3)/2) on [-1, 1] (the Beta-shaped law of the AiBoss overview,
+// section "TurboQuantの技術原理").
+//
+// Lloyd-Max needs, per cell [lo, hi] of the positive half-line, the cell's
+// mass and first moment.  With u = sin(th) both become integrals over an
+// angle:
+//   mass(lo, hi)   = integral over [asin lo, asin hi] of cos(th)^(d-2) dth
+//   moment(lo, hi) = ((1-lo^2)^((d-1)/2) - (1-hi^2)^((d-1)/2)) / (d-1)
+// The angular integrand is analytic (no endpoint singularity for any d >= 3),
+// so composite Gauss-Legendre quadrature converges geometrically.  Both
+// quantities are carried relative to the density at `lo` (its maximum on the
+// cell), so nothing underflows at large d; the normalising constant cancels
+// in the conditional mean and is never evaluated.
 // ---------------------------------------------------------------------------
-double beta_cf(double a, double b, double x) {
-  const double tiny = 1e-300, eps = 1e-17;
-  double qab = a + b, qap = a + 1.0, qam = a - 1.0;
-  double c = 1.0, dd = 1.0 - qab * x / qap;
-  if (std::fabs(dd) < tiny) dd = tiny;
-  dd = 1.0 / dd;
-  double h = dd;
-  for (int m = 1; m <= 100000; ++m) {
-    double m2 = 2.0 * m;
-    double aa = m * (b - m) * x / ((qam + m2) * (a + m2));
-    dd = 1.0 + aa * dd;
-    if (std::fabs(dd) < tiny) dd = tiny;
-    c = 1.0 + aa / c;
-    if (std::fabs(c) < tiny) c = tiny;
-    dd = 1.0 / dd;
-    h *= dd * c;
-    aa = -(a + m) * (qab + m) * x / ((a + m2) * (qap + m2));
-    dd = 1.0 + aa * dd;
-    if (std::fabs(dd) < tiny) dd = tiny;
-    c = 1.0 + aa / c;
-    if (std::fabs(c) < tiny) c = tiny;
-    dd = 1.0 / dd;
-    double del = dd * c;
-    h *= del;
-    if (std::fabs(del - 1.0) < eps) break;
+constexpr int kGaussNodes = 24;
+
+struct GaussLegendre {
+  double x[kGaussNodes], w[kGaussNodes];  // nodes and weights on [-1, 1]
+  GaussLegendre() {
+    // Newton's method on the Legendre polynomial P_n, started from the
+    // asymptotic root estimate cos(pi (i + 3/4) / (n + 1/2)); P_n and its
+    // derivative come from the three-term recurrence.
+    const int n = kGaussNodes;
+    for (int i = 0; i < n; ++i) {
+      double r = std::cos(M_PI * (i + 0.75) / (n + 0.5)), dp = 1.0;
+      for (int it = 0; it < 100; ++it) {
+        double p_prev = 1.0, p = r;
+        for (int k = 2; k <= n; ++k) {
+          const double p_next = ((2.0 * k - 1.0) * r * p - (k - 1.0) * p_prev) / k;
+          p_prev = p;
+          p = p_next;
+        }
+        dp = n * (r * p - p_prev) / (r * r - 1.0);
+        const double step = p / dp;
+        r -= step;
+        if (std::fabs(step) < 1e-17) break;
+      }
+      x[i] = r;
+      w[i] = 2.0 / ((1.0 - r * r) * dp * dp);
+    }
   }
-  return h;
+};
+
+const GaussLegendre &gauss_legendre() {
+  static const GaussLegendre g;
+  return g;
 }
 
-// Lloyd-Max on the positive half-line (the law is symmetric, t_{L/2} = 0).
-// For a cell [lo, hi] with 0 <= lo < hi <= 1 and a = (d-1)/2, writing
-// w(u) = (1-u^2)^a and x(u) = (1-u)/2:
-//   integral of u (1-u^2)^((d-3)/2) du    = (w(lo) - w(hi)) / (2a)
-//   integral of   (1-u^2)^((d-3)/2) du    = (w(lo) h(x(lo)) - w(hi) h(x(hi))) / (2a)
-// where h(x) is the continued fraction of the incomplete beta function,
-// B_x(a, a) = x^a (1-x)^a h(x) / a.  The normalising constant of the density
-// cancels in the conditional mean, so no Gamma function is evaluated:
-//   c = (w(lo) - w(hi)) / (w(lo) h(x(lo)) - w(hi) h(x(hi))).
-double pow_term(int d, double u) {
-  if (std::fabs(u) >= 1.0) return 0.0;
-  return std::exp(0.5 * (d - 1) * std::log1p(-u * u));
+// log of (1-u^2)^(1/2) = log cos(asin u), accurate for small u
+double log_cos_of(double u) { return 0.5 * std::log1p(-u * u); }
+
+// Mass of the cell [lo, hi] (0 <= lo < hi <= 1) divided by the density's
+// value at lo, i.e. integral of exp((d-2) (log cos th - log cos th_lo)).
+double cell_mass_rel(int d, double lo, double hi) {
+  const double e = d - 2.0;
+  const double th0 = std::asin(lo);
+  double th1 = std::asin(hi);
+  if (e > 0.0) {
+    // beyond cos(th) = cos(th0) exp(-60/e) the integrand is below e^-60 of
+    // its value at th0 and adds nothing at fp64 resolution
+    const double c_cut = std::sqrt(1.0 - lo * lo) * std::exp(-60.0 / e);
+    th1 = std::fmin(th1, std::acos(c_cut));
+  }
+  const double lc0 = log_cos_of(lo);
+  // panels no wider than half the angular scale of the integrand
+  const double scale = 1.0 / std::sqrt(e + 1.0 + e * std::tan(th0) * std::tan(th0) * e);
+  const int panels = std::max(1, (int)std::ceil((th1 - th0) / (0.5 * scale)));
+  const double h = (th1 - th0) / panels;
+  const GaussLegendre &g = gauss_legendre();
+  double total = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double mid = th0 + (p + 0.5) * h;
+    double part = 0.0;
+    for (int i = 0; i < kGaussNodes; ++i) {
+      const double th = mid + 0.5 * h * g.x[i];
+      part += g.w[i] * std::exp(e * (log_cos_of(std::sin(th)) - lc0));
+    }
+    total += 0.5 * h * part;
+  }
+  return total;
 }
 
-double cell_mean(int d, double lo, double hi) {
-  const double a = 0.5 * (d - 1);
-  const double wl = pow_term(d, lo), wh = pow_term(d, hi);
-  const double hl = beta_cf(a, a, 0.5 * (1.0 - lo));
-  const double hh = wh > 0.0 ? beta_cf(a, a, 0.5 * (1.0 - hi)) : 0.0;
-  return (wl - wh) / (wl * hl - wh * hh);
+// First moment of the cell divided by the density's value at lo (closed form).
+double cell_moment_rel(int d, double lo, double hi) {
+  const double lc0 = log_cos_of(lo);
+  const double top = std::exp(lc0);  // (1-lo^2)^((d-1)/2) / (1-lo^2)^((d-2)/2)
+  const double bot = hi >= 1.0 ? 0.0 : std::exp((d - 1.0) * log_cos_of(hi) - (d - 2.0) * lc0);
+  return (top - bot) / (d - 1.0);
 }
+
+double cell_mean(int d, double lo, double hi) { return cell_moment_rel(d, lo, hi) / cell_mass_rel(d, lo, hi); }
 
 int lloyd_max(int d, int bits, double *c, double *t) {
   const int L = 1 << bits, H = L / 2;
