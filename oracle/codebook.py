@@ -21,12 +21,15 @@ i.e. (u+1)/2 ~ Beta((d-1)/2, (d-1)/2).  Its limit for large d is N(0, 1/d).
 """
 from __future__ import annotations
 
+import functools
+
 import mpmath
 import numpy as np
 from scipy.special import betainc, ndtri
 from scipy.stats import norm as _norm
 
 
+@functools.lru_cache(maxsize=None)
 def _log_norm_const(d: int) -> float:
     """log of Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)), the density's normalising constant.
 

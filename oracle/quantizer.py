@@ -75,7 +75,10 @@ def _indices(y, n, bounds):
     t = _as64(bounds)
     nn = np.where(n > 0, n, 1.0)
     yy = np.where(n[:, None] > 0, y, 0.0)
-    return np.sum(t[None, None, :] * nn[:, None, None] < yy[:, :, None], axis=2).astype(np.int64)
+    idx = np.zeros(yy.shape, dtype=np.int64)
+    for tk in t:  # one comparison per boundary, counted
+        idx += (tk * nn)[:, None] < yy
+    return idx
 
 
 def encode_mse(x, pi, centroids, bounds):

@@ -15,8 +15,8 @@ L2-normalised vectors of dimension 1536, TurboQuant_prod 4-bit, 1000 queries,
 top-10.  Checked on samples the oracle can compute: the codes of sampled rows;
 for sampled queries, the returned rows re-scored by the oracle from its own
 encoding of those rows (values within the score gate, in descending order);
-and no row of a random 20000-row sample, scored by the oracle, beats the
-returned tenth score by more than the gate.  recall@10 against the fp64 exact
+and no other row of the whole database, encoded and scored by the oracle,
+beats the returned tenth score by more than the gate.  recall@10 against the fp64 exact
 top-10 is printed; it has no value on the pages to be checked against (parity
 unpinned).
 """
@@ -81,6 +81,7 @@ def test_heterogeneous_layer_full_size(kind):
     print(f"{kind} layer (d={d}, T={T}): max rel err over sampled slices {worst:.2e}")
 
 
+@pytest.mark.timeout(900)
 def test_search_full_size_sampled():
     from vector_quantization_rotation_amd import api, synth, workloads
     S = workloads.SEARCH
@@ -123,11 +124,25 @@ def test_search_full_size_sampled():
         assert np.all(np.diff(vals[qi]) <= 0), qi
         ref = np.array([est_c[i, pos[int(r)]] for r in idx[qi]])
         assert np.all(np.abs(vals[qi] - ref) <= tol[i]), (qi, vals[qi] - ref)
-    # completeness on a random sample of rows: none beats the tenth returned score by more than the gate
-    sample = np.sort(rng.choice(n, size=20000, replace=False))
-    est_s, _ = oracle_scores(qs, sample)
+    # completeness over the whole database: the oracle encodes every row (64K rows at a time) and no row
+    # outside the returned ten beats the tenth returned score by more than the gate.  The estimate is
+    # taken in its rotated form, n_hat <Pi q, c[idx]> + sqrt(pi/2)/d gamma <S q, 2 bits - 1>, equal to
+    # <q, decode(x)> to 1e-12 relative
+    qpi = Q[qs].astype(np.float64) @ pi.astype(np.float64).T
+    qs_ = Q[qs].astype(np.float64) @ s.astype(np.float64).T
+    best_out = np.full(len(qs), -np.inf)
+    cb, tb = oracle.lloyd_max(d, bits - 1)
+    for r0 in range(0, n, 65536):
+        xr = X[r0:r0 + 65536].cpu().numpy()
+        eidx, enh, esb, egam = oracle.encode_prod(xr, pi, s, cb, tb)
+        est = (enh.astype(np.float64)[:, None] * (cb[eidx] @ qpi.T)
+               + oracle.qjl_scale(d) * egam.astype(np.float64)[:, None] * ((2.0 * esb - 1.0) @ qs_.T)).T
+        for i, qi in enumerate(qs):
+            mine = (idx[qi] >= r0) & (idx[qi] < r0 + est.shape[1])
+            est[i, idx[qi][mine] - r0] = -np.inf
+        best_out = np.maximum(best_out, est.max(axis=1))
     for i, qi in enumerate(qs):
-        assert np.all(est_s[i] <= vals[qi, -1] + 2 * tol[i]), qi
+        assert best_out[i] <= vals[qi, -1] + 2 * tol[i], (qi, best_out[i], vals[qi, -1])
 
     # recall@10 against the exact fp64 top-10 over all rows (reported, parity unpinned)
     exact = np.full((len(qs), n), -np.inf)

@@ -303,8 +303,8 @@ def test_attn_peaked_softmax_long_tail(api, T, layout):
     """One dominant token and a tail of T - 1 tokens with equal keys whose softmax weight relative to
     the maximum is 3e-8, below the integer weight grid of the token-tiled kernels: the chunk holding
     the dominant token rounds its tail weights to zero, the other chunks keep them (each chunk has its
-    own maximum).  Held to 2e-4, ten times inside the gate.  (The long-chunk case, where dropped
-    weights could bias the value sums, is held to the same bound in the full-size attention test.)"""
+    own maximum).  Held to 2e-4, ten times inside the gate.  (The whole-sequence chunk, where the tail
+    behind the dominant token is long, is test_attn_whole_sequence_chunk_tail_with_common_offset.)"""
     d, Hq, Hkv = 128, 4, 1
     rng = np.random.default_rng(77)
     xa, xb = rng.standard_normal((2, d)).astype(np.float32)
@@ -339,6 +339,70 @@ def test_attn_peaked_softmax_long_tail(api, T, layout):
     err = parity.rel_rows(out[0], ref[0])
     print(f"peaked softmax T={T} layout={layout}: max rel err {err.max():.2e}")
     assert np.all(err <= 2e-4), err
+
+
+def _broadcast_sequence(t, nseq):
+    """One sequence's cache array [T, ...] repeated for nseq sequences on the device: [nseq, T, ...]."""
+    return t.unsqueeze(0).expand(nseq, *t.shape).contiguous()
+
+
+@pytest.mark.parametrize("kind,vbits", [("sink", 2), ("spiky", 2), ("sink", 3)])
+def test_attn_whole_sequence_chunk_tail_with_common_offset(api, kind, vbits):
+    """A plan with as many (batch, kv-head) units as resident work-group slots, so that one work-group
+    streams the whole sequence, over values that share a common offset (V = mu + N(0, 1)), held to
+    2e-4.  'sink': one dominant key and 32767 equal keys whose softmax weight is 2^-20 of it, so
+    that the tail carries about 3 % of the mass on the coarse end of the integer weight grid (a
+    weight grid fixed to the dominant token would bias the output along mu by about 4e-3).
+    'spiky': distinct random keys and a query scaled so that scores spread over about 6 log2 units.
+    2-bit values take the wave-streaming kernel (2048 units), 3-bit values the 4-wave kernel (512
+    units).  Every unit holds the same sequence, so the oracle attends one of them."""
+    d, T, G = 128, 32768, 4
+    Hkv = 128
+    B = 16 if vbits == 2 else 4
+    Hq = G * Hkv
+    rng = np.random.default_rng(90)
+    mu = 2.0 * rng.standard_normal(d)
+    V = synth.round_bf16((mu[None] + rng.standard_normal((T, d))).astype(np.float32))
+    if kind == "sink":
+        xa, xb = rng.standard_normal((2, d)).astype(np.float32)
+        K = np.repeat(xb[None], T, axis=0)
+        K[7] = xa
+    else:
+        K = rng.standard_normal((T, d)).astype(np.float32)
+    K = synth.round_bf16(K)
+    piK, piV, sV = synth.haar_rotation(d, 91), synth.haar_rotation(d, 92), synth.gaussian_projection(d, 93)
+    ke = parity.oracle_mse(K, piK, 3)
+    ve = parity.oracle_prod(V, piV, sV, vbits)
+    Kt = oracle.decode_mse(ke["idx"], ke["n_hat"], piK, ke["c"])
+    Vt = oracle.decode_prod(ve["idx"], ve["n_hat"], ve["signs"], ve["gamma"], piV, sV, ve["c"])
+    if kind == "sink":
+        diff = Kt[7] - Kt[0]
+        lam = 20.0 * math.log(2.0) * math.sqrt(d) / float(diff @ diff)
+        qg = np.stack([lam * diff + 0.01 * h * rng.standard_normal(d) for h in range(G)])
+    else:
+        qg = rng.standard_normal((G, d))
+        qg *= 6.0 * math.log(2.0) * math.sqrt(d) / np.std(Kt @ qg.T, axis=0)[:, None]
+    qg = synth.round_bf16(qg.astype(np.float32))
+    ref = oracle.decode_attention(qg[None], Kt.reshape(1, 1, T, d), Vt.reshape(1, 1, T, d), np.array([T]),
+                                  1.0 / math.sqrt(d))[0]
+    nseq = B * Hkv
+    kq = api.Quantizer(d, 3, api.TQ_MSE, piK)
+    vq = api.Quantizer(d, vbits, api.TQ_PROD, piV, sV)
+    kc = _broadcast_sequence(_dev(ke["record"]), nseq).view(B, Hkv, T, -1)
+    kn = _broadcast_sequence(_dev(parity.f16_bits(ke["n_hat"])), nseq).view(B, Hkv, T)
+    vt = _broadcast_sequence(_dev(oracle.tile_records(ve["record"], d, vbits).view(np.int32)), nseq)
+    vt = vt.view(B, Hkv, -1, vbits, d)
+    vn = _broadcast_sequence(_dev(parity.f16_bits(ve["n_hat"])), nseq).view(B, Hkv, T)
+    vg = _broadcast_sequence(_dev(parity.f16_bits(ve["gamma"])), nseq).view(B, Hkv, T)
+    q = _dev(np.broadcast_to(qg[None, None], (B, Hkv, G, d)).reshape(B, Hq, d)).to(torch.bfloat16)
+    seq = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    print(f"whole-sequence chunk: kind={kind} value bits={vbits} B={B} Hkv={Hkv} T={T}", flush=True)
+    out = api.attn_decode(kq, vq, q, kc, kn, vt, vn, vg, seq, 1.0 / math.sqrt(d), vlayout=api.TQ_LAYOUT_TILE32)
+    out = out.cpu().numpy().reshape(B * Hkv, G, d)
+    del kc, kn, vt, vn, vg
+    err = parity.rel_rows(out, np.broadcast_to(ref[None], out.shape))
+    print(f"whole-sequence chunk: kind={kind} value bits={vbits}: max rel err {err.max():.2e}")
+    assert np.all(err <= 2e-4), err.max()
 
 
 def test_tile_records_matches_oracle(api):

@@ -188,7 +188,7 @@ def test_record_sizes_reproduce_printed_ratios():
     assert 16 / 2 == figs["values_2bit_ratio"]["value"]
 
 
-def test_margins_helpers():
+def test_margins_helpers_shapes():
     d = 64
     c, t = oracle.lloyd_max(d, 2)
     pi = synth.haar_rotation(d, 1)
@@ -199,6 +199,61 @@ def test_margins_helpers():
     assert sm.shape == (16, d) and np.all(sm >= 0)
     mm = oracle.fp16_midpoint_margin(np.array([1.0 + 2.0 ** -11, 1.0]))
     assert mm[0] == 0.0 and mm[1] == pytest.approx(2.0 ** -11)
+
+
+# Hand-computable margins.  The tie zone is |y_j - t_k n| <= 1e-5 sigma with sigma = n/sqrt(d)
+# for codes and |(S r)_i| <= 1e-5 ||r|| for signs (the reading of "within 1e-5 (relative) of a
+# decision boundary or zero"), so the margins are those distances in those units.
+_PERM = np.array([[0, 1, 0, 0], [0, 0, 1, 0], [1, 0, 0, 0], [0, 0, 0, 1]], dtype=np.float64)  # y = (x1, x2, x0, x3)
+
+
+def test_code_margins_hand_example():
+    # d = 4, x = (3, 4, 0, 0): ||x|| = 5, sigma = 5 / sqrt(4) = 2.5; bounds (-0.5, 0, 0.5) scale to (-2.5, 0, 2.5)
+    x = np.array([[3.0, 4.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]])
+    t = np.array([-0.5, 0.0, 0.5])
+    m = oracle.code_margins(x, np.eye(4), t)
+    assert np.allclose(m[0], [0.5 / 2.5, 1.5 / 2.5, 0.0, 0.0], rtol=1e-15, atol=0)
+    assert np.all(np.isinf(m[1]))  # zero vector: no decision is near a boundary
+    # y = Pi x, not Pi^T x: the 3-cycle permutation moves the margins to (x1, x2, x0, x3)
+    mp = oracle.code_margins(x[:1], _PERM, t)
+    assert np.allclose(mp[0], [1.5 / 2.5, 0.0, 0.5 / 2.5, 0.0], rtol=1e-15, atol=0)
+    # a coordinate a small delta above t_k n has margin delta / sigma
+    delta = 1e-6
+    xb = np.array([[2.5 + delta, 0.0, 0.0, 0.0]])
+    xb[0, 1] = math.sqrt(25.0 - xb[0, 0] ** 2)  # keep ||x|| at 5 to fp64 precision
+    n = math.sqrt(np.sum(xb[0] ** 2))
+    mb = oracle.code_margins(xb, np.eye(4), t)
+    assert mb[0, 0] == pytest.approx(abs(xb[0, 0] - 0.5 * n) / (n / 2), rel=1e-6)
+    assert mb[0, 0] == pytest.approx(delta / 2.5, rel=1e-6)
+
+
+def test_sign_margins_hand_example():
+    # Pi = I, hand codebook c = (-0.25, 0.25), t = (0,): x = (3, 4, 0, 0), n_hat = 5,
+    # idx = (1, 1, 0, 0) (0 goes to the lower cell), decode = (1.25, 1.25, -1.25, -1.25),
+    # r = (1.75, 2.75, 1.25, 1.25), ||r||^2 = 13.75
+    x = np.array([[3.0, 4.0, 0.0, 0.0]])
+    c, t = np.array([-0.25, 0.25]), np.array([0.0])
+    rn = math.sqrt(13.75)
+    m = oracle.sign_margins(x, np.eye(4), np.eye(4), c, t)
+    assert np.allclose(m[0], np.array([1.75, 2.75, 1.25, 1.25]) / rn, rtol=1e-15, atol=0)
+    # hand S: S r = (1.75 + 2.75, 2.75 - 1.25, 2 * 1.75 + 1.25, 3 * 1.25) = (4.5, 1.5, 4.75, 3.75)
+    S = np.array([[1, 1, 0, 0], [0, 1, -1, 0], [2, 0, 0, 1], [0, 0, 0, 3]], dtype=np.float64)
+    m = oracle.sign_margins(x, np.eye(4), S, c, t)
+    assert np.allclose(m[0], np.array([4.5, 1.5, 4.75, 3.75]) / rn, rtol=1e-15, atol=0)
+    # the transposed S would give different margins
+    assert not np.allclose(m[0], np.abs(np.array([1.75, 2.75, 1.25, 1.25]) @ S) / rn)
+    # x rebuilt exactly by Algorithm 1 (c = (-0.5, 0.5), x = (1, 1, 1, 1), n_hat = 2): r = 0 -> inf
+    z = oracle.sign_margins(np.ones((1, 4)), np.eye(4), S, np.array([-0.5, 0.5]), t)
+    assert np.all(np.isinf(z))
+
+
+def test_inner_product_estimate_hand_example():
+    # est[a, i] = <q_a, x~_i>: 2 queries x 3 rows at d = 3
+    q = np.array([[1.0, 0.0, -1.0], [0.0, 2.0, 1.0]])
+    xt = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0], [-1.0, 0.5, 0.0]])
+    est = oracle.inner_product_estimate(q, xt)
+    assert est.shape == (2, 3)
+    assert np.array_equal(est, np.array([[-2.0, -2.0, -1.0], [7.0, 16.0, 1.0]]))
 
 
 def test_tile_layout_hand_example():

@@ -25,9 +25,43 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
 
 
+_HALF_BITS = (torch.int16, torch.float16, torch.uint16)  # fp16 bit patterns (norms, gammas)
+
+
 def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _need(t, name: str, dtypes, shape=None, device=None, contiguous: bool = True):
+    """Check a tensor handed to the C ABI: on the device, dtype, shape, dense layout.
+
+    The library receives raw pointers and cannot check any of this itself, so a
+    wrong tensor would become an out-of-bounds device access; raise instead.
+    """
+    _dev(t, name)
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _need_rows(t, name: str, dtypes, n: int, width: int, device):
+    """[n, >= width] rows with unit stride along a row (row stride may exceed width)."""
+    _need(t, name, dtypes, device=device, contiguous=False)
+    if t.dim() != 2 or t.shape[0] != n or t.shape[1] < width or (n > 0 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected [{n}, >= {width}] with unit column stride, got shape "
+                         f"{tuple(t.shape)} stride {t.stride()}")
     return t
 
 
@@ -71,9 +105,11 @@ class Quantizer:
 
         Returns (codes uint8 [n, code_bytes], norms int16-bits [n], gammas or None).
         """
-        _dev(x, "x")
+        _need(x, "x", tuple(_DT), contiguous=False)
+        if x.shape[-1] != self.d:
+            raise ValueError(f"x: last dimension {x.shape[-1]} != d = {self.d}")
         x2 = x.reshape(-1, x.shape[-1])
-        if x2.stride(-1) != 1:
+        if x2.stride(-1) != 1 or (x2.shape[0] > 1 and (x2.stride(0) * x2.element_size()) % 16 != 0):
             x2 = x2.contiguous()
         n = x2.shape[0]
         dev = x.device
@@ -81,6 +117,8 @@ class Quantizer:
             codes = torch.empty((n, self.code_bytes), dtype=torch.uint8, device=dev)
         if norms is None:
             norms = torch.empty((n,), dtype=torch.int16, device=dev)
+        _need(codes, "codes", torch.uint8, (n, self.code_bytes), dev)
+        _need(norms, "norms", _HALF_BITS, (n,), dev)
         lib = load()
         if self.mode == TQ_MSE:
             rc = lib.tq_encode_mse(self._h, _ptr(x2), _DT[x2.dtype], n, x2.stride(0), _ptr(codes), _ptr(norms), _stream())
@@ -88,15 +126,25 @@ class Quantizer:
             return codes, norms, None
         if gammas is None:
             gammas = torch.empty((n,), dtype=torch.int16, device=dev)
+        _need(gammas, "gammas", _HALF_BITS, (n,), dev)
         rc = lib.tq_encode_prod(self._h, _ptr(x2), _DT[x2.dtype], n, x2.stride(0), _ptr(codes), _ptr(norms),
                                 _ptr(gammas), _stream())
         _lib._check("tq_encode_prod", rc)
         return codes, norms, gammas
 
     def decode(self, codes: torch.Tensor, norms: torch.Tensor, gammas: torch.Tensor | None = None, out=None):
-        n = codes.shape[0]
+        """Records [n, code_bytes] (+ fp16-bit norms, gammas [n]) -> fp32 rows [n, d]."""
+        _dev(codes, "codes")
+        n, dev = codes.shape[0], codes.device
+        _need(codes, "codes", torch.uint8, (n, self.code_bytes), dev)
+        _need(norms, "norms", _HALF_BITS, (n,), dev)
+        if self.mode == TQ_PROD:
+            if gammas is None:
+                raise ValueError("gammas are required for an Algorithm 2 quantizer")
+            _need(gammas, "gammas", _HALF_BITS, (n,), dev)
         if out is None:
-            out = torch.empty((n, self.d), dtype=torch.float32, device=codes.device)
+            out = torch.empty((n, self.d), dtype=torch.float32, device=dev)
+        _need_rows(out, "out", torch.float32, n, self.d, dev)
         rc = load().tq_decode(self._h, _ptr(codes), _ptr(norms), _ptr(gammas), n, _ptr(out), out.stride(0), _stream())
         _lib._check("tq_decode", rc)
         return out
@@ -104,7 +152,16 @@ class Quantizer:
     def score(self, queries: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, gammas=None, k: int = 0):
         """k == 0: [m, n] scores; k > 0: (values [m, k], indices [m, k]) of the best records per query."""
         lib = load()
-        m, n = queries.shape[0], codes.shape[0]
+        _dev(queries, "queries")
+        _dev(codes, "codes")
+        m, n, dev = queries.shape[0], codes.shape[0], queries.device
+        _need_rows(queries, "queries", torch.float32, m, self.d, dev)
+        _need(codes, "codes", torch.uint8, (n, self.code_bytes), dev)
+        _need(norms, "norms", _HALF_BITS, (n,), dev)
+        if self.mode == TQ_PROD:
+            if gammas is None:
+                raise ValueError("gammas are required for an Algorithm 2 quantizer")
+            _need(gammas, "gammas", _HALF_BITS, (n,), dev)
         ws_b = lib.tq_score_ws_bytes(self._h, m, n, k)
         ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=queries.device)
         if k == 0:
@@ -121,10 +178,15 @@ class Quantizer:
 
 def tile_records(q: Quantizer, codes: torch.Tensor, out=None):
     """Row-layout records [nseq, T, code_bytes] -> TQ_LAYOUT_TILE32 words [nseq, ceil(T/32), planes, d] (int32)."""
+    _dev(codes, "codes")
+    if codes.dim() != 3:
+        raise ValueError("codes must be [nseq, T, code_bytes]")
     nseq, T = codes.shape[0], codes.shape[1]
+    _need(codes, "codes", torch.uint8, (nseq, T, q.code_bytes))
     ntile = (T + 31) // 32
     if out is None:
         out = torch.empty((nseq, ntile, q.planes, q.d), dtype=torch.int32, device=codes.device)
+    _need(out, "out", (torch.int32, torch.uint32), (nseq, ntile, q.planes, q.d), codes.device)
     rc = load().tq_tile_records(q.handle, _ptr(codes), nseq, T, _ptr(out), _stream())
     _lib._check("tq_tile_records", rc)
     return out
@@ -134,17 +196,46 @@ def attn_decode_ws_bytes(kq: Quantizer, B: int, Hq: int, Hkv: int, Tstride: int,
     return load().tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
 
 
+def _attn_args(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout):
+    """Check every tensor of a decode-attention call against the shapes the C ABI assumes."""
+    _dev(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    dev = q.device
+    if d != kq.d or d != vq.d:
+        raise ValueError(f"q: head dim {d} does not match the quantizers (d = {kq.d}, {vq.d})")
+    _need(q, "q", tuple(_DT), device=dev)
+    _dev(kcodes, "kcodes")
+    if kcodes.dim() != 4:
+        raise ValueError("kcodes must be [B, Hkv, Tstride, code_bytes]")
+    Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
+    _need(kcodes, "kcodes", torch.uint8, (B, Hkv, Tstride, kq.code_bytes), dev)
+    for t, nm in ((knorms, "knorms"), (vnorms, "vnorms"), (vgammas, "vgammas")):
+        _need(t, nm, _HALF_BITS, (B, Hkv, Tstride), dev)
+    if vlayout == TQ_LAYOUT_TILE32:
+        _need(vcodes, "vcodes", (torch.int32, torch.uint32), (B, Hkv, (Tstride + 31) // 32, vq.planes, d), dev)
+    elif vlayout == TQ_LAYOUT_ROWS:
+        _need(vcodes, "vcodes", torch.uint8, (B, Hkv, Tstride, vq.code_bytes), dev)
+    else:
+        raise ValueError(f"unknown value layout {vlayout}")
+    _need(seq_len, "seq_len", torch.int32, (B,), dev)
+    if out is not None:
+        _need(out, "out", torch.float32, (B, Hq, d), dev)
+    return B, Hq, Hkv, Tstride, d, dev
+
+
 def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
                 seq_len: torch.Tensor, scale: float, out=None, ws=None, vlayout: int = TQ_LAYOUT_ROWS):
     """q [B, Hq, d]; key caches [B, Hkv, Tstride, ...]; value records in `vlayout`; -> out [B, Hq, d] fp32."""
     lib = load()
-    B, Hq, d = q.shape
-    Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout)
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     ws_b = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
     if ws is None:
-        ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=q.device)
+        ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", torch.uint8, device=dev)
     rc = lib.tq_attn_decode(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms),
                             _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), float(scale),
                             _ptr(out), _ptr(ws), ws.numel(), _stream())
@@ -155,18 +246,27 @@ def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, v
 def attn_decode_bound(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
                       seq_len: torch.Tensor, scale: float, out: torch.Tensor, ws: torch.Tensor,
                       vlayout: int = TQ_LAYOUT_ROWS):
-    """attn_decode with every argument marshalled once: returns a no-argument callable that
-    enqueues the same call on the current stream (for tight decode loops)."""
+    """attn_decode with every argument checked and marshalled once: returns a no-argument
+    callable that enqueues the same call on the stream that is current when it is called
+    (for tight decode loops).  The callable holds references to every tensor it reads or
+    writes, so they stay alive as long as it does."""
     lib = load()
-    B, Hq, d = q.shape
-    Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout)
+    if out is None:
+        raise ValueError("out is required")
+    _need(ws, "ws", torch.uint8, device=dev)
+    need = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
+    if ws.numel() < need:
+        raise ValueError(f"ws holds {ws.numel()} bytes, the call needs {need}")
+    keep = (kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, ws)
     args = (kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms), _ptr(vcodes),
             _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), C.c_float(scale), _ptr(out), _ptr(ws),
-            C.c_size_t(ws.numel()), _stream())
+            C.c_size_t(ws.numel()))
     fn = lib.tq_attn_decode
 
     def call():
-        rc = fn(*args)
+        rc = fn(*args, _stream())
         if rc != 0:
             _lib._check("tq_attn_decode", rc)
+    call.tensors = keep
     return call

@@ -156,9 +156,28 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
   }
 }
 
+// The integer weight grid has a fixed step relative to the softmax reference, so a token far below
+// the reference carries few significant bits.  When every score of a head in a whole step lies more
+// than REF_DROP below the reference and the current fold segment is at least the kernel's minimum
+// length, the reference moves down to that step's maximum (a fold), so that a long tail behind one
+// dominant token is weighed on a grid set by its own scale.  The reference never goes more than
+// REF_SPAN below the highest score of the chunk, m_top (tokens further down weigh below 2^-REF_SPAN of
+// that token): every weight is then at most 2^(REF_SPAN + slack) and a running sum over fewer than
+// 2^31 tokens stays below 2^80 (fp32 has room to 2^128).
+constexpr float REF_DROP = 8.f;
+constexpr float REF_SPAN = 48.f;
+// reference after a fold for one head: up to the step maximum smax when it exceeds the reference,
+// down to it (no lower than m_top - REF_SPAN) when it lies more than REF_DROP below, else unchanged
+__device__ __forceinline__ float moved_reference(float m_ref, float smax, float m_top, bool allow_down) {
+  float m_new = fmaxf(m_ref, smax);
+  if (allow_down && smax < m_ref - REF_DROP) m_new = fminf(m_ref, fmaxf(smax, m_top - REF_SPAN));
+  return m_new;
+}
+
 constexpr float FA_SLACK = 1.f;     // score headroom above the reference maximum (log2 units)
 constexpr float FA_NCAP = 1.25f;   // norm and gamma caps: this times the largest seen
 constexpr float FA_HEADROOM = 2.f;  // 2^FA_SLACK
+constexpr int FA_MINSEG = 2;        // fold segment length (256-token steps) before a downward move
 
 // D: head dim; KB: key index bits; VB: value index bits (Algorithm-2 records hold VB+1 planes)
 //
@@ -190,7 +209,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   __shared__ float s_kn[4][64];                                        // per wave: n_K
   __shared__ float s_max[4][FA_GMAX + 2];                              // per wave: score max per head, n_V max, gamma max
   __shared__ float s_merge[4][FA_GMAX][3];                             // per wave and head: l, Ym, Yq
-  __shared__ int s_flag[4];                                            // per wave: a step value above the reference
+  __shared__ int s_flag[4];  // per wave: bit 0 a step value above the reference, bit 1 + h head h within REF_DROP
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, split = blockIdx.y;
@@ -236,6 +255,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   const int vo_v = ((hl >> 1) * VPL * D + wave * (NTW * 16) + ln) * 4;
 
   float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f;  // work-group uniform (m_ref per lane head)
+  float m_top = -INFINITY;                              // highest score of the chunk so far (per head)
+  int since_fold = 0;
   float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;        // this lane's tokens, head hl
   float accf[VMP + 1][NTW];
   intx4 vacc[VMP + 1][NTW];
@@ -317,18 +338,29 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(sn * 2));
     }
     bool over = fvn > vn_ref || fvg > vg_ref;
+    bool near = false;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int tw = tbase + 8 * grp;
       const bool ok = head_ok && (wbase + tw) < c1;
       sc[grp] = ok ? (sc[grp] * qinv - qconst) * s_kn[wave][tw] * a.scale_log2 : -INFINITY;
       over = over || sc[grp] > m_ref + FA_SLACK;
+      near = near || sc[grp] >= m_ref - REF_DROP;
     }
     const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0ull;  // every lane votes
-    if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
+    const uint64_t wave_near = __builtin_amdgcn_ballot_w64(near);
+    int flag = wave_over ? 1 : 0;
+#pragma unroll
+    for (int h = 0; h < FA_GMAX; ++h) flag |= ((wave_near >> (16 * h)) & 0xFFFFull) != 0 ? 2 << h : 0;
+    if (lane == 0) s_flag[wave] = flag;
     __syncthreads();  // B1: flags visible; previous step's value pass done everywhere
-    const int any_over = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-    if (any_over) {
+    const int flags = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+    // a whole step (every token valid) in which some present head has no score within REF_DROP of the
+    // reference, once the fold segment is FA_MINSEG steps long: move that reference down
+    const bool whole = s0 + FA_SUB <= c1;
+    ++since_fold;
+    const bool low = whole && since_fold >= FA_MINSEG && ((flags >> 1) & ((1 << gw) - 1)) != ((1 << gw) - 1);
+    if ((flags & 1) || low) {
       // ---- rare: move the reference to this step's maxima and fold the int32 accumulators ----
       float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       smax = rows16_max(smax);
@@ -343,7 +375,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
         step_vn = fmaxf(step_vn, s_max[wv][FA_GMAX]);
         step_vg = fmaxf(step_vg, s_max[wv][FA_GMAX + 1]);
       }
-      const float m_new = fmaxf(m_ref, step_m);
+      m_top = fmaxf(m_top, step_m);
+      const float m_new = moved_reference(m_ref, step_m, m_top, whole);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
 #pragma unroll
@@ -363,6 +396,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       m_ref = m_new;
       vn_ref = fmaxf(vn_ref, FA_NCAP * step_vn);
       vg_ref = fmaxf(vg_ref, FA_NCAP * step_vg);
+      since_fold = 0;
     }
     // ---- weights: p = 2^(s - m_ref) <= 2^FA_SLACK; p n and p gamma as four 7-bit digits, one dword per digit row ----
     {
@@ -504,6 +538,7 @@ constexpr float WV_HEADROOM = 2.f;        // 2^WV_SLACK
 constexpr int WV_RING = 3;                // ring slots: stages s+1 and s+2 are in flight while s is used
 constexpr float WV_WMAX = 8388352.f;      // 2^23 - 256: weights are integers below 2^23 (see wv_weight)
 constexpr float WV_MAGIC = 8388608.f;     // 2^23
+constexpr int WV_MINSEG = 8;              // fold segment length (steps) before a downward move
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -651,6 +686,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int voff_n = lane < 32 ? lane * 4 : 0x7FFFFF00;  // past every buffer's end for lanes 32..63
 
   float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f;
+  float m_top = -INFINITY;  // highest score of the chunk so far (per head)
   float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;
   float accf[2][NTC];
   intx4 vacc[2][NTC];
@@ -753,9 +789,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       mg = fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3]));
     }
     const float dmax = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
-    const uint64_t over = __builtin_amdgcn_ballot_w64(dmax > WV_SLACK) | __builtin_amdgcn_ballot_w64(mn > vn_ref) |
-                          __builtin_amdgcn_ballot_w64(mg > vg_ref);
+    uint64_t over = __builtin_amdgcn_ballot_w64(dmax > WV_SLACK) | __builtin_amdgcn_ballot_w64(mn > vn_ref) |
+                    __builtin_amdgcn_ballot_w64(mg > vg_ref);
     ++since_fold;
+    if constexpr (WHOLE) {
+      if (since_fold >= WV_MINSEG) {
+        // a head (16 lanes) none of whose tokens comes within REF_DROP of the reference
+        const uint64_t near = __builtin_amdgcn_ballot_w64(dmax >= -REF_DROP);
+        if ((near & 0xFFFFull) == 0 || (near & 0xFFFF0000ull) == 0 || (near & 0xFFFF00000000ull) == 0 ||
+            (near >> 48) == 0)
+          over = 1ull;
+      }
+    }
     if (over != 0ull || since_fold >= 16384) {
       // rare: move the reference to this step's maxima and fold the integer accumulators (the scores
       // are formed again from their parts, n_K read again: d holds +inf while the reference is -inf)
@@ -767,7 +812,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       const float smax = rows16_max(fmaxf(fmaxf(sct[0], sct[1]), fmaxf(sct[2], sct[3])));
       const float vnm = wave_max_f32(mn);
       const float vgm = wave_max_f32(mg);
-      const float m_new = fmaxf(m_ref, smax);
+      m_top = fmaxf(m_top, smax);
+      const float m_new = moved_reference(m_ref, smax, m_top, WHOLE);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref * (WV_HEADROOM / WV_WMAX), iq = vg_ref * (WV_HEADROOM / WV_WMAX);
 #pragma unroll
@@ -797,7 +843,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       uint32_t bm[4], bq[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        // p = 2^(s - m_ref) <= 2^WV_SLACK (hardware exp2: results below 2^-126 flush to zero)
+        // p = 2^(s - m_ref) <= 2^WV_SLACK (hardware exp2: results below 2^-126 flush to zero; after a
+        // downward move p may exceed 1 only by the same headroom)
         const float p = __builtin_amdgcn_exp2f(d[grp]);
         l_run += p;
         // (whole steps: the fp16 norms enter the products as they are, in mixed-precision FMAs)
