@@ -88,7 +88,11 @@ int tq_codebook_build(int d, int bits, double *centroids, double *bounds);
 
 /* Create a quantizer for dimension d on the current HIP device.
  *   mode TQ_MSE : 1 <= bits <= 4, s ignored (may be NULL)
- *   mode TQ_PROD: 2 <= bits <= 4, s required
+ *   mode TQ_PROD: 1 <= bits <= 4, s required.  bits = 1 is the pure sign
+ *     (QJL) mode, the 1-bit mode of the AiBoss overview (section
+ *     "TurboQuantの主な機能"): Algorithm 1 at 0 bits keeps only the norm (its one
+ *     centroid is 0), so the residual is x itself and a record is the sign
+ *     plane of S x alone.
  *   d:  multiple of 64, 64 <= d <= 2048
  *   pi: host, d*d floats row-major, the rotation (caller keeps ownership;
  *       it is copied).  The library assumes it is orthogonal to fp32
@@ -120,7 +124,9 @@ int tq_encode_mse(const tq_quantizer *q, const void *x, int xt, int64_t n, int64
 
 /* Algorithm 2 encode of n vectors (q must be TQ_PROD).  As tq_encode_mse with
  * the (b-1)-bit codebook, then r = x - n_hat * Pi^T c[idx], sign plane bit i =
- * [(S r)_i >= 0] and gammas[i] = fp16(||r||).
+ * [(S r)_i >= 0] and gammas[i] = fp16(||r||).  At b = 1 there is no index
+ * plane: r = x, the record is the sign plane of S x, norms and gammas both
+ * hold fp16(||x||).
  *   gammas: device, n fp16 bit patterns */
 int tq_encode_prod(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx,
                    uint8_t *codes, uint16_t *norms, uint16_t *gammas, void *stream);
@@ -154,29 +160,82 @@ int tq_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, i
                     void *stream);
 
 /* Decode attention of one new query token per sequence against a compressed
- * cache: keys through Algorithm 1 (kq, TQ_MSE), values through Algorithm 2
- * (vq, TQ_PROD), as the ai-navigate-news Gemma 4 post assigns them (section
- * "仕組み（技術的）").  For batch b and query head h, with g = h / (Hq/Hkv):
+ * cache: values through Algorithm 2 (vq, TQ_PROD), keys through Algorithm 1
+ * (kq, TQ_MSE), as the ai-navigate-news Gemma 4 post assigns them (section
+ * "仕組み（技術的）"), or through Algorithm 2 as well (kq TQ_PROD, unbiased
+ * scores).  For batch b and query head h, with g = h / (Hq/Hkv):
  *   s_t = scale * <q[b,h], K~[b,g,t]>  for t < seq_len[b]
  *   out[b,h] = sum_t softmax(s)_t V~[b,g,t]      (zero when seq_len[b] == 0)
  * where K~, V~ are the decodes of the records.
  *   q:       device [B, Hq, d] of type qt (TQ_F32, TQ_BF16 or TQ_F16)
  *   kcodes:  device [B, Hkv, Tstride, kcode_bytes], knorms [B, Hkv, Tstride]
+ *   kgammas: device [B, Hkv, Tstride] key residual norms when kq is TQ_PROD;
+ *            ignored (may be NULL) when kq is TQ_MSE
  *   vcodes:  device, value records in layout `vlayout`:
- *            TQ_LAYOUT_ROWS   [B, Hkv, Tstride, vcode_bytes]
- *            TQ_LAYOUT_TILE32 [B, Hkv, ceil(Tstride/32), planes, d] uint32 words
- *            (the fast int8 matrix-core kernel; d in {128, 256}, key bits
- *            with 2^(kbits-1) * d/64 <= 16; other shapes TQ_ERR_UNSUPPORTED)
+ *            TQ_LAYOUT_ROWS   [B, Hkv, Tstride, vcode_bytes]: any d and bit
+ *                             widths (one wave per sequence split)
+ *            TQ_LAYOUT_TILE32 [B, Hkv, ceil(Tstride/32), planes, d] uint32
+ *                             words: the matrix-core kernels, for TQ_MSE keys
+ *                             and values with at least one index bit, at
+ *                             d = 128 (key bits 1-4, value index bits 1-3),
+ *                             d = 256 (key bits 1-3, value index bits 1-3)
+ *                             and d = 512 (key bits 1-3, 1-bit value
+ *                             indices); other cases TQ_ERR_UNSUPPORTED.
+ *                             Head dim 128 with 1-bit value indices, key bits
+ *                             1-3 and Tstride a multiple of 8 (16-byte aligned
+ *                             arrays) takes the wave-streaming kernel.
  *   vnorms, vgammas: device [B, Hkv, Tstride]
  *   seq_len: device [B] int32, 0 <= seq_len[b] <= Tstride
  *   out:     device [B, Hq, d] fp32
  *   ws:      device workspace of at least tq_attn_decode_ws_bytes(...) bytes
  * kq and vq must share d; Hq % Hkv == 0. */
 int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
-                   int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
-                   const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
-                   const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+                   int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                   const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                   int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes,
+                   void *stream);
 size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout);
+
+/* Attention of a chunk of M query tokens per sequence against the compressed cache (prefill in
+ * chunks), causal: query token m of sequence b sits at position q_pos[b] + m and attends the cached
+ * tokens 0 .. q_pos[b] + m, so the chunk's own keys and values must already be in the cache (encode
+ * them first with tq_encode_mse / tq_encode_prod).  Long prompts are where the compression pays
+ * (techblog-plum explainer, section "注意点・未確認事項": contexts of 4K tokens or less gain little).
+ * Keys through Algorithm 1 or 2 (kq), values through Algorithm 2 (vq), scores and outputs as
+ * tq_attn_decode for each query token:
+ *   q:     device [B, M, Hq, d] of type qt;  out: device [B, M, Hq, d] fp32
+ *   q_pos: device [B] int32, q_pos[b] >= 0 and q_pos[b] + M <= Tstride (a query token past Tstride
+ *          attends the Tstride cached tokens)
+ *   cache arguments as tq_attn_decode; vlayout must be TQ_LAYOUT_ROWS (TQ_LAYOUT_TILE32:
+ *          TQ_ERR_UNSUPPORTED)
+ *   ws:    device workspace of at least tq_attn_prefill_ws_bytes(...) bytes */
+int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
+                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                    const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                    int64_t Tstride, const int32_t *q_pos, float scale, float *out, void *ws, size_t ws_bytes,
+                    void *stream);
+size_t tq_attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride, int vlayout);
+
+/* One decode step with the new token appended: for every (b, g) the new key k_new[b,g] and value
+ * v_new[b,g] are encoded (keys by kq's algorithm, values by Algorithm 2, exactly as tq_encode_mse /
+ * tq_encode_prod would) into the cache at position t = seq_len[b], then the step attends as
+ * tq_attn_decode over the t + 1 tokens 0..t, the new one included.  This is the step just before
+ * the cache is read in a decode loop (the past_key_values update of the ai-navigate-news Gemma 4
+ * post, section "セットアップ").  The encode runs inside the step's query preparation, so the step
+ * launches the same kernels as tq_attn_decode.
+ *   k_new, v_new: device [B, Hkv, d] of type xt (TQ_F32, TQ_BF16 or TQ_F16); d <= 512
+ *   kcodes, knorms, kgammas, vcodes, vnorms, vgammas: the cache, as for tq_attn_decode, written at
+ *     position seq_len[b] (row records, or one bit of each token-tiled word for TQ_LAYOUT_TILE32)
+ *   seq_len: device [B] int32, the tokens already cached; read only: the caller advances it (e.g.
+ *     seq_len += 1 on the same stream) before the next step.  A sequence with seq_len[b] >= Tstride
+ *     has no room: nothing is written and its attention covers the Tstride cached tokens.
+ *   ws, ws_bytes: as tq_attn_decode (tq_attn_decode_ws_bytes with the same Tstride)
+ * Returns TQ_ERR_UNSUPPORTED for d > 512, otherwise as tq_attn_decode. */
+int tq_attn_decode_append(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                          int Hkv, const void *k_new, const void *v_new, int xt, uint8_t *kcodes, uint16_t *knorms,
+                          uint16_t *kgammas, uint8_t *vcodes, uint16_t *vnorms, uint16_t *vgammas, int vlayout,
+                          int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /* Optional per-kernel timing.  When enabled, the library records a pair of
  * HIP events on the launch stream around every kernel it launches (a few

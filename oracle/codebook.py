@@ -84,8 +84,13 @@ def lloyd_max(d: int, bits: int, max_iter: int = 20000):
       becomes the conditional mean of its cell; keep the codebook symmetric
       (c[L-1-k] = -c[k]); stop when the update falls to the fp64 floor.
     """
-    if bits < 1:
-        raise ValueError("bits must be >= 1")
+    if bits < 0:
+        raise ValueError("bits must be >= 0")
+    if bits == 0:
+        # one cell, the whole interval: its conditional mean is the mean of the symmetric law.  This
+        # is Algorithm 1 at 0 bits, the first stage of Algorithm 2 at b = 1 (the 1-bit mode of the
+        # AiBoss overview, section "TurboQuantの主な機能": the sign of S x and the norm alone)
+        return np.zeros(1), np.zeros(0)
     L = 1 << bits
     c = ndtri((np.arange(L) + 0.5) / L) / np.sqrt(d)
     for _ in range(max_iter):

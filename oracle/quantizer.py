@@ -201,6 +201,8 @@ def code_margins(x, pi, bounds):
     _, n, y = _norms_and_rotated(x, pi)
     d = y.shape[1]
     t = _as64(bounds)
+    if t.size == 0:  # a one-cell codebook (Algorithm 2 at b = 1) takes no index decision
+        return np.full(y.shape, np.inf)
     dist = np.min(np.abs(y[:, :, None] - t[None, None, :] * n[:, None, None]), axis=2)
     sigma = n / math.sqrt(d)
     with np.errstate(divide="ignore", invalid="ignore"):

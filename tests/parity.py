@@ -26,15 +26,18 @@ def f16_from_bits(t) -> np.ndarray:
     return np.asarray(t, dtype=np.int16).view(np.float16)
 
 
-def check_codes(idx_gpu, idx_ref, margins, what="index"):
-    """Return (mismatches, ties); assert every mismatch is a tie-zone decision."""
+def check_codes(idx_gpu, idx_ref, margins, what="index", max_frac=1e-4):
+    """Return (mismatches, ties); assert every mismatch is a tie-zone decision and, for inputs drawn
+    from the workloads' laws (max_frac not None), that mismatches stay below max_frac of all codes.
+    Inputs built to crowd the tie zone pass max_frac=None."""
     bad = idx_gpu != idx_ref
     ties = margins <= TIE
     n_bad = int(bad.sum())
     assert not np.any(bad & ~ties), (
         f"{what}: {int((bad & ~ties).sum())} mismatches outside the tie zone "
         f"(min margin {float(np.min(margins[bad])):.3g})")
-    assert n_bad <= 1e-4 * idx_ref.size, f"{what}: {n_bad} mismatches of {idx_ref.size}"
+    if max_frac is not None:
+        assert n_bad <= max_frac * idx_ref.size, f"{what}: {n_bad} mismatches of {idx_ref.size}"
     return n_bad, int(ties.sum())
 
 
@@ -103,11 +106,11 @@ def untile(tiles, T, nplanes, d):
     return np.packbits(bits, axis=2, bitorder="little").reshape(T, nplanes * d // 8)
 
 
-def check_prod_signs(sb_gpu, idx_gpu, enc, x, pi, s):
+def check_prod_signs(sb_gpu, idx_gpu, enc, x, pi, s, max_frac=1e-4):
     """Sign bits vs the oracle's, on rows whose index decisions all agree (elsewhere the residual differs)."""
     same = np.all(idx_gpu == enc["idx"], axis=1)
     margins = oracle.sign_margins(x, pi, s, enc["c"], enc["t"])
-    nbad, nties = check_codes(sb_gpu[same], enc["signs"][same], margins[same], "sign")
+    nbad, nties = check_codes(sb_gpu[same], enc["signs"][same], margins[same], "sign", max_frac)
     return nbad, nties, same
 
 

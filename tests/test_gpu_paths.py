@@ -131,19 +131,24 @@ def test_encode_boundary_exact_coordinates(api, rot, mode, bits):
     codes, norms, gammas = qz.encode(_dev(x))
     codes = codes.cpu().numpy()
     margins = oracle.code_margins(x, pi, t)
+    # a quarter of the coordinates sit in the tie zone by construction, so the fraction cap of the
+    # workloads' inputs does not apply; every differing decision must still lie in the tie zone
     if prod:
         enc = parity.oracle_prod(x, pi, s, bits)
         idx, sb = oracle.parse_prod_record(codes, d, bits)
-        nbad, nties = parity.check_codes(idx, enc["idx"], margins)
-        parity.check_prod_signs(sb, idx, enc, x, pi, s)
+        nbad, nties = parity.check_codes(idx, enc["idx"], margins, max_frac=None)
+        parity.check_prod_signs(sb, idx, enc, x, pi, s, max_frac=None)
     else:
         enc = parity.oracle_mse(x, pi, bits)
         idx = oracle.parse_mse_record(codes, d, bits)
-        nbad, nties = parity.check_codes(idx, enc["idx"], margins)
+        nbad, nties = parity.check_codes(idx, enc["idx"], margins, max_frac=None)
     assert parity.check_norms(norms.cpu().numpy(), x) == 0
     print(f"boundary encode rot={rot} {mode} b={bits}: {nties} tie-zone coordinates, {nbad} differ")
     if rot == "identity":
-        # with an exact rotation the zeros are exact: index L/2 - 1 on both sides
+        # with an exact rotation a zero coordinate is exactly on the middle boundary: index L/2 - 1
+        # (the lower cell) on both sides
+        L = 1 << (bits - 1 if prod else bits)
+        assert np.all(idx[x == 0] == L // 2 - 1) and np.all(enc["idx"][x == 0] == L // 2 - 1)
         assert nties >= 4 * n
 
 
@@ -168,7 +173,9 @@ def test_encode_norm_saturation_and_subnormal(api, xdtype, mode, bits):
     nb = norms.cpu().numpy()
     assert parity.check_norms(nb, x) == 0
     nh = parity.f16_from_bits(nb)
-    assert np.all(nh[:8 * 5][np.repeat(rho[:5], 8) >= 65520] == np.float16(65504))
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)  # the norms of the rows as given (bf16 rounding moves them)
+    assert np.any(nx >= 65520) and np.all(nh[nx >= 65520] == np.float16(65504))
+    assert np.any((nx > 0) & (nx < 6.1e-5)) and np.all(nh[(nx > 0) & (nx < 6.1e-5)] < np.float16(6.104e-5))
     if prod:
         enc = parity.oracle_prod(x, pi, s, bits)
         idx, sb = oracle.parse_prod_record(codes, d, bits)

@@ -92,7 +92,8 @@ def test_quantizer_create_rejects_bad_shapes_without_device():
     assert lib.tq_quantizer_create(C.byref(h), 100, 2, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID  # d % 64
     assert lib.tq_quantizer_create(C.byref(h), 4096, 2, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID
     assert lib.tq_quantizer_create(C.byref(h), 128, 5, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_UNSUPPORTED
-    assert lib.tq_quantizer_create(C.byref(h), 128, 1, _lib.TQ_PROD, pi, pi) == _lib.TQ_ERR_UNSUPPORTED
+    assert lib.tq_quantizer_create(C.byref(h), 128, 0, _lib.TQ_PROD, pi, pi) == _lib.TQ_ERR_UNSUPPORTED
+    assert lib.tq_quantizer_create(C.byref(h), 128, 5, _lib.TQ_PROD, pi, pi) == _lib.TQ_ERR_UNSUPPORTED
     assert lib.tq_quantizer_create(C.byref(h), 128, 3, _lib.TQ_PROD, pi, None) == _lib.TQ_ERR_INVALID
     assert lib.tq_quantizer_create(C.byref(h), 128, 3, 7, pi, pi) == _lib.TQ_ERR_INVALID
     assert lib.tq_quantizer_create(None, 128, 3, _lib.TQ_MSE, pi, None) == _lib.TQ_ERR_INVALID
@@ -106,9 +107,35 @@ def test_entry_points_reject_null_quantizer():
     assert lib.tq_encode_prod(z, z, 0, 1, 128, z, z, z, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_decode(z, z, z, z, 1, z, 128, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_score(z, z, 1, 128, z, z, z, 1, 0, z, z, z, 0, z) == _lib.TQ_ERR_INVALID
-    assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_attn_decode_ws_bytes(z, 1, 4, 1, 16, 0) == 0
+    assert lib.tq_attn_prefill(z, z, z, 1, 1, 4, 4, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_prefill_ws_bytes(z, 1, 4, 4, 1, 16, 0) == 0
+    assert lib.tq_attn_decode_append(z, z, z, 1, 1, 4, 1, z, z, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0,
+                                     z) == _lib.TQ_ERR_INVALID
     assert lib.tq_tile_records(z, z, 1, 32, z, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_score_ws_bytes(z, 1, 1, 0) == 0
     assert lib.tq_quantizer_info(z, None, None, None, None, None) == _lib.TQ_ERR_INVALID
     lib.tq_quantizer_destroy(z)  # no-op on null
+
+
+def test_binding_rejects_host_tensors_and_wrong_shapes():
+    """The binding checks every tensor before a pointer reaches the C ABI (a host pointer or a short
+    buffer would otherwise become an out-of-bounds device access)."""
+    import types
+    import torch
+    from vector_quantization_rotation_amd import api
+    kq = types.SimpleNamespace(d=128, bits=3, mode=api.TQ_MSE, planes=3, code_bytes=48)
+    vq = types.SimpleNamespace(d=128, bits=2, mode=api.TQ_PROD, planes=2, code_bytes=32)
+    B, Hq, Hkv, T = 1, 4, 1, 64
+    q = torch.zeros((B, Hq, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((B, Hkv, T, 48), dtype=torch.uint8)
+    h16 = torch.zeros((B, Hkv, T), dtype=torch.int16)
+    vc = torch.zeros((B, Hkv, T, 32), dtype=torch.uint8)
+    seq = torch.zeros((B,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        api.attn_decode(kq, vq, q, kc, h16, vc, h16, h16, seq, 0.1)
+    with pytest.raises(ValueError, match="device tensor"):
+        api.attn_prefill(kq, vq, q.view(B, 1, Hq, 128), kc, h16, vc, h16, h16, seq, 0.1)
+    with pytest.raises(ValueError):
+        api._need(torch.zeros(3), "x", torch.float32, (4,))

@@ -196,7 +196,8 @@ def attn_decode_ws_bytes(kq: Quantizer, B: int, Hq: int, Hkv: int, Tstride: int,
     return load().tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
 
 
-def _attn_args(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout):
+def _attn_args(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout,
+               kgammas=None):
     """Check every tensor of a decode-attention call against the shapes the C ABI assumes."""
     _dev(q, "q")
     if q.dim() != 3:
@@ -213,6 +214,10 @@ def _attn_args(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, vcodes, vnorms, 
     _need(kcodes, "kcodes", torch.uint8, (B, Hkv, Tstride, kq.code_bytes), dev)
     for t, nm in ((knorms, "knorms"), (vnorms, "vnorms"), (vgammas, "vgammas")):
         _need(t, nm, _HALF_BITS, (B, Hkv, Tstride), dev)
+    if kq.mode == TQ_PROD:
+        if kgammas is None:
+            raise ValueError("kgammas are required for Algorithm 2 keys")
+        _need(kgammas, "kgammas", _HALF_BITS, (B, Hkv, Tstride), dev)
     if vlayout == TQ_LAYOUT_TILE32:
         _need(vcodes, "vcodes", (torch.int32, torch.uint32), (B, Hkv, (Tstride + 31) // 32, vq.planes, d), dev)
     elif vlayout == TQ_LAYOUT_ROWS:
@@ -226,10 +231,12 @@ def _attn_args(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, vcodes, vnorms, 
 
 
 def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
-                seq_len: torch.Tensor, scale: float, out=None, ws=None, vlayout: int = TQ_LAYOUT_ROWS):
-    """q [B, Hq, d]; key caches [B, Hkv, Tstride, ...]; value records in `vlayout`; -> out [B, Hq, d] fp32."""
+                seq_len: torch.Tensor, scale: float, out=None, ws=None, vlayout: int = TQ_LAYOUT_ROWS, kgammas=None):
+    """q [B, Hq, d]; key caches [B, Hkv, Tstride, ...] (kgammas for Algorithm-2 keys); value records in
+    `vlayout`; -> out [B, Hq, d] fp32."""
     lib = load()
-    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout)
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout,
+                                             kgammas)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     ws_b = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
@@ -237,31 +244,87 @@ def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, v
         ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=dev)
     _need(ws, "ws", torch.uint8, device=dev)
     rc = lib.tq_attn_decode(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms),
-                            _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), float(scale),
-                            _ptr(out), _ptr(ws), ws.numel(), _stream())
+                            _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len),
+                            float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream())
     _lib._check("tq_attn_decode", rc)
+    return out
+
+
+def attn_prefill(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
+                 q_pos: torch.Tensor, scale: float, out=None, ws=None, kgammas=None):
+    """Causal attention of M query tokens per sequence, q [B, M, Hq, d] (token m at position q_pos[b] + m),
+    against the row-record cache that already holds them -> out [B, M, Hq, d] fp32."""
+    lib = load()
+    _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, M, Hq, d]")
+    B, M, Hq, d = q.shape
+    dev = q.device
+    _need(q, "q", tuple(_DT), device=dev)
+    _attn_args(kq, vq, q.reshape(B, M * Hq, d), kcodes, knorms, vcodes, vnorms, vgammas, q_pos, None,
+               TQ_LAYOUT_ROWS, kgammas)
+    Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if out is None:
+        out = torch.empty((B, M, Hq, d), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, M, Hq, d), dev)
+    ws_b = lib.tq_attn_prefill_ws_bytes(kq.handle, B, M, Hq, Hkv, Tstride, TQ_LAYOUT_ROWS)
+    if ws is None:
+        ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", torch.uint8, device=dev)
+    rc = lib.tq_attn_prefill(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, M, Hq, Hkv, _ptr(kcodes), _ptr(knorms),
+                             _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), TQ_LAYOUT_ROWS, Tstride,
+                             _ptr(q_pos), float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _lib._check("tq_attn_prefill", rc)
+    return out
+
+
+def attn_decode_append(kq: Quantizer, vq: Quantizer, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       kcodes, knorms, vcodes, vnorms, vgammas, seq_len: torch.Tensor, scale: float, out=None,
+                       ws=None, vlayout: int = TQ_LAYOUT_ROWS, kgammas=None):
+    """One decode step with the new token appended: k_new, v_new [B, Hkv, d] are encoded into the cache at
+    position seq_len[b] (the cache tensors are written in place) and the step attends over seq_len[b] + 1
+    tokens.  seq_len is only read: advance it before the next step.  -> out [B, Hq, d] fp32."""
+    lib = load()
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout,
+                                             kgammas)
+    _need(k_new, "k_new", tuple(_DT), (B, Hkv, d), dev)
+    _need(v_new, "v_new", (k_new.dtype,), (B, Hkv, d), dev)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws_b = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
+    if ws is None:
+        ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", torch.uint8, device=dev)
+    rc = lib.tq_attn_decode_append(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(k_new), _ptr(v_new),
+                                   _DT[k_new.dtype], _ptr(kcodes), _ptr(knorms), _ptr(kgammas), _ptr(vcodes),
+                                   _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), float(scale),
+                                   _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _lib._check("tq_attn_decode_append", rc)
     return out
 
 
 def attn_decode_bound(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
                       seq_len: torch.Tensor, scale: float, out: torch.Tensor, ws: torch.Tensor,
-                      vlayout: int = TQ_LAYOUT_ROWS):
+                      vlayout: int = TQ_LAYOUT_ROWS, kgammas=None):
     """attn_decode with every argument checked and marshalled once: returns a no-argument
     callable that enqueues the same call on the stream that is current when it is called
     (for tight decode loops).  The callable holds references to every tensor it reads or
     writes, so they stay alive as long as it does."""
     lib = load()
-    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout)
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout,
+                                             kgammas)
     if out is None:
         raise ValueError("out is required")
     _need(ws, "ws", torch.uint8, device=dev)
     need = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
     if ws.numel() < need:
         raise ValueError(f"ws holds {ws.numel()} bytes, the call needs {need}")
-    keep = (kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, ws)
-    args = (kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms), _ptr(vcodes),
-            _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), C.c_float(scale), _ptr(out), _ptr(ws),
-            C.c_size_t(ws.numel()))
+    keep = (kq, vq, q, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, seq_len, out, ws)
+    args = (kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes), _ptr(knorms), _ptr(kgammas),
+            _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride, _ptr(seq_len), C.c_float(scale), _ptr(out),
+            _ptr(ws), C.c_size_t(ws.numel()))
     fn = lib.tq_attn_decode
 
     def call():

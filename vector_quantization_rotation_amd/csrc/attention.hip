@@ -11,6 +11,7 @@
 //
 // Generic path: one wavefront per (batch, kv head, head subgroup, sequence
 // split); lane j owns coordinates j, j+64, ...; online softmax per head.
+#include "append.cuh"
 #include "common.cuh"
 
 namespace tq {
@@ -28,12 +29,20 @@ int coords_per_lane_supported(int d) {
   return (cp == 1 || cp == 2 || cp == 4 || cp == 8 || cp == 16 || cp == 24 || cp == 32) ? cp : 0;
 }
 
-AttnPlan make_plan(int d, int B, int Hq, int Hkv, int64_t T) {
+// heads per wave of attn_split_kernel: 32 query coordinates per lane, half that for Algorithm-2 keys
+// (each head also holds S_K q)
+constexpr int split_heads(int cp, bool kprod) {
+  return kprod ? (32 / cp / 2 > 0 ? 32 / cp / 2 : 1) : (32 / cp > 0 ? 32 / cp : 1);
+}
+
+// M query tokens per sequence: M G query rows per (batch, kv-head) pair
+AttnPlan make_plan(int d, int B, int Hq, int Hkv, int64_t T, bool kprod, int M = 1) {
   AttnPlan p{};
   p.CP = coords_per_lane_supported(d);
   p.G = Hq / Hkv;
-  p.GW = p.CP ? std::min(p.G, std::max(1, 32 / p.CP)) : 1;
-  p.nsub = (p.G + p.GW - 1) / p.GW;
+  const int rows = M * p.G;
+  p.GW = p.CP ? std::min(rows, split_heads(p.CP, kprod)) : 1;
+  p.nsub = (rows + p.GW - 1) / p.GW;
   const int64_t units = (int64_t)B * Hkv * p.nsub;
   int64_t want = std::max<int64_t>(1, 4096 / std::max<int64_t>(units, 1));
   int64_t chunk = std::max<int64_t>(kAttnChunkMin, (T + want - 1) / std::max<int64_t>(want, 1));
@@ -47,11 +56,18 @@ size_t partial_floats(int d) { return 2 + 2 * (size_t)d; }
 
 }  // namespace
 
-// q'[b,h,:] = Pi_K q[b,h,:]
+// q'[b,h,:] = Pi_K q[b,h,:] into qrot[bh][0..d), and for Algorithm-2 keys (sT not null) also
+// S_K q[b,h,:] into qrot[bh][d..2d); ld = d or 2d.  A decode step that appends a token (app.on) has it
+// encoded into the cache by the work-group of the first query head of each kv head.
 template <int QT>
-__global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *piT, float *qrot) {
+__global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *piT, const float *sT,
+                                                        int ld, float *qrot, int Hq, int G, AppendArgs app) {
   extern __shared__ float sq[];
   const int64_t bh = blockIdx.x;
+  if (app.on && (bh % Hq) % G == 0) {
+    __shared__ AppendShared app_sh;
+    append_token(app, (int)(bh / Hq), (int)((bh % Hq) / G), app_sh);
+  }
   for (int j = threadIdx.x; j < d; j += 256) {
     float v;
     if (QT == TQ_F32) v = static_cast<const float *>(q)[bh * d + j];
@@ -64,34 +80,51 @@ __global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, co
   for (int j = threadIdx.x; j < d; j += 256) {
     float acc = 0.f;
     for (int k = 0; k < d; ++k) acc = fmaf(piT[(int64_t)k * d + j], sq[k], acc);
-    qrot[bh * d + j] = acc;
+    qrot[bh * ld + j] = acc;
   }
+  if (sT)
+    for (int j = threadIdx.x; j < d; j += 256) {
+      float acc = 0.f;
+      for (int k = 0; k < d; ++k) acc = fmaf(sT[(int64_t)k * d + j], sq[k], acc);
+      qrot[bh * ld + d + j] = acc;
+    }
 }
 
-template <int CP, int GW>
+// KPROD: Algorithm-2 keys (kbits index planes, then the sign plane; score adds kqjl gamma <S_K q, s>).
+// The M query tokens of a sequence (M = 1 for a decode step) and the G query heads of a kv head form the
+// M G query rows of a (batch, kv-head) pair, ordered token-major; a wave takes GW consecutive rows.  Row
+// (m, h) is query row (b M + m) Hq + g G + h and attends the first min(len[b] + m + add, Tstride) tokens
+// (a decode step: m = 0, add = 1 when it appended a token; a prefill chunk: add = 1, causal).
+template <int CP, int GW, bool KPROD>
 __global__ __launch_bounds__(64) void attn_split_kernel(
-    const float *qrot, int Hq, int Hkv, int G, int nsub, int d, const uint8_t *kcodes, const uint16_t *knorms,
-    int64_t kcb, int kbits, const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t vcb,
-    int vbmse, int64_t Tstride, const int32_t *seq_len, float scale_log2, float vqjl, Codebook kc, Codebook vc,
-    int chunk, int nsplit, float *part) {
+    const float *qrot, int Hq, int Hkv, int G, int M, int nsub, int d, const uint8_t *kcodes,
+    const uint16_t *knorms, const uint16_t *kgammas, int64_t kcb, int kbits, float kqjl, const uint8_t *vcodes,
+    const uint16_t *vnorms, const uint16_t *vgammas, int64_t vcb, int vbmse, int64_t Tstride, const int32_t *len,
+    int add, float scale_log2, float vqjl, Codebook kc, Codebook vc, int chunk, int nsplit, float *part) {
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;  // ((b * Hkv) + g) * nsub + sub
   const int split = blockIdx.y;
   const int sub = unit % nsub;
   const int bg = unit / nsub;
   const int g = bg % Hkv, b = bg / Hkv;
-  const int h0 = g * G + sub * GW;
-  const int gw = imin32(GW, G - sub * GW);
-  const int64_t T = seq_len[b];
+  const int r0 = sub * GW;                   // first row of this wave among the M G rows
+  const int gw = imin32(GW, M * G - r0);
+  const int64_t base_len = imax64(len[b], 0) + add;
+  auto row_q = [&](int h) { const int r = r0 + h; return ((int64_t)b * M + r / G) * Hq + g * G + r % G; };
+  auto row_T = [&](int h) { return imin64(base_len + (r0 + h) / G, Tstride); };
+  const int64_t T = row_T(gw - 1);  // the rows are token-major: the last one sees the most tokens
   const int64_t t0 = (int64_t)split * chunk;
   const int64_t t1 = imin64(T, t0 + chunk);
 
-  float qv[GW][CP];
+  const int ldq = KPROD ? 2 * d : d;
+  float qv[GW][CP], qs[KPROD ? GW : 1][CP];
 #pragma unroll
   for (int h = 0; h < GW; ++h)
 #pragma unroll
-    for (int c = 0; c < CP; ++c)
-      qv[h][c] = h < gw ? qrot[((int64_t)b * Hq + h0 + h) * d + lane + 64 * c] : 0.f;
+    for (int c = 0; c < CP; ++c) {
+      qv[h][c] = h < gw ? qrot[row_q(h) * ldq + lane + 64 * c] : 0.f;
+      if (KPROD) qs[KPROD ? h : 0][c] = h < gw ? qrot[row_q(h) * ldq + d + lane + 64 * c] : 0.f;
+    }
   float m[GW], l[GW], am[GW][CP], aq[GW][CP];
 #pragma unroll
   for (int h = 0; h < GW; ++h) {
@@ -105,7 +138,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   for (int64_t t = t0; t < t1; ++t) {
     const uint8_t *kr = kcodes + (base + t) * kcb;
     const uint8_t *vr = vcodes + (base + t) * vcb;
-    float kval[CP], vm[CP], vs[CP];
+    float kval[CP], ksg[CP], vm[CP], vs[CP];
 #pragma unroll
     for (int c = 0; c < CP; ++c) {
       int idx = 0;
@@ -114,6 +147,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
         idx |= (int)((w >> lane) & 1ull) << p;
       }
       kval[c] = kc.c[idx];
+      if (KPROD) {
+        unsigned long long w = *reinterpret_cast<const unsigned long long *>(kr + kbits * wbytes + 8 * c);
+        ksg[c] = ((w >> lane) & 1ull) ? 1.f : -1.f;
+      }
       int vi = 0;
       for (int p = 0; p < vbmse; ++p) {
         unsigned long long w = *reinterpret_cast<const unsigned long long *>(vr + p * wbytes + 8 * c);
@@ -124,15 +161,21 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
       vs[c] = ((ws >> lane) & 1ull) ? 1.f : -1.f;
     }
     const float kn = f16_to_f32(knorms[base + t]) * scale_log2;
+    const float kg = KPROD ? f16_to_f32(kgammas[base + t]) * kqjl * scale_log2 : 0.f;
     const float vn = f16_to_f32(vnorms[base + t]);
     const float vg = f16_to_f32(vgammas[base + t]) * vqjl;
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
       if (h >= gw) break;
-      float part_s = 0.f;
+      if (t >= row_T(h)) continue;  // causal: this row's query token sees fewer tokens
+      float part_s = 0.f, part_q = 0.f;
 #pragma unroll
-      for (int c = 0; c < CP; ++c) part_s = fmaf(qv[h][c], kval[c], part_s);
-      const float s = wave_sum_f32(part_s) * kn;  // log2-domain score
+      for (int c = 0; c < CP; ++c) {
+        part_s = fmaf(qv[h][c], kval[c], part_s);
+        if (KPROD) part_q = fmaf(qs[KPROD ? h : 0][c], ksg[c], part_q);
+      }
+      // log2-domain score
+      const float s = KPROD ? fmaf(wave_sum_f32(part_s), kn, wave_sum_f32(part_q) * kg) : wave_sum_f32(part_s) * kn;
       if (s > m[h]) {
         const float corr = exp2f(m[h] - s);
         l[h] *= corr;
@@ -154,7 +197,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 #pragma unroll
   for (int h = 0; h < GW; ++h) {
     if (h >= gw) break;
-    float *dst = part + (((int64_t)b * Hq + h0 + h) * nsplit + split) * (2 + 2 * (int64_t)d);
+    float *dst = part + (row_q(h) * nsplit + split) * (2 + 2 * (int64_t)d);
     if (lane == 0) { dst[0] = m[h]; dst[1] = l[h]; }
 #pragma unroll
     for (int c = 0; c < CP; ++c) {
@@ -413,47 +456,66 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T);
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
                   const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                  void *ws, hipStream_t st);
+                  void *ws, const AppendArgs *app, hipStream_t st);
+
+// workspace of the row-record path: rotated queries, split partials, merged rows (M query tokens per sequence)
+size_t rows_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride) {
+  const bool kprod = kq->mode == TQ_PROD;
+  const int d = kq->d;
+  const size_t BH = (size_t)B * M * Hq;
+  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride, kprod, M);
+  size_t qb = (BH * (kprod ? 2 : 1) * d * 4 + 255) & ~(size_t)255;
+  return qb + ((BH * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255) + attn_merge_ws_bytes((int64_t)BH, d);
+}
 
 size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout) {
-  if (vlayout == TQ_LAYOUT_TILE32) return attn_fast_ws_bytes(kq->d, kq->bits, B, Hq, Hkv, Tstride);
-  const int d = kq->d;
-  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
-  size_t qb = ((size_t)B * Hq * d * 4 + 255) & ~(size_t)255;
-  return qb + (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255) +
-         attn_merge_ws_bytes(B * Hq, d);
+  const bool kprod = kq->mode == TQ_PROD;
+  if (vlayout == TQ_LAYOUT_TILE32 && !kprod) return attn_fast_ws_bytes(kq->d, kq->bits, B, Hq, Hkv, Tstride);
+  return rows_ws_bytes(kq, B, 1, Hq, Hkv, Tstride);
 }
 
 template <int CP>
-static void launch_split(const AttnPlan &p, dim3 grid, hipStream_t st, const float *qrot, int Hq, int Hkv, int d,
-                         const tq_quantizer *kq, const tq_quantizer *vq, const uint8_t *kcodes,
-                         const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
-                         const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale_log2,
-                         float *part) {
-  constexpr int GW = (32 / CP) > 0 ? (32 / CP) : 1;
-  hipLaunchKernelGGL((attn_split_kernel<CP, GW>), grid, dim3(64), 0, st, qrot, Hq, Hkv, p.G, p.nsub, d, kcodes,
-                     knorms, (int64_t)kq->code_bytes, kq->bits, vcodes, vnorms, vgammas, (int64_t)vq->code_bytes,
-                     vq->bmse, Tstride, seq_len, scale_log2, vq->qjl_scale, kq->cb, vq->cb, p.chunk, p.nsplit, part);
+static void launch_split(const AttnPlan &p, dim3 grid, hipStream_t st, const float *qrot, int Hq, int Hkv, int M,
+                         int d, const tq_quantizer *kq, const tq_quantizer *vq, const uint8_t *kcodes,
+                         const uint16_t *knorms, const uint16_t *kgammas, const uint8_t *vcodes,
+                         const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride, const int32_t *len,
+                         int add, float scale_log2, float *part) {
+  if (kq->mode == TQ_PROD)
+    hipLaunchKernelGGL((attn_split_kernel<CP, split_heads(CP, true), true>), grid, dim3(64), 0, st, qrot, Hq, Hkv, p.G,
+                       M, p.nsub, d, kcodes, knorms, kgammas, (int64_t)kq->code_bytes, kq->bmse, kq->qjl_scale,
+                       vcodes, vnorms, vgammas, (int64_t)vq->code_bytes, vq->bmse, Tstride, len, add, scale_log2,
+                       vq->qjl_scale, kq->cb, vq->cb, p.chunk, p.nsplit, part);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<CP, split_heads(CP, false), false>), grid, dim3(64), 0, st, qrot, Hq, Hkv,
+                       p.G, M, p.nsub, d, kcodes, knorms, kgammas, (int64_t)kq->code_bytes, kq->bmse, 0.f, vcodes,
+                       vnorms, vgammas, (int64_t)vq->code_bytes, vq->bmse, Tstride, len, add, scale_log2,
+                       vq->qjl_scale, kq->cb, vq->cb, p.chunk, p.nsplit, part);
 }
 
-int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
-                    const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
-                    const uint16_t *vgammas, int vlayout, int64_t Tstride, const int32_t *seq_len, float scale,
-                    float *out, void *ws, size_t ws_bytes, hipStream_t st) {
-  if (vlayout == TQ_LAYOUT_TILE32)
-    return run_attn_fast(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, reinterpret_cast<const uint32_t *>(vcodes), vnorms,
-                         vgammas, Tstride, seq_len, scale, out, ws, st);
+// Row-record path for M query tokens per sequence: q [B, M, Hq, d] -> out [B, M, Hq, d]; query token m of
+// sequence b attends the first min(len[b] + m + add, Tstride) tokens
+static int run_attn_rows(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
+                         int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                         const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride,
+                         const int32_t *len, int add, float scale, float *out, void *ws, const AppendArgs &ap,
+                         hipStream_t st) {
+  const bool kprod = kq->mode == TQ_PROD;
   const int d = kq->d;
-  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride);
+  AttnPlan p = make_plan(d, B, Hq, Hkv, Tstride, kprod, M);
   if (!p.CP) return TQ_ERR_UNSUPPORTED;
+  const int ldq = kprod ? 2 * d : d;
+  const int64_t BH = (int64_t)B * M * Hq;
   float *qrot = static_cast<float *>(ws);
-  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + (((size_t)B * Hq * d * 4 + 255) & ~(size_t)255));
+  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + (((size_t)BH * ldq * 4 + 255) & ~(size_t)255));
   const size_t shq = (size_t)d * 4;
+  const float *sT = kprod ? kq->sT : nullptr;
+  const int G = Hq / Hkv;
   {
   ProfScope ps("attn_qrot", st);
-  if (qt == TQ_F32) hipLaunchKernelGGL(attn_qrot_kernel<TQ_F32>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
-  else if (qt == TQ_BF16) hipLaunchKernelGGL(attn_qrot_kernel<TQ_BF16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
-  else hipLaunchKernelGGL(attn_qrot_kernel<TQ_F16>, dim3(B * Hq), dim3(256), shq, st, q, d, kq->piT, qrot);
+  const dim3 qg((unsigned)BH);
+  if (qt == TQ_F32) hipLaunchKernelGGL(attn_qrot_kernel<TQ_F32>, qg, dim3(256), shq, st, q, d, kq->piT, sT, ldq, qrot, Hq, G, ap);
+  else if (qt == TQ_BF16) hipLaunchKernelGGL(attn_qrot_kernel<TQ_BF16>, qg, dim3(256), shq, st, q, d, kq->piT, sT, ldq, qrot, Hq, G, ap);
+  else hipLaunchKernelGGL(attn_qrot_kernel<TQ_F16>, qg, dim3(256), shq, st, q, d, kq->piT, sT, ldq, qrot, Hq, G, ap);
   }
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
@@ -461,20 +523,54 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   dim3 grid((unsigned)(B * Hkv * p.nsub), (unsigned)p.nsplit);
   {
   ProfScope ps("attn_split", st);
+#define TQ_SPLIT(CPV) launch_split<CPV>(p, grid, st, qrot, Hq, Hkv, M, d, kq, vq, kcodes, knorms, kgammas, vcodes, \
+                                        vnorms, vgammas, Tstride, len, add, scale_log2, part)
   switch (p.CP) {
-    case 1: launch_split<1>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    case 2: launch_split<2>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    case 4: launch_split<4>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    case 8: launch_split<8>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    case 16: launch_split<16>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    case 24: launch_split<24>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
-    default: launch_split<32>(p, grid, st, qrot, Hq, Hkv, d, kq, vq, kcodes, knorms, vcodes, vnorms, vgammas, Tstride, seq_len, scale_log2, part); break;
+    case 1: TQ_SPLIT(1); break;
+    case 2: TQ_SPLIT(2); break;
+    case 4: TQ_SPLIT(4); break;
+    case 8: TQ_SPLIT(8); break;
+    case 16: TQ_SPLIT(16); break;
+    case 24: TQ_SPLIT(24); break;
+    default: TQ_SPLIT(32); break;
   }
+#undef TQ_SPLIT
   }
   if ((rc = launch_check()) != TQ_OK) return rc;
   float *merged = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
-                                            (((size_t)B * Hq * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255));
-  return attn_combine(part, B * Hq, p.nsplit, d, vq->pi, vq->s, merged, out, st);
+                                            (((size_t)BH * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255));
+  return attn_combine(part, (int)BH, p.nsplit, d, vq->pi, vq->s, merged, out, st);
+}
+
+int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
+                    const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas, const uint8_t *vcodes,
+                    const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
+                    const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes,
+                    const AppendArgs *app, hipStream_t st) {
+  const bool kprod = kq->mode == TQ_PROD;
+  if (vlayout == TQ_LAYOUT_TILE32) {
+    // the matrix-core kernels take Algorithm-1 keys and values with at least one index bit
+    if (kprod || vq->bmse < 1) return TQ_ERR_UNSUPPORTED;
+    return run_attn_fast(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, reinterpret_cast<const uint32_t *>(vcodes), vnorms,
+                         vgammas, Tstride, seq_len, scale, out, ws, app, st);
+  }
+  AppendArgs ap{};
+  if (app) ap = *app;
+  return run_attn_rows(kq, vq, q, qt, B, 1, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, Tstride, seq_len,
+                       ap.on ? 1 : 0, scale, out, ws, ap, st);
+}
+
+size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride) {
+  return rows_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
+}
+
+int run_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
+                     int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride,
+                     const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st) {
+  AppendArgs ap{};
+  return run_attn_rows(kq, vq, q, qt, B, M, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, Tstride, q_pos,
+                       1, scale, out, ws, ap, st);
 }
 
 }  // namespace tq

@@ -34,6 +34,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "append.cuh"
 #include "common.cuh"
 
 namespace tq {
@@ -53,6 +54,7 @@ struct FastAttnArgs {
   float *part;              // [B*Hq, nsplit, 2 + 2D]
   int64_t Tstride, ntile;
   int Hq, Hkv, G, nsub, chunk, nsplit;
+  int seq_add;              // 1 when the step appended a token at seq_len[b] (it is attended too)
   float scale_log2, vqjl;
   float vbeta[4];           // Walsh coefficients of the value codebook (odd subsets)
   float kbeta[8];           // Walsh coefficients of the key codebook (applied after the MFMA when folded)
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   // sequence length is wave-uniform: keep it (and everything derived) in scalar registers
-  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0), a.Tstride);
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
   const int64_t seq = (int64_t)b * a.Hkv + g;
   const int64_t c0 = (int64_t)split * a.chunk;
   const int64_t c1 = imin64(T, c0 + a.chunk);
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int h0 = g * a.G + sub * FA_GMAX;
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   const bool head_ok = hl < gw;
-  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0), a.Tstride);
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
   const int64_t seq = (int64_t)b * a.Hkv + g;
   const int64_t c0 = (int64_t)split * a.chunk;
   const int64_t c1 = imin64(T, c0 + a.chunk);
@@ -982,6 +984,7 @@ struct PrepArgs {
   float ctop;
   int *qimg;
   float *qinfo;
+  AppendArgs app;  // the decode step's new token (app.on), encoded by the work-group of head 0, subgroup 0
 };
 
 // four fixed-point digits of u (|u| <= 224) as e4m3 bytes: u = sum_d k_d Q_d + e with Q_d = 2^(4 - 5 d),
@@ -1023,6 +1026,10 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   const bool present = h < gw;  // a head past the group's end gets zero images and offsets
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  if (a.app.on && sub == 0 && h == 0) {
+    __shared__ AppendShared app_sh;
+    append_token(a.app, b, g, app_sh);
+  }
   for (int j = tid; j < D; j += 256) {
     float v = 0.f;
     if (present) {
@@ -1308,7 +1315,7 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, 
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
                   const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                  void *ws, hipStream_t st) {
+                  void *ws, const AppendArgs *app, hipStream_t st) {
   const int D = kq->d, KB = kq->bits, VB = vq->bmse;
   if (!fast_supported(D, KB, VB)) return TQ_ERR_UNSUPPORTED;
   FastPlan fp = fast_plan(D, KB, VB, B, Hq, Hkv, Tstride);
@@ -1336,12 +1343,14 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   pa.ctop = (float)kq->c64[(1 << KB) - 1];
   pa.qimg = reinterpret_cast<int *>(w + fp.img_off);
   pa.qinfo = reinterpret_cast<float *>(w + fp.info_off);
+  if (app) pa.app = *app;
   FastAttnArgs fa{};
   fa.qimg = pa.qimg; fa.qinfo = pa.qinfo; fa.kcodes = kcodes; fa.knorms = knorms; fa.vtiles = vtiles;
   fa.vnorms = vnorms; fa.vgammas = vgammas; fa.seq_len = seq_len;
   fa.part = reinterpret_cast<float *>(w + fp.part_off);
   fa.Tstride = Tstride; fa.ntile = (Tstride + 31) / 32;
   fa.Hq = Hq; fa.Hkv = Hkv; fa.G = Hq / Hkv; fa.nsub = fp.nsub; fa.chunk = fp.chunk; fa.nsplit = fp.nsplit;
+  fa.seq_add = (app && app->on) ? 1 : 0;
   fa.scale_log2 = scale * 1.4426950408889634f;
   fa.vqjl = vq->qjl_scale;
   for (int i = 0; i < 4; ++i) fa.vbeta[i] = (float)vb64[i];

@@ -134,7 +134,8 @@ struct EpiStore {
 // Algorithm-1 index planes for 64 coordinates (one tile column block) per row.
 // For Algorithm 2 also the rotated residual y - n_hat c[idx] and its squared norm over the block (fp32:
 // the fp16 gamma tolerates 1e-5 relative), one partial per (row, block) so no atomics are needed.
-// BM index bits; the cell index is a binary search over the row's scaled boundaries t_k n.
+// BM index bits; the cell index is a binary search over the row's scaled boundaries t_k n.  BM = 0
+// (Algorithm 2 at one bit) writes no index plane and the residual is y itself.
 template <int BM>
 struct EpiQuant {
   uint8_t *codes;
@@ -155,7 +156,7 @@ struct EpiQuant {
       nl = n32[row0 + rb + lane];
       hl = f16_to_f32(nhat[row0 + rb + lane]);
     }
-    float tb[L - 1], cc[L];
+    float tb[L > 1 ? L - 1 : 1], cc[L];  // (BM = 0: one cell, no boundary, centroid 0)
 #pragma unroll
     for (int k = 0; k < L - 1; ++k) tb[k] = cb.t[k];
 #pragma unroll
@@ -562,6 +563,7 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
   float *rs = prod ? resid : nullptr, *rq = prod ? rsq : nullptr;
   const int64_t cbytes = (int64_t)q->code_bytes;
   switch (q->bmse) {
+    case 0: rc = rotate(EpiQuant<0>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
     case 1: rc = rotate(EpiQuant<1>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
     case 2: rc = rotate(EpiQuant<2>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
     case 3: rc = rotate(EpiQuant<3>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;

@@ -111,6 +111,10 @@ double cell_moment_rel(int d, double lo, double hi) {
 double cell_mean(int d, double lo, double hi) { return cell_moment_rel(d, lo, hi) / cell_mass_rel(d, lo, hi); }
 
 int lloyd_max(int d, int bits, double *c, double *t) {
+  if (bits == 0) {  // one cell: its centroid is the mean of the symmetric law
+    c[0] = 0.0;
+    return TQ_OK;
+  }
   const int L = 1 << bits, H = L / 2;
   std::vector<double> pos(H), nxt(H);
   // start from the Gaussian-limit quantiles of the positive half
@@ -195,6 +199,30 @@ int launch_check() {
 
 }  // namespace tq
 
+static int attn_decode_impl(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                            int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                            const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                            int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws,
+                            size_t ws_bytes, const tq::AppendArgs *app, void *stream) {
+  if (!kq || !vq || vq->mode != TQ_PROD || kq->d != vq->d) return TQ_ERR_INVALID;
+  const bool kprod = kq->mode == TQ_PROD;
+  if (kq->device != vq->device) return TQ_ERR_INVALID;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tstride < 0 || !valid_dtype(qt)) return TQ_ERR_INVALID;
+  if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return TQ_ERR_INVALID;
+  if ((int64_t)B * Hq > 2147483647 / 2 || (int64_t)B * Hkv * ((Hq / Hkv + 3) / 4) > 2147483647) return TQ_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID;
+  if (B == 0) return TQ_OK;
+  if (!q || !out || !seq_len) return TQ_ERR_INVALID;
+  if (Tstride > 0 && (!kcodes || !knorms || !vcodes || !vnorms || !vgammas || (kprod && !kgammas)))
+    return TQ_ERR_INVALID;
+  if ((Tstride > 0 && (!aligned16(kcodes) || !aligned16(vcodes))) || !aligned16(out) || !aligned16(q))
+    return TQ_ERR_INVALID;
+  size_t need = tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride, vlayout);
+  if (need > 0 && (!ws || ws_bytes < need)) return TQ_ERR_WORKSPACE;
+  return tq::run_attn_decode(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, kprod ? kgammas : nullptr, vcodes, vnorms,
+                             vgammas, vlayout, Tstride, seq_len, scale, out, ws, ws_bytes, app, (hipStream_t)stream);
+}
+
 extern "C" {
 
 const char *tq_version(void) { return "0.1.0"; }
@@ -225,7 +253,7 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
   if (mode == TQ_MSE) {
     if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
   } else if (mode == TQ_PROD) {
-    if (bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
     if (!s) return TQ_ERR_INVALID;
   } else {
     return TQ_ERR_INVALID;
@@ -368,24 +396,79 @@ int tq_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, i
 }
 
 int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
-                   const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes, const uint16_t *vnorms,
-                   const uint16_t *vgammas, int vlayout, int64_t Tstride, const int32_t *seq_len, float scale,
-                   float *out, void *ws, size_t ws_bytes, void *stream) {
-  if (!kq || !vq || kq->mode != TQ_MSE || vq->mode != TQ_PROD || kq->d != vq->d) return TQ_ERR_INVALID;
-  if (kq->device != vq->device) return TQ_ERR_INVALID;
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tstride < 0 || !valid_dtype(qt)) return TQ_ERR_INVALID;
+                   const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas, const uint8_t *vcodes,
+                   const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
+                   const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  return attn_decode_impl(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, vlayout,
+                          Tstride, seq_len, scale, out, ws, ws_bytes, nullptr, stream);
+}
+
+size_t tq_attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride, int vlayout) {
+  if (!kq || B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || Tstride < 0 || vlayout != TQ_LAYOUT_ROWS) return 0;
+  return tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
+}
+
+int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
+                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                    const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                    int64_t Tstride, const int32_t *q_pos, float scale, float *out, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (!kq || !vq || vq->mode != TQ_PROD || kq->d != vq->d || kq->device != vq->device) return TQ_ERR_INVALID;
+  const bool kprod = kq->mode == TQ_PROD;
+  if (B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tstride < 0 || !valid_dtype(qt)) return TQ_ERR_INVALID;
   if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return TQ_ERR_INVALID;
-  if ((int64_t)B * Hq > 2147483647 / 2 || (int64_t)B * Hkv * ((Hq / Hkv + 3) / 4) > 2147483647) return TQ_ERR_UNSUPPORTED;
+  if (vlayout != TQ_LAYOUT_ROWS) return TQ_ERR_UNSUPPORTED;
+  if ((int64_t)B * M * Hq > 2147483647 / 2) return TQ_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return TQ_ERR_INVALID;
   if (B == 0) return TQ_OK;
-  if (!q || !out || !seq_len) return TQ_ERR_INVALID;
-  if (Tstride > 0 && (!kcodes || !knorms || !vcodes || !vnorms || !vgammas)) return TQ_ERR_INVALID;
+  if (!q || !out || !q_pos) return TQ_ERR_INVALID;
+  if (Tstride > 0 && (!kcodes || !knorms || !vcodes || !vnorms || !vgammas || (kprod && !kgammas)))
+    return TQ_ERR_INVALID;
   if ((Tstride > 0 && (!aligned16(kcodes) || !aligned16(vcodes))) || !aligned16(out) || !aligned16(q))
     return TQ_ERR_INVALID;
-  size_t need = tq::attn_ws_bytes(kq, B, Hq, Hkv, Tstride, vlayout);
+  const size_t need = tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
   if (need > 0 && (!ws || ws_bytes < need)) return TQ_ERR_WORKSPACE;
-  return tq::run_attn_decode(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, vcodes, vnorms, vgammas, vlayout, Tstride,
-                             seq_len, scale, out, ws, ws_bytes, (hipStream_t)stream);
+  return tq::run_attn_prefill(kq, vq, q, qt, B, M, Hq, Hkv, kcodes, knorms, kprod ? kgammas : nullptr, vcodes, vnorms,
+                              vgammas, Tstride, q_pos, scale, out, ws, (hipStream_t)stream);
+}
+
+int tq_attn_decode_append(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                          int Hkv, const void *k_new, const void *v_new, int xt, uint8_t *kcodes, uint16_t *knorms,
+                          uint16_t *kgammas, uint8_t *vcodes, uint16_t *vnorms, uint16_t *vgammas, int vlayout,
+                          int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!kq || !vq || !valid_dtype(xt)) return TQ_ERR_INVALID;
+  if (kq->d > tq::APPEND_DMAX_HOST) return TQ_ERR_UNSUPPORTED;
+  if (B > 0 && (Tstride <= 0 || !k_new || !v_new)) return TQ_ERR_INVALID;
+  tq::AppendArgs app{};
+  app.on = 1;
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.xt = xt;
+  app.d = kq->d;
+  app.Hkv = Hkv;
+  app.vlayout = vlayout;
+  app.Tstride = Tstride;
+  app.seq_len = seq_len;
+  app.kcodes = kcodes;
+  app.knorms = knorms;
+  app.kgammas = kgammas;
+  app.vcodes = vcodes;
+  app.vnorms = vnorms;
+  app.vgammas = vgammas;
+  auto side = [](const tq_quantizer *z, tq::AppendSide &sd) {
+    sd.bm = z->bmse;
+    sd.prod = z->mode == TQ_PROD ? 1 : 0;
+    sd.piT = z->piT;
+    sd.pi = z->pi;
+    sd.sT = z->sT;
+    for (int k = 0; k < (1 << z->bmse); ++k) sd.c[k] = z->c64[k];
+    for (int k = 0; k + 1 < (1 << z->bmse); ++k) sd.t[k] = z->t64[k];
+  };
+  side(kq, app.k);
+  side(vq, app.v);
+  return attn_decode_impl(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, vlayout,
+                          Tstride, seq_len, scale, out, ws, ws_bytes, &app, stream);
 }
 
 }  // extern "C"

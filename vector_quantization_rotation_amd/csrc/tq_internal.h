@@ -18,6 +18,35 @@ struct Codebook {
   float t[kMaxCentroids - 1];     // boundaries (midpoints)
 };
 
+constexpr int APPEND_DMAX_HOST = 512;  // head dims the decode-step append handles
+
+// Decode-step append (the new token's key and value encoded into the cache by the step's query
+// preparation kernel): one side (key or value) of the encoding.
+struct AppendSide {
+  int bm;            // index bits (0 for the 1-bit sign mode)
+  int prod;          // Algorithm 2: a sign plane and a gamma follow the index planes
+  const float *piT;  // Pi^T (y = Pi x reads it column-wise, coalesced)
+  const float *pi;   // Pi (z = Pi^T c reads it column-wise)
+  const float *sT;   // S^T (Algorithm 2)
+  double t[kMaxCentroids - 1];
+  double c[kMaxCentroids];
+};
+
+// everything the append reads and writes
+struct AppendArgs {
+  int on;                      // 0: a plain decode step
+  const void *k_new, *v_new;   // [B, Hkv, d] of type xt
+  int xt, d, Hkv;
+  int vlayout;                 // TQ_LAYOUT_ROWS or TQ_LAYOUT_TILE32
+  int64_t Tstride;
+  const int32_t *seq_len;      // position of the new token (tokens already cached)
+  uint8_t *kcodes;
+  uint16_t *knorms, *kgammas;  // kgammas for Algorithm-2 keys
+  uint8_t *vcodes;             // rows, or uint32 tile words (TQ_LAYOUT_TILE32)
+  uint16_t *vnorms, *vgammas;
+  AppendSide k, v;
+};
+
 }  // namespace tq
 
 struct tq_quantizer {
@@ -73,9 +102,15 @@ int run_score(const tq_quantizer *q, const float *queries, int64_t m, int64_t ld
               void *ws, size_t ws_bytes, hipStream_t st);
 size_t attn_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, int64_t Tstride, int vlayout);
 int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
-                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint8_t *vcodes,
-                    const uint16_t *vnorms, const uint16_t *vgammas, int vlayout, int64_t Tstride,
-                    const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+                    int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                    const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                    int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes,
+                    const AppendArgs *app, hipStream_t st);
+size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride);
+int run_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
+                     int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride,
+                     const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st);
 int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
                      hipStream_t st);
 int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
