@@ -237,6 +237,22 @@ int tq_attn_decode_append(const tq_quantizer *kq, const tq_quantizer *vq, const 
                           int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* tq_attn_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments and result as tq_attn_decode
+ * without ws/ws_bytes: the workspace is a device array of TQ_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU, held until the process ends.  The call allocates nothing; its first call on
+ * a device looks up that device's array once.
+ *   Returns TQ_ERR_WORKSPACE, launching nothing, when tq_attn_decode_ws_bytes(kq, B, Hq, Hkv,
+ *   Tstride, vlayout) exceeds TQ_NOALLOC_SCRATCH_BYTES; TQ_ERR_INVALID when the current device is
+ *   not the quantizer's.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other streams or
+ * threads) race and must be ordered by the caller.  Nothing in the array needs to start at zero. */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_attn_decode_noalloc(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,
+                           int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
+                           const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                           int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *stream);
+
 /* Optional per-kernel timing.  When enabled, the library records a pair of
  * HIP events on the launch stream around every kernel it launches (a few
  * microseconds of overhead per launch); disabled by default.

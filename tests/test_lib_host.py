@@ -108,6 +108,7 @@ def test_entry_points_reject_null_quantizer():
     assert lib.tq_decode(z, z, z, z, 1, z, 128, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_score(z, z, 1, 128, z, z, z, 1, 0, z, z, z, 0, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_attn_decode(z, z, z, 1, 1, 4, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
+    assert lib.tq_attn_decode_noalloc(z, z, z, 1, 1, 4, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_attn_decode_ws_bytes(z, 1, 4, 1, 16, 0) == 0
     assert lib.tq_attn_prefill(z, z, z, 1, 1, 4, 4, 1, z, z, z, z, z, z, 0, 16, z, 1.0, z, z, 0, z) == _lib.TQ_ERR_INVALID
     assert lib.tq_attn_prefill_ws_bytes(z, 1, 4, 4, 1, 16, 0) == 0

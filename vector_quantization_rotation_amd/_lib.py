@@ -18,6 +18,7 @@ TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP, TQ_ERR_NOMEM, TQ_ERR_WORK
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_LAYOUT_ROWS, TQ_LAYOUT_TILE32 = 0, 1
+TQ_NOALLOC_SCRATCH_BYTES = 16 << 20  # the library's fixed workspace of tq_attn_decode_noalloc
 
 # (name, restype, argtypes) for every symbol declared in include/tq.h
 _P, _I, _I64, _SZ, _F, _D = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_float, C.c_double
@@ -34,6 +35,7 @@ SIGNATURES = [
     ("tq_tile_records", _I, [_P, _P, _I64, _I64, _P, _P]),
     ("tq_attn_decode", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ, _P]),
     ("tq_attn_decode_ws_bytes", _SZ, [_P, _I, _I, _I, _I64, _I]),
+    ("tq_attn_decode_noalloc", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P]),
     ("tq_attn_prefill", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ,
                              _P]),
     ("tq_attn_prefill_ws_bytes", _SZ, [_P, _I, _I, _I, _I, _I64, _I]),

@@ -305,6 +305,28 @@ def attn_decode_append(kq: Quantizer, vq: Quantizer, q: torch.Tensor, k_new: tor
     return out
 
 
+def attn_decode_noalloc(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
+                        seq_len: torch.Tensor, scale: float, out: torch.Tensor, vlayout: int = TQ_LAYOUT_ROWS,
+                        kgammas=None):
+    """attn_decode through tq_attn_decode_noalloc: no device allocation anywhere in the call (out is
+    the caller's); the workspace is the library's fixed per-GPU array of TQ_NOALLOC_SCRATCH_BYTES.
+    Calls that overlap on one GPU race on that array."""
+    lib = load()
+    B, Hq, Hkv, Tstride, d, dev = _attn_args(kq, vq, q, kcodes, knorms, vcodes, vnorms, vgammas, seq_len, out, vlayout,
+                                             kgammas)
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    need = lib.tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
+    if need > _lib.TQ_NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"this call needs {need} bytes of workspace; the no-allocation entry point holds "
+                         f"{_lib.TQ_NOALLOC_SCRATCH_BYTES}")
+    rc = lib.tq_attn_decode_noalloc(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, Hq, Hkv, _ptr(kcodes),
+                                    _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout,
+                                    Tstride, _ptr(seq_len), float(scale), _ptr(out), _stream())
+    _lib._check("tq_attn_decode_noalloc", rc)
+    return out
+
+
 def attn_decode_bound(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
                       seq_len: torch.Tensor, scale: float, out: torch.Tensor, ws: torch.Tensor,
                       vlayout: int = TQ_LAYOUT_ROWS, kgammas=None):
