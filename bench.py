@@ -29,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # dense MFMA, MI355X
+INT8_PEAK_TOPS = 5000.0
 
 
 def log(*a):
@@ -42,6 +44,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
+    ap.add_argument("--cpu-encode-rows", type=int, default=524288, help="rows per kind the oracle encodes")
+    ap.add_argument("--only", choices=["", "encode", "attention"], default="",
+                    help="a short run of one part (for counter profiles): the one-layer encode, or the timed "
+                         "attention steps")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
@@ -70,6 +76,30 @@ def measured_traffic():
     return int(kv["traffic bytes per launch"])
 
 
+def encode_only(steps: int):
+    """The one-layer encode workload (keys Algorithm 1 3-bit, values Algorithm 2 3-bit, 2 x 2^21 bf16 rows of
+    d 128) run `steps` times, for counter profiles of the encode kernels; prints one JSON line."""
+    import torch
+    from vector_quantization_rotation_amd import api, synth
+    d, eB, eH, eT = 128, 8, 8, 32768
+    ch = synth.outlier_channels(eH, d, 4, 203)
+    K = synth.kv_bf16_torch((eB, eH, eT, d), 201, ch, "cuda").view(-1, d)
+    V = synth.kv_bf16_torch((eB, eH, eT, d), 202, ch, "cuda").view(-1, d)
+    kq = api.Quantizer(d, 3, api.TQ_MSE, synth.haar_rotation(d, 211))
+    vq = api.Quantizer(d, 3, api.TQ_PROD, synth.haar_rotation(d, 212), synth.gaussian_projection(d, 213))
+    kc, kn, _ = kq.encode(K)
+    vc, vn, vg = vq.encode(V)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        kq.encode(K, codes=kc, norms=kn)
+        vq.encode(V, codes=vc, norms=vn, gammas=vg)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"encode": {"ms": round(dt * 1e3, 4), "vectors": 2 * K.shape[0],
+                                 "value": round(2 * K.shape[0] / dt, 1), "unit": "vectors/s"}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -85,6 +115,9 @@ def main():
         sys.exit(1)
     api.load()
     torch.cuda.set_device(0)
+    if args.only == "encode":
+        encode_only(args.steps)
+        return
 
     # ---------------- decode attention (timed steps) ----------------
     from vector_quantization_rotation_amd import workloads
@@ -122,7 +155,7 @@ def main():
     # timed region: HIP events around the dominant kernel only (events around every launch of the step
     # add a few microseconds each to the step's wall time)
     _lib.profile_reset()
-    _lib.profile_select("attn_split")
+    _lib.profile_select("attn_wave")
     _lib.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -131,7 +164,18 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     _lib.profile_enable(False)
-    split_ms, split_n = _lib.profile_query("attn_split")
+    split_ms, split_n = _lib.profile_query("attn_wave")
+    kernel_name = "attn_wave_kernel<3>"
+    if split_n == 0:  # the 4-wave kernel ran (a shape the wave-streaming kernel does not take)
+        kernel_name = "attn_fast_kernel<128,3,1>"
+        _lib.profile_reset()
+        _lib.profile_select("attn_fast")
+        _lib.profile_enable(True)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        _lib.profile_enable(False)
+        split_ms, split_n = _lib.profile_query("attn_fast")
     # every kernel of the step, from a short pass outside the timed region
     _lib.profile_select("")
     _lib.profile_reset()
@@ -146,9 +190,13 @@ def main():
     value = packed / (ms_per_step * 1e-3) / 1e9
     kernel_ms = split_ms / max(split_n, 1)
     achieved = packed / (kernel_ms * 1e-3) / 1e9
-    log(f"attention: {ms_per_step:.4f} ms/step, {value:.1f} GB/s; split kernel {kernel_ms:.4f} ms "
+    log(f"attention: {ms_per_step:.4f} ms/step, {value:.1f} GB/s; {kernel_name} {kernel_ms:.4f} ms "
         f"({achieved:.1f} GB/s); attn kernels total {all_ms / args.steps:.4f} ms/step (untimed pass)")
     out_gpu = out.cpu().numpy()
+    if args.only == "attention":
+        print(json.dumps({"attention": {"ms_per_step": round(ms_per_step, 5), "value": round(value, 2),
+                                        "kernel": kernel_name, "kernel_ms": round(kernel_ms, 5)}}), flush=True)
+        return
 
     # ---------------- encode throughput (one layer's cache) ----------------
     eB, eH, eT = 8, 8, 32768
@@ -181,6 +229,12 @@ def main():
     enc_prod_ms, enc_prod_n = _lib.profile_query("encode_prod")
     enc_bytes = 2 * nvec * d * 2 + ek[0].numel() + 2 * nvec + ev[0].numel() + 4 * nvec
     enc_vps = 2 * nvec / edt
+    # matrix-core work the fused kernels execute: exact bf16 pieces, 3 products per rotation of a bf16
+    # row, 6 per QJL projection of the fp32 residual (d x d each), 2 flop per product term
+    enc_flop_exec = 2.0 * nvec * d * d * (3 + 3 + 6)
+    enc_flop_useful = 2.0 * nvec * d * d * (1 + 1 + 1)  # one pass per rotation / projection
+    enc_hbm_ms = enc_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    enc_mfma_ms = enc_flop_exec / (BF16_PEAK_TFLOPS * 1e12) * 1e3
     log(f"encode: {edt * 1e3:.3f} ms for {2 * nvec} vectors = {enc_vps:.3e} vectors/s, {enc_bytes / edt / 1e9:.1f} GB/s; "
         f"kernels mse {enc_mse_ms / max(enc_mse_n, 1):.4f} ms, prod {enc_prod_ms / max(enc_prod_n, 1):.4f} ms")
     del Ke, Ve
@@ -250,17 +304,46 @@ def main():
     sn = torch.empty((SS["n"],), dtype=torch.int16, device="cuda")
     sg = torch.empty((SS["n"],), dtype=torch.int16, device="cuda")
     s_enc = timed(lambda: sq.encode(X, codes=sc, norms=sn, gammas=sg))
-    del X
+    Qh = workloads.search_queries()
+    Qs = torch.from_numpy(Qh).cuda()
+    # exact top-k of sampled queries by fp64 inner products over every row (for recall@k)
+    rq = np.sort(np.random.default_rng(13).choice(SS["queries"], size=16, replace=False))
+    exact = (Qs[torch.as_tensor(rq, device="cuda")].double() @ X.double().T)
+    ex_idx = torch.topk(exact, SS["k"], dim=1).indices.cpu().numpy()
+    del X, exact
     torch.cuda.empty_cache()
-    Qs = torch.from_numpy(workloads.search_queries()).cuda()
     s_scan = timed(lambda: sq.score(Qs, sc, sn, sg, k=SS["k"]))
+    _lib.profile_reset()
+    _lib.profile_select("score_scan")
+    _lib.profile_enable(True)
+    _, s_idx = sq.score(Qs, sc, sn, sg, k=SS["k"])
+    torch.cuda.synchronize()
+    _lib.profile_enable(False)
+    _lib.profile_select("")
+    scan_ms, scan_n = _lib.profile_query("score_scan")
+    scan_ms /= max(scan_n, 1)
+    got = s_idx.cpu().numpy()[rq]
+    recall = float(np.mean([len(set(got[i]) & set(ex_idx[i])) / SS["k"] for i in range(len(rq))]))
     s_bytes = int(sc.numel() + 4 * SS["n"])
+    # int8 matrix-core work of the scan kernel: per (32 queries x 256 records) tile and 64 coordinates,
+    # 5 images x 2 digit rows of 16x16x64 products; useful work: one multiply-add per (query, row, coordinate)
+    # on each of the 4 bit planes
+    scan_ops_exec = (SS["queries"] / 32) * (SS["n"] / 256) * (SS["d"] / 64) * 5 * 16 * (2 * 16 * 16 * 64)
+    scan_ops_useful = 2.0 * SS["queries"] * SS["n"] * SS["d"] * SS["bits"]
+    scan_bound_ms = scan_ops_exec / (INT8_PEAK_TOPS * 1e12) * 1e3
     search = {"workload": f"{SS['n']} x d{SS['d']} clustered, prod {SS['bits']}-bit, {SS['queries']} queries, top-{SS['k']}",
               "encode_ms": round(s_enc * 1e3, 3), "encode_vectors_per_s": round(SS["n"] / s_enc, 1),
               "scan_topk_ms": round(s_scan * 1e3, 3), "queries_per_s": round(SS["queries"] / s_scan, 1),
-              "pairs_per_s": round(SS["queries"] * SS["n"] / s_scan, 1), "packed_db_bytes": s_bytes}
+              "pairs_per_s": round(SS["queries"] * SS["n"] / s_scan, 1), "packed_db_bytes": s_bytes,
+              "recall_at_k": round(recall, 4), "recall_queries": len(rq),
+              "scan_kernel_ms": round(scan_ms, 4),
+              "scan_roofline": {"bound": "mfma", "ops_executed": scan_ops_exec, "ops_useful": scan_ops_useful,
+                                "bound_ms": round(scan_bound_ms, 4), "frac": round(scan_bound_ms / scan_ms, 4),
+                                "frac_useful": round(scan_ops_useful / (INT8_PEAK_TOPS * 1e12) * 1e3 / scan_ms, 4),
+                                "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8 dense)"}}
     log(f"search: encode {s_enc * 1e3:.2f} ms ({SS['n'] / s_enc:.3e} vectors/s); scan+top-{SS['k']} "
-        f"{s_scan * 1e3:.2f} ms for {SS['queries']} queries ({SS['queries'] * SS['n'] / s_scan:.3e} pairs/s)")
+        f"{s_scan * 1e3:.2f} ms for {SS['queries']} queries ({SS['queries'] * SS['n'] / s_scan:.3e} pairs/s); "
+        f"scan kernel {scan_ms:.3f} ms; recall@{SS['k']} over {len(rq)} queries {recall:.3f}")
     del sc, sn, sg, Qs
     torch.cuda.empty_cache()
 
@@ -321,6 +404,58 @@ def main():
                "host_cpus": os.cpu_count()}
         parity = {"max_rel_err": max(errs), "tolerance": 2e-3, "slices": slices}
         log(f"cpu oracle: {cpu['value']} GB/s over {t_cpu:.1f}s; parity max rel err {max(errs):.2e}")
+        # the oracle's encode of a sample of the one-layer encode workload (same law and seeds)
+        nenc = args.cpu_encode_rows
+        Ks = synth.kv_bf16_torch((eB, eH, eT, d), 201, echans, "cuda").view(-1, d)[:nenc].float().cpu().numpy()
+        Vs = synth.kv_bf16_torch((eB, eH, eT, d), 202, echans, "cuda").view(-1, d)[:nenc].float().cpu().numpy()
+        piKe, piVe, sVe = synth.haar_rotation(d, 211), synth.haar_rotation(d, 212), synth.gaussian_projection(d, 213)
+        cK, tK = oracle.lloyd_max(d, 3)
+        cV, tV = oracle.lloyd_max(d, 2)
+        t1 = time.perf_counter()
+        oracle.encode_mse(Ks, piKe, cK, tK)
+        oracle.encode_prod(Vs, piVe, sVe, cV, tV)
+        t_enc = time.perf_counter() - t1
+        cpu["encode"] = {"value": round(2 * nenc / t_enc, 1), "unit": "vectors/s", "cores": int(blas_threads),
+                         "sample": f"{nenc} key rows (Algorithm 1, 3-bit) + {nenc} value rows (Algorithm 2, 3-bit) "
+                                   f"of the one-layer encode workload, fp64 oracle, {t_enc:.1f}s"}
+        log(f"cpu oracle encode: {2 * nenc / t_enc:.3e} vectors/s over {t_enc:.1f}s")
+
+    # ---------------- decode step with the new token appended (same shape) ----------------
+    # the token goes into the last slot of every sequence (position T - 1) and the step attends all T
+    # tokens; run after the oracle's sample, since it rewrites that slot
+    kn_new = synth.kv_bf16_torch((B, Hkv, 1, d), 711, synth.outlier_channels(Hkv, d, 4, 712), "cuda").view(B, Hkv, d)
+    vn_new = synth.kv_bf16_torch((B, Hkv, 1, d), 713, synth.outlier_channels(Hkv, d, 4, 712), "cuda").view(B, Hkv, d)
+    seq_app = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+
+    def app_step():
+        api.attn_decode_append(kq, vq, q, kn_new, vn_new, kc, kn, vt, vn, vg, seq_app, scale, out=out, ws=ws,
+                               vlayout=layout)
+
+    app_dt = timed(app_step, reps=args.steps)
+    plain_dt = timed(step, reps=args.steps)
+    append = {"ms_per_step": round(app_dt * 1e3, 4), "plain_step_ms": round(plain_dt * 1e3, 4),
+              "overhead_ms": round((app_dt - plain_dt) * 1e3, 4),
+              "workload": f"decode step that encodes one new key and value per (batch, kv head) into the cache at "
+                          f"position {T - 1} and attends {T} tokens; B {B}, {Hq} query heads over {Hkv} kv heads, "
+                          f"d{d}, keys mse 3-bit, values prod 2-bit (token-tiled)"}
+    log(f"append step: {app_dt * 1e3:.4f} ms (plain step {plain_dt * 1e3:.4f} ms)")
+
+    # ---------------- chunked prefill: 512 query tokens against a 4096-token cache ----------------
+    pB, pM, pT = 1, 512, 4096
+    pc = workloads.build_attention_cache(pB, Hq, Hkv, pT, d, tiles=False)
+    pq = torch.randn((pB, pM, Hq, d), generator=torch.Generator("cuda").manual_seed(721), device="cuda").to(torch.bfloat16)
+    qpos = torch.full((pB,), pT - pM, dtype=torch.int32, device="cuda")
+    pout = torch.empty((pB, pM, Hq, d), dtype=torch.float32, device="cuda")
+    pws = torch.empty((_lib.load().tq_attn_prefill_ws_bytes(pc.kq.handle, pB, pM, Hq, Hkv, pT, 0),), dtype=torch.uint8,
+                      device="cuda")
+    pre_dt = timed(lambda: api.attn_prefill(pc.kq, pc.vq, pq, pc.kcodes, pc.knorms, pc.vcodes, pc.vnorms, pc.vgammas,
+                                            qpos, scale, out=pout, ws=pws), reps=5)
+    prefill = {"ms": round(pre_dt * 1e3, 4), "query_tokens_per_s": round(pB * pM / pre_dt, 1),
+               "workload": f"{pM} query tokens (causal, positions {pT - pM}..{pT - 1}) x {Hq} heads over {Hkv} kv heads, "
+                           f"d{d}, against a {pT}-token row-record cache (keys mse 3-bit, values prod 2-bit)",
+               "kernel": "attn_split_kernel (row records, one wave per 16 query rows)"}
+    log(f"prefill: {pre_dt * 1e3:.3f} ms for {pM} query tokens")
+    del pc, pq, pout, pws
 
     res = {
         "metric": "packed-KV GB/s in compressed decode attention (% HBM peak); encode vectors/s",
@@ -342,16 +477,25 @@ def main():
                    "packed_bytes": int(packed), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_split", "kernel_ms": round(kernel_ms, 5)},
+                     "kernel": kernel_name, "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
         "encode": {"value": round(enc_vps, 1), "unit": "vectors/s", "ms": round(edt * 1e3, 4),
                    "vectors": 2 * nvec, "gbs": round(enc_bytes / edt / 1e9, 2),
                    "mse_kernel_ms": round(enc_mse_ms / max(enc_mse_n, 1), 5),
                    "prod_kernel_ms": round(enc_prod_ms / max(enc_prod_n, 1), 5),
-                   "workload": "one layer: batch 8 x 8 kv heads x 32768 tokens x d128; K mse 3-bit + V prod 3-bit"},
+                   "workload": "one layer: batch 8 x 8 kv heads x 32768 tokens x d128; K mse 3-bit + V prod 3-bit",
+                   "roofline": {"hbm": {"bytes": int(enc_bytes), "bound_ms": round(enc_hbm_ms, 4),
+                                        "frac": round(enc_hbm_ms / (edt * 1e3), 4), "peak": HBM_PEAK_GBS,
+                                        "unit": "GB/s"},
+                                "mfma": {"flop_executed": enc_flop_exec, "flop_useful": enc_flop_useful,
+                                         "bound_ms": round(enc_mfma_ms, 4),
+                                         "frac": round(enc_mfma_ms / (edt * 1e3), 4), "peak": BF16_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s (bf16 dense)"}}},
         "decode": decode,
         "heterogeneous_layers": het,
         "search": search,
+        "append": append,
+        "prefill": prefill,
         "parity_sample": parity,
     }
     print(json.dumps(res), flush=True)

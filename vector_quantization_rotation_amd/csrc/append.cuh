@@ -18,6 +18,7 @@ constexpr int APPEND_THREADS = 256;
 
 struct AppendShared {
   double x[APPEND_DMAX], y[APPEND_DMAX], r[APPEND_DMAX];
+  double part[APPEND_THREADS / 64][APPEND_DMAX];  // per-wave partial sums of a matrix-vector product
   int idx[APPEND_DMAX];
   uint8_t bits[5][APPEND_DMAX];  // [plane][coordinate]
   double red[APPEND_THREADS / 64];
@@ -35,6 +36,50 @@ __device__ __forceinline__ double append_block_sum(double v, AppendShared &sh) {
   return s;
 }
 
+// one pass of append_matvec over NB column blocks of 64 starting at c0: every load is unconditional (the
+// block count is uniform), so a batch of RB rows x NB columns is in flight at once
+template <int NB>
+__device__ inline void append_matvec_pass(const float *A, const double *v, int d, int c0, AppendShared &sh) {
+  constexpr int RB = NB <= 2 ? 16 : 8;  // rows per batch (a wave's row count d / 4 is a multiple of 16)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rows = d / 4, r0 = w * rows;
+  double acc[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) acc[cb] = 0.0;
+  for (int r = r0; r < r0 + rows; r += RB) {
+    float a[RB][NB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) a[u][cb] = A[(int64_t)(r + u) * d + c0 + 64 * cb + lane];
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) acc[cb] = fma((double)a[u][cb], v[r + u], acc[cb]);
+  }
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) sh.part[w][c0 + 64 * cb + lane] = acc[cb];
+}
+
+// y[col] = sum_row A[row d + col] v[row] in fp64 (A a d x d fp32 matrix in global memory, d a multiple of
+// 64; v and y in LDS): wave w sums the rows w d/4 .. (w+1) d/4 for every column, each lane 64 columns
+// apart, up to four column blocks per pass; the four partial sums are added through LDS.  Ends with a
+// barrier.
+__device__ inline void append_matvec(const float *A, const double *v, double *y, int d, AppendShared &sh) {
+  const int nb = d / 64;
+  for (int c0 = 0; c0 < d; c0 += 4 * 64) {
+    const int cnt = nb - c0 / 64 < 4 ? nb - c0 / 64 : 4;  // uniform across the work-group
+    if (cnt == 1) append_matvec_pass<1>(A, v, d, c0, sh);
+    else if (cnt == 2) append_matvec_pass<2>(A, v, d, c0, sh);
+    else if (cnt == 3) append_matvec_pass<3>(A, v, d, c0, sh);
+    else append_matvec_pass<4>(A, v, d, c0, sh);
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < d; col += APPEND_THREADS)
+    y[col] = (sh.part[0][col] + sh.part[1][col]) + (sh.part[2][col] + sh.part[3][col]);
+  __syncthreads();
+}
+
 // one vector (already in sh.x, d coordinates): its plane bits into sh.bits, its fp16 norm and gamma
 __device__ inline void append_encode(const AppendSide &sd, int d, AppendShared &sh, uint16_t &nh_out,
                                      uint16_t &gm_out) {
@@ -44,11 +89,10 @@ __device__ inline void append_encode(const AppendSide &sd, int d, AppendShared &
   const double n = sqrt(append_block_sum(ss, sh));
   const int L = 1 << sd.bm;
   // y_j = (Pi x)_j = sum_k Pi^T[k][j] x_k
+  append_matvec(sd.piT, sh.x, sh.y, d, sh);
   for (int j = tid; j < d; j += APPEND_THREADS) {
-    double acc = 0.0;
-    for (int k = 0; k < d; ++k) acc = fma((double)sd.piT[(int64_t)k * d + j], sh.x[k], acc);
     // idx_j = #{k : t_k n < y_j}; the zero vector compares y = 0 against t_k
-    const double yy = n > 0.0 ? acc : 0.0, nn = n > 0.0 ? n : 1.0;
+    const double yy = n > 0.0 ? sh.y[j] : 0.0, nn = n > 0.0 ? n : 1.0;
     int idx = 0;
     for (int k = 0; k + 1 < L; ++k) idx += (sd.t[k] * nn < yy) ? 1 : 0;
     sh.idx[j] = idx;
@@ -60,23 +104,21 @@ __device__ inline void append_encode(const AppendSide &sd, int d, AppendShared &
   if (!sd.prod) return;
   __syncthreads();  // every index is in sh.idx
   const double nhd = (double)f16_to_f32(nh);
-  // r = x - n_hat Pi^T c[idx]:  (Pi^T c)_k = sum_j Pi[j][k] c[idx_j]
+  // r = x - n_hat Pi^T c[idx]:  (Pi^T c)_k = sum_j Pi[j][k] c[idx_j]  (c[idx_j] staged in sh.r)
+  for (int j = tid; j < d; j += APPEND_THREADS) sh.r[j] = sd.c[sh.idx[j]];
+  __syncthreads();
+  append_matvec(sd.pi, sh.r, sh.y, d, sh);
   double rs = 0.0;
   for (int k = tid; k < d; k += APPEND_THREADS) {
-    double z = 0.0;
-    for (int j = 0; j < d; ++j) z = fma((double)sd.pi[(int64_t)j * d + k], sd.c[sh.idx[j]], z);
-    const double r = sh.x[k] - nhd * z;
+    const double r = sh.x[k] - nhd * sh.y[k];
     sh.r[k] = r;
     rs = fma(r, r, rs);
   }
   const double rn = sqrt(append_block_sum(rs, sh));  // (the block sum's barriers order the sh.r writes)
   gm_out = f64_to_f16_rne_sat(rn);
   // sign bit i = [(S r)_i >= 0]:  (S r)_i = sum_k S^T[k][i] r_k
-  for (int i = tid; i < d; i += APPEND_THREADS) {
-    double acc = 0.0;
-    for (int k = 0; k < d; ++k) acc = fma((double)sd.sT[(int64_t)k * d + i], sh.r[k], acc);
-    sh.bits[sd.bm][i] = acc >= 0.0 ? 1 : 0;
-  }
+  append_matvec(sd.sT, sh.r, sh.y, d, sh);
+  for (int i = tid; i < d; i += APPEND_THREADS) sh.bits[sd.bm][i] = sh.y[i] >= 0.0 ? 1 : 0;
 }
 
 __device__ inline void append_load(const void *src, int xt, int64_t off, int d, AppendShared &sh) {
@@ -115,25 +157,27 @@ __device__ inline void append_write_tiles(uint32_t *seq_tiles, int64_t t, int pl
   }
 }
 
-// the work-group's (b, g): key, then value, into the cache at t = seq_len[b] (nothing when t is outside
-// [0, Tstride))
-__device__ inline void append_token(const AppendArgs &a, int b, int g, AppendShared &sh) {
+// the new key (which = 0) or value (which = 1) of (b, g) into the cache at t = seq_len[b] (nothing when
+// t is outside [0, Tstride)); the two are encoded by different work-groups of the same launch
+__device__ inline void append_token(const AppendArgs &a, int b, int g, int which, AppendShared &sh) {
   const int64_t t = a.seq_len[b];
   if (t < 0 || t >= a.Tstride) return;
   const int d = a.d;
   const int64_t seq = (int64_t)b * a.Hkv + g;
   const int64_t row = seq * a.Tstride + t;
   uint16_t nh, gm;
-  append_load(a.k_new, a.xt, seq * d, d, sh);
-  append_encode(a.k, d, sh, nh, gm);
-  __syncthreads();
-  const int kplanes = a.k.bm + a.k.prod;
-  append_write_row(a.kcodes + row * (int64_t)(kplanes * d / 8), kplanes, d, sh);
-  if (threadIdx.x == 0) {
-    a.knorms[row] = nh;
-    if (a.k.prod) a.kgammas[row] = gm;
+  if (which == 0) {
+    append_load(a.k_new, a.xt, seq * d, d, sh);
+    append_encode(a.k, d, sh, nh, gm);
+    __syncthreads();
+    const int kplanes = a.k.bm + a.k.prod;
+    append_write_row(a.kcodes + row * (int64_t)(kplanes * d / 8), kplanes, d, sh);
+    if (threadIdx.x == 0) {
+      a.knorms[row] = nh;
+      if (a.k.prod) a.kgammas[row] = gm;
+    }
+    return;
   }
-  __syncthreads();  // the key's bits are written before the value's overwrite them
   append_load(a.v_new, a.xt, seq * d, d, sh);
   append_encode(a.v, d, sh, nh, gm);
   __syncthreads();

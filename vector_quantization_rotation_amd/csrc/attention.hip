@@ -57,16 +57,18 @@ size_t partial_floats(int d) { return 2 + 2 * (size_t)d; }
 }  // namespace
 
 // q'[b,h,:] = Pi_K q[b,h,:] into qrot[bh][0..d), and for Algorithm-2 keys (sT not null) also
-// S_K q[b,h,:] into qrot[bh][d..2d); ld = d or 2d.  A decode step that appends a token (app.on) has it
-// encoded into the cache by the work-group of the first query head of each kv head.
+// S_K q[b,h,:] into qrot[bh][d..2d); ld = d or 2d.  A decode step that appends a token (app.on) has its
+// key and value encoded into the cache by the work-groups of the first two query heads of each kv head.
 template <int QT>
 __global__ __launch_bounds__(256) void attn_qrot_kernel(const void *q, int d, const float *piT, const float *sT,
                                                         int ld, float *qrot, int Hq, int G, AppendArgs app) {
   extern __shared__ float sq[];
   const int64_t bh = blockIdx.x;
-  if (app.on && (bh % Hq) % G == 0) {
+  if (app.on && (bh % Hq) % G < 2) {  // the key by the group's first query head, the value by its second
     __shared__ AppendShared app_sh;
-    append_token(app, (int)(bh / Hq), (int)((bh % Hq) / G), app_sh);
+    const int b = (int)(bh / Hq), g = (int)((bh % Hq) / G), which = (int)((bh % Hq) % G);
+    append_token(app, b, g, which, app_sh);
+    if (G == 1) append_token(app, b, g, 1, app_sh);  // one head per kv head: this work-group does both
   }
   for (int j = threadIdx.x; j < d; j += 256) {
     float v;

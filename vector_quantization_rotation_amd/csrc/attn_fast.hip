@@ -162,7 +162,9 @@ __device__ __forceinline__ void fa_load_values(uint32_t (&vw)[4][D / 64][VB + 1]
 // the reference carries few significant bits.  When every score of a head in a whole step lies more
 // than REF_DROP below the reference and the current fold segment is at least the kernel's minimum
 // length, the reference moves down to that step's maximum (a fold), so that a long tail behind one
-// dominant token is weighed on a grid set by its own scale.  The reference never goes more than
+// dominant token is weighed on a grid set by its own scale.  The minimum length adapts: an upward
+// move within twice that many steps of a downward one (scores that spread widely rather than a long
+// low tail) doubles it, up to the kernel's maximum, so the moves stay rare where they buy nothing.  The reference never goes more than
 // REF_SPAN below the highest score of the chunk, m_top (tokens further down weigh below 2^-REF_SPAN of
 // that token): every weight is then at most 2^(REF_SPAN + slack) and a running sum over fewer than
 // 2^31 tokens stays below 2^80 (fp32 has room to 2^128).
@@ -179,7 +181,8 @@ __device__ __forceinline__ float moved_reference(float m_ref, float smax, float 
 constexpr float FA_SLACK = 1.f;     // score headroom above the reference maximum (log2 units)
 constexpr float FA_NCAP = 1.25f;   // norm and gamma caps: this times the largest seen
 constexpr float FA_HEADROOM = 2.f;  // 2^FA_SLACK
-constexpr int FA_MINSEG = 2;        // fold segment length (256-token steps) before a downward move
+constexpr int FA_MINSEG = 2;        // fold segment length (256-token steps) before a downward move, at first
+constexpr int FA_MAXSEG = 32;       // ... and at most
 
 // D: head dim; KB: key index bits; VB: value index bits (Algorithm-2 records hold VB+1 planes)
 //
@@ -211,11 +214,16 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   __shared__ float s_kn[4][64];                                        // per wave: n_K
   __shared__ float s_max[4][FA_GMAX + 2];                              // per wave: score max per head, n_V max, gamma max
   __shared__ float s_merge[4][FA_GMAX][3];                             // per wave and head: l, Ym, Yq
-  __shared__ int s_flag[4];  // per wave: bit 0 a step value above the reference, bit 1 + h head h within REF_DROP
+  // per wave: bit 0 a score above the reference's headroom, bit 1 + h head h within REF_DROP of it, bit 5
+  // a norm or gamma above its cap
+  __shared__ int s_flag[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, split = blockIdx.y;
-  const int nbg = (int)gridDim.x / a.nsub;  // (batch, kv-head) pairs; units = nbg x head subgroups
+  // (batch, kv-head) pairs; units = nbg x head subgroups, the subgroup slowest: the work-groups of one
+  // pair's subgroups are nbg ids apart, so they land on the same XCD (work-groups go to the 8 XCDs
+  // round-robin by id) and share its L2 when nbg is a multiple of 8
+  const int nbg = (int)gridDim.x / a.nsub;
   const int sub = unit / nbg, bg = unit % nbg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int h0 = g * a.G + sub * FA_GMAX;
@@ -259,6 +267,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f;  // work-group uniform (m_ref per lane head)
   float m_top = -INFINITY;                              // highest score of the chunk so far (per head)
   int since_fold = 0;
+  int down_seg = FA_MINSEG;                             // segment length before a downward move
+  int since_down = 1 << 30;                             // steps since the last downward move
   float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;        // this lane's tokens, head hl
   float accf[VMP + 1][NTW];
   intx4 vacc[VMP + 1][NTW];
@@ -339,7 +349,8 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       fa_load_keys<D, KB>(kw, rk, vo_k, (int)(sn * KCB));
       fa_load_norms(nk, nv, ng, rkn, rvn, rvg, vo_n, (int)(sn * 2));
     }
-    bool over = fvn > vn_ref || fvg > vg_ref;
+    const bool over_n = fvn > vn_ref || fvg > vg_ref;
+    bool over = false;
     bool near = false;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -350,8 +361,9 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
       near = near || sc[grp] >= m_ref - REF_DROP;
     }
     const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0ull;  // every lane votes
+    const bool wave_over_n = __builtin_amdgcn_ballot_w64(over_n) != 0ull;
     const uint64_t wave_near = __builtin_amdgcn_ballot_w64(near);
-    int flag = wave_over ? 1 : 0;
+    int flag = (wave_over ? 1 : 0) | (wave_over_n ? 32 : 0);
 #pragma unroll
     for (int h = 0; h < FA_GMAX; ++h) flag |= ((wave_near >> (16 * h)) & 0xFFFFull) != 0 ? 2 << h : 0;
     if (lane == 0) s_flag[wave] = flag;
@@ -361,8 +373,11 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
     // reference, once the fold segment is FA_MINSEG steps long: move that reference down
     const bool whole = s0 + FA_SUB <= c1;
     ++since_fold;
-    const bool low = whole && since_fold >= FA_MINSEG && ((flags >> 1) & ((1 << gw) - 1)) != ((1 << gw) - 1);
-    if ((flags & 1) || low) {
+    ++since_down;
+    const bool low = whole && since_fold >= down_seg && ((flags >> 1) & ((1 << gw) - 1)) != ((1 << gw) - 1);
+    if ((flags & 33) || low) {
+      if ((flags & 1) && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, FA_MAXSEG);
+      if (low) since_down = 0;
       // ---- rare: move the reference to this step's maxima and fold the int32 accumulators ----
       float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       smax = rows16_max(smax);
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
         step_vg = fmaxf(step_vg, s_max[wv][FA_GMAX + 1]);
       }
       m_top = fmaxf(m_top, step_m);
-      const float m_new = moved_reference(m_ref, step_m, m_top, whole);
+      const float m_new = moved_reference(m_ref, step_m, m_top, low);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
 #pragma unroll
@@ -540,7 +555,8 @@ constexpr float WV_HEADROOM = 2.f;        // 2^WV_SLACK
 constexpr int WV_RING = 3;                // ring slots: stages s+1 and s+2 are in flight while s is used
 constexpr float WV_WMAX = 8388352.f;      // 2^23 - 256: weights are integers below 2^23 (see wv_weight)
 constexpr float WV_MAGIC = 8388608.f;     // 2^23
-constexpr int WV_MINSEG = 8;              // fold segment length (steps) before a downward move
+constexpr int WV_MINSEG = 8;              // fold segment length (steps) before a downward move, at first
+constexpr int WV_MAXSEG = 128;            // ... and at most
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -707,6 +723,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const uint32_t f4_ones = f4_ones_reg();
   const int kofs = 4 * (hl & 1);
   int since_fold = 0;
+  int down_seg = WV_MINSEG;   // segment length before a downward move
+  int since_down = 1 << 30;   // steps since the last downward move
   float sm_l = 0.f, sq_l = 0.f;  // weight scales WV_WMAX 2^-r / (largest n_V, gamma_V so far)
   float ism_l = 0.f, isq_l = 0.f;  // their inverses (0 while a scale is 0)
 
@@ -791,19 +809,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       mg = fmaxf(fmaxf(fvg[0], fvg[1]), fmaxf(fvg[2], fvg[3]));
     }
     const float dmax = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
-    uint64_t over = __builtin_amdgcn_ballot_w64(dmax > WV_SLACK) | __builtin_amdgcn_ballot_w64(mn > vn_ref) |
-                    __builtin_amdgcn_ballot_w64(mg > vg_ref);
+    const uint64_t up = __builtin_amdgcn_ballot_w64(dmax > WV_SLACK);
+    uint64_t over = up | __builtin_amdgcn_ballot_w64(mn > vn_ref) | __builtin_amdgcn_ballot_w64(mg > vg_ref);
     ++since_fold;
+    ++since_down;
+    bool down = false;
     if constexpr (WHOLE) {
-      if (since_fold >= WV_MINSEG) {
+      if (since_fold >= down_seg) {
         // a head (16 lanes) none of whose tokens comes within REF_DROP of the reference
         const uint64_t near = __builtin_amdgcn_ballot_w64(dmax >= -REF_DROP);
-        if ((near & 0xFFFFull) == 0 || (near & 0xFFFF0000ull) == 0 || (near & 0xFFFF00000000ull) == 0 ||
-            (near >> 48) == 0)
-          over = 1ull;
+        down = (near & 0xFFFFull) == 0 || (near & 0xFFFF0000ull) == 0 || (near & 0xFFFF00000000ull) == 0 ||
+               (near >> 48) == 0;
       }
     }
-    if (over != 0ull || since_fold >= 16384) {
+    if (over != 0ull || down || since_fold >= 16384) {
+      if (up != 0ull && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, WV_MAXSEG);
+      if (down) since_down = 0;
       // rare: move the reference to this step's maxima and fold the integer accumulators (the scores
       // are formed again from their parts, n_K read again: d holds +inf while the reference is -inf)
       float sct[4];
@@ -815,7 +836,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       const float vnm = wave_max_f32(mn);
       const float vgm = wave_max_f32(mg);
       m_top = fmaxf(m_top, smax);
-      const float m_new = moved_reference(m_ref, smax, m_top, WHOLE);
+      const float m_new = moved_reference(m_ref, smax, m_top, down);
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref * (WV_HEADROOM / WV_WMAX), iq = vg_ref * (WV_HEADROOM / WV_WMAX);
 #pragma unroll
@@ -984,7 +1005,8 @@ struct PrepArgs {
   float ctop;
   int *qimg;
   float *qinfo;
-  AppendArgs app;  // the decode step's new token (app.on), encoded by the work-group of head 0, subgroup 0
+  AppendArgs app;  // the decode step's new token (app.on): key and value encoded by the work-groups of heads 0
+                   // and 1 of subgroup 0
 };
 
 // four fixed-point digits of u (|u| <= 224) as e4m3 bytes: u = sum_d k_d Q_d + e with Q_d = 2^(4 - 5 d),
@@ -1026,9 +1048,9 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   const bool present = h < gw;  // a head past the group's end gets zero images and offsets
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  if (a.app.on && sub == 0 && h == 0) {
+  if (a.app.on && sub == 0 && h < 2) {  // the key by head 0's work-group, the value by head 1's
     __shared__ AppendShared app_sh;
-    append_token(a.app, b, g, app_sh);
+    append_token(a.app, b, g, h, app_sh);
   }
   for (int j = tid; j < D; j += 256) {
     float v = 0.f;
@@ -1295,7 +1317,7 @@ int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, 
   }
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
-  ProfScope ps("attn_split", st);
+  ProfScope ps("attn_fast", st);
   hipLaunchKernelGGL((attn_fast_kernel<D, KB, VB>), dim3(units, fp.nsplit), dim3(FA_THREADS), 0, st, fa);
   return launch_check();
 }
@@ -1365,7 +1387,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {
-      ProfScope ps("attn_split", st);
+      ProfScope ps("attn_wave", st);
       const dim3 grid((unsigned)units, (unsigned)fp.nsplit);
       if (KB == 1) hipLaunchKernelGGL(attn_wave_kernel<1>, grid, dim3(64), 0, st, fa);
       if (KB == 2) hipLaunchKernelGGL(attn_wave_kernel<2>, grid, dim3(64), 0, st, fa);
