@@ -131,6 +131,31 @@ int tq_encode_mse(const tq_quantizer *q, const void *x, int xt, int64_t n, int64
 int tq_encode_prod(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx,
                    uint8_t *codes, uint16_t *norms, uint16_t *gammas, void *stream);
 
+/* Encode nseq sequences of T vectors straight into a cache, by q's algorithm
+ * (TQ_MSE: Algorithm 1, TQ_PROD: Algorithm 2, with the arithmetic of
+ * tq_encode_mse / tq_encode_prod): row s*T + t of x becomes position t0 + t of
+ * sequence s.  This is the prompt (prefill) write of the decode cache that
+ * tq_attn_decode reads, in either of its layouts, with no separate tiling pass.
+ *   x:       device, nseq*T rows of d values of type xt, row stride ldx
+ *            elements (16-byte aligned rows)
+ *   t0, Tstride: first position written and positions per sequence of the
+ *            cache; t0 + T <= Tstride
+ *   layout:  TQ_LAYOUT_ROWS: codes = device [nseq][Tstride][code_bytes]
+ *            TQ_LAYOUT_TILE32: codes = device uint32 [nseq][ceil(Tstride/32)][planes][d];
+ *            t0 must be a multiple of 32; the words that hold positions
+ *            t0 .. t0+T-1 are written whole, positions from t0+T to the end of
+ *            the last such word as zero bits (a later tq_attn_decode_append
+ *            sets them); nseq <= 65535 (else TQ_ERR_UNSUPPORTED)
+ *   norms:   device [nseq][Tstride] fp16 bit patterns (positions t0.. written)
+ *   gammas:  device [nseq][Tstride], TQ_PROD only (ignored for TQ_MSE)
+ * Other positions of the cache are not touched.  TQ_ERR_INVALID for a null
+ * argument, a misaligned pointer or row stride, or positions outside the
+ * cache.  Head dims 64 and 128 write the cache from the encode kernel itself;
+ * other head dims stage the records in memory the call allocates on the stream
+ * and then move them into place. */
+int tq_encode_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx, int64_t t0,
+                    int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas, void *stream);
+
 /* Decode n records to fp32 rows.
  *   TQ_MSE : out = n_hat * Pi^T c[idx]
  *   TQ_PROD: out = n_hat * Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T (2 bits - 1)

@@ -29,6 +29,7 @@ SIGNATURES = [
     ("tq_quantizer_info", _I, [_P, C.POINTER(_I), C.POINTER(_I), C.POINTER(_I), C.POINTER(_I), C.POINTER(_SZ)]),
     ("tq_encode_mse", _I, [_P, _P, _I, _I64, _I64, _P, _P, _P]),
     ("tq_encode_prod", _I, [_P, _P, _I, _I64, _I64, _P, _P, _P, _P]),
+    ("tq_encode_cache", _I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
     ("tq_decode", _I, [_P, _P, _P, _P, _I64, _P, _I64, _P]),
     ("tq_score", _I, [_P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _P, _SZ, _P]),
     ("tq_score_ws_bytes", _SZ, [_P, _I64, _I64, _I]),

@@ -192,6 +192,45 @@ def tile_records(q: Quantizer, codes: torch.Tensor, out=None):
     return out
 
 
+def encode_cache(q: Quantizer, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, gammas=None, t0: int = 0,
+                 layout: int = TQ_LAYOUT_ROWS):
+    """Encode x [nseq, T, d] into positions t0 .. t0+T-1 of a cache of Tstride positions per sequence.
+
+    layout TQ_LAYOUT_ROWS: codes uint8 [nseq, Tstride, code_bytes]; TQ_LAYOUT_TILE32: codes int32
+    [nseq, ceil(Tstride/32), planes, d] (t0 a multiple of 32).  norms (and gammas for an Algorithm 2
+    quantizer) are fp16-bit [nseq, Tstride].  Writes in place; returns (codes, norms, gammas).
+    """
+    _need(x, "x", tuple(_DT), contiguous=False)
+    if x.dim() != 3 or x.shape[-1] != q.d:
+        raise ValueError(f"x: expected [nseq, T, {q.d}], got {tuple(x.shape)}")
+    nseq, T, dev = x.shape[0], x.shape[1], x.device
+    x2 = x.reshape(-1, q.d)
+    if x2.stride(-1) != 1 or (x2.shape[0] > 1 and (x2.stride(0) * x2.element_size()) % 16 != 0) or \
+            x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    _dev(norms, "norms")
+    if norms.dim() != 2 or norms.shape[0] != nseq:
+        raise ValueError(f"norms: expected [{nseq}, Tstride], got {tuple(norms.shape)}")
+    Tstride = norms.shape[1]
+    _need(norms, "norms", _HALF_BITS, (nseq, Tstride), dev)
+    if layout == TQ_LAYOUT_TILE32:
+        _need(codes, "codes", (torch.int32, torch.uint32), (nseq, (Tstride + 31) // 32, q.planes, q.d), dev)
+    elif layout == TQ_LAYOUT_ROWS:
+        _need(codes, "codes", torch.uint8, (nseq, Tstride, q.code_bytes), dev)
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    if q.mode == TQ_PROD:
+        if gammas is None:
+            raise ValueError("gammas are required for an Algorithm 2 quantizer")
+        _need(gammas, "gammas", _HALF_BITS, (nseq, Tstride), dev)
+    else:
+        gammas = None
+    rc = load().tq_encode_cache(q.handle, _ptr(x2), _DT[x2.dtype], nseq, T, x2.stride(0), t0, Tstride, layout,
+                                _ptr(codes), _ptr(norms), _ptr(gammas), _stream())
+    _lib._check("tq_encode_cache", rc)
+    return codes, norms, gammas
+
+
 def attn_decode_ws_bytes(kq: Quantizer, B: int, Hq: int, Hkv: int, Tstride: int, vlayout: int = TQ_LAYOUT_ROWS) -> int:
     return load().tq_attn_decode_ws_bytes(kq.handle, B, Hq, Hkv, Tstride, vlayout)
 

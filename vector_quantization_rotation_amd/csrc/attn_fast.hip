@@ -1169,7 +1169,8 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
 // token-tiled layout: word [seq][tile][plane][coord] bit i = plane bit of token 32*tile + i
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void tile_records_kernel(const uint8_t *codes, int64_t cb, int planes, int D,
-                                                          int64_t T, int64_t ntile, uint32_t *tiles) {
+                                                          int64_t T, int64_t ntile, int64_t toff, int64_t ntile_dst,
+                                                          uint32_t *tiles) {
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.y;
   const int64_t tp = blockIdx.x;  // pair of tiles
@@ -1186,21 +1187,27 @@ __global__ __launch_bounds__(64) void tile_records_kernel(const uint8_t *codes, 
     const int p = wi / wpp, j = (wi % wpp) * 32 + lane;
     if (lane < 32) {
       const int64_t t0 = 2 * tp, t1 = 2 * tp + 1;
-      if (t0 < ntile) tiles[((seq * ntile + t0) * planes + p) * D + j] = lo;
-      if (t1 < ntile) tiles[((seq * ntile + t1) * planes + p) * D + j] = hi;
+      if (t0 < ntile) tiles[((seq * ntile_dst + toff + t0) * planes + p) * D + j] = lo;
+      if (t1 < ntile) tiles[((seq * ntile_dst + toff + t1) * planes + p) * D + j] = hi;
     }
   }
 }
 
-int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
-                     hipStream_t st) {
+// rows [nseq][T] into the words of tiles toff .. toff + ceil(T/32) - 1 of sequences of ntile_dst tiles
+int run_tile_records_at(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, int64_t toff,
+                        int64_t ntile_dst, uint32_t *tiles, hipStream_t st) {
   const int64_t ntile = (T + 31) / 32;
   if (nseq == 0 || ntile == 0) return TQ_OK;
   ProfScope ps("tile_records", st);
   dim3 grid((unsigned)((ntile + 1) / 2), (unsigned)nseq);
   hipLaunchKernelGGL(tile_records_kernel, grid, dim3(64), 0, st, codes, (int64_t)q->code_bytes, q->planes, q->d, T,
-                     ntile, tiles);
+                     ntile, toff, ntile_dst, tiles);
   return launch_check();
+}
+
+int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
+                     hipStream_t st) {
+  return run_tile_records_at(q, codes, nseq, T, 0, (T + 31) / 32, tiles, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -41,16 +41,41 @@ constexpr int EB = 64;  // rows per tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// Rows of x are nseq sequences of T tokens (a plain encode: one sequence of n rows); token t of sequence s
+// is written to position t0 + t of that sequence's cache row of Tstride positions: records (row layout)
+// or, when `tiles` is set, the token-tiled words [s][t / 32][plane][coordinate], bit t % 32 (t0 a
+// multiple of 32; every word holding a written position is written whole, positions past the last
+// token as zero bits).  A 64-row tile never spans two sequences.
 struct EncArgs {
   const void *x;
-  int64_t ldx, n, ntiles;
-  const uint16_t *pi3;  // [3][D][D] pieces of Pi (row j, column k)
-  const uint16_t *m3;   // [3][D][D] pieces of S Pi^T (Algorithm 2)
-  uint8_t *codes;
-  int64_t code_bytes;
+  int64_t ldx, ntiles;
+  int64_t T, tps;        // tokens per sequence, 64-row tiles per sequence
+  int64_t t0, Tstride;   // first cache position written, positions per sequence in the cache
+  const uint16_t *pi3;   // [3][D][D] pieces of Pi (row j, column k)
+  const uint16_t *m3;    // [3][D][D] pieces of S Pi^T (Algorithm 2)
+  uint8_t *codes;        // row layout
+  uint32_t *tiles;       // token-tiled layout (codes unused)
+  int64_t code_bytes, ntile32;  // ntile32: 32-token words per sequence in the tiled cache
   uint16_t *norms, *gammas;
   Codebook cb;
 };
+
+// 32 x 32 bit-matrix transpose within each half-wave: on entry lane r of a half holds row r (bit c =
+// column c), on exit lane c holds column c (bit r = row r).  Off-diagonal blocks of width 16, 8, 4, 2, 1
+// are exchanged between lanes r and r ^ j: the lower lane keeps its bits in the low half of every
+// 2j-bit block and takes the partner's low halves shifted up; the upper lane keeps its high halves and
+// takes the partner's high halves shifted down.
+__device__ __forceinline__ uint32_t transpose32_bits(uint32_t a, int lane) {
+  uint32_t m = 0x0000FFFFu;
+#pragma unroll
+  for (int j = 16; j >= 1; j >>= 1) {
+    const uint32_t p = (uint32_t)__shfl_xor((int)a, j, 64);
+    const bool low = (lane & j) == 0;
+    a = low ? ((a & m) | ((p << j) & ~m)) : ((a & ~m) | ((p >> j) & m));
+    if (j > 1) m ^= m << (j >> 1);
+  }
+  return a;
+}
 
 template <int XT>
 struct EncIn {
@@ -293,8 +318,9 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
   const int sr = tid / NW, sk = (tid % NW) * PER;
   uint4 raw[RAW];
   auto load_raw = [&](int64_t tile) {
-    const int64_t row = tile * EB + sr;
-    if (row < a.n) {
+    const int64_t sq = tile / a.tps, tl = (tile - sq * a.tps) * EB + sr;
+    if (tl < a.T) {
+      const int64_t row = sq * a.T + tl;
       const uint4 *src =
           reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.x) + (row * a.ldx + sk) * ESZ);
 #pragma unroll
@@ -308,8 +334,9 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
   int64_t tile = blockIdx.x;
   if (tile < a.ntiles) load_raw(tile);
   for (int it = 0; tile < a.ntiles; ++it, tile += gridDim.x) {
-    const int64_t row0 = tile * EB;
-    const int rows = (int)imin64(EB, a.n - row0);
+    const int64_t sq = tile / a.tps, tl0 = (tile - sq * a.tps) * EB;  // sequence, first token of the tile
+    const int rows = (int)imin64(EB, a.T - tl0);
+    const int64_t row0 = sq * a.Tstride + a.t0 + tl0;  // cache position of the tile's first token
     const int buf = it & 1;
 
     // ---- stage the tile: pieces into LDS, fp64 norm ----
@@ -441,7 +468,17 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       for (int p = 0; p < BM; ++p) plane[p] = (((L / 2 - 1) >> p) & 1) ? 0xFFFFFFFFu : 0u;
     }
     uint8_t *rec = a.codes + (row0 + lane) * a.code_bytes + (CW / 8) * wave;
-    if (lane < rows) {
+    // token-tiled words of this wave's columns: lane = (half hh, column c) after the transpose
+    const int tc = lane & 31, thh = lane >> 5;
+    const bool twr = tc < CW && tl0 + 32 * thh < a.T;
+    uint32_t *tw = a.tiles + ((sq * a.ntile32 + (a.t0 + tl0) / 32 + thh) * (BM + (PROD ? 1 : 0))) * D + CW * wave + tc;
+    if (a.tiles) {
+#pragma unroll
+      for (int p = 0; p < BM; ++p) {
+        const uint32_t w = transpose32_bits(lane < rows ? plane[p] : 0u, lane);
+        if (twr) tw[p * D] = w;
+      }
+    } else if (lane < rows) {
 #pragma unroll
       for (int p = 0; p < BM; ++p) {
         if (CW == 32) *reinterpret_cast<uint32_t *>(rec + p * (D / 8)) = plane[p];
@@ -489,7 +526,10 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       sg = shift_in(sg, s4.y >= 0.0f);
       sg = shift_in(sg, s4.x >= 0.0f);
     }
-    if (lane < rows) {
+    if (a.tiles) {
+      const uint32_t w = transpose32_bits(lane < rows ? sg : 0u, lane);
+      if (twr) tw[BM * D] = w;
+    } else if (lane < rows) {
       if (CW == 32) *reinterpret_cast<uint32_t *>(rec + BM * (D / 8)) = sg;
       else *reinterpret_cast<uint16_t *>(rec + BM * (D / 8)) = (uint16_t)sg;
     }
@@ -514,7 +554,6 @@ int enc_blocks_per_cu() {
 
 template <int XT, int D, bool PROD, int BM>
 void launch_encode(EncArgs ea, hipStream_t st) {
-  ea.ntiles = cdiv64(ea.n, EB);
   const int64_t slots = (int64_t)device_cus() * enc_blocks_per_cu<XT, D, PROD, BM>();
   const unsigned grid = (unsigned)imin64(ea.ntiles, slots);
   hipLaunchKernelGGL((encode_kernel<XT, D, PROD, BM>), dim3(grid), dim3(enc_waves(D, PROD) * 64), 0, st, ea);

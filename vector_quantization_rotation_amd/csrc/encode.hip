@@ -38,10 +38,20 @@ bool encode_fused_supported(const tq_quantizer *q) {
 
 int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
                      uint16_t *norms, uint16_t *gammas, hipStream_t st) {
-  if (n == 0) return TQ_OK;
+  return run_encode_fused_cache(q, x, xt, 1, n, ldx, 0, n, TQ_LAYOUT_ROWS, codes, norms, gammas, st);
+}
+
+int run_encode_fused_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx,
+                           int64_t t0, int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas,
+                           hipStream_t st) {
+  if (nseq == 0 || T == 0) return TQ_OK;
   EncArgs ea{};
-  ea.x = x; ea.ldx = ldx; ea.n = n; ea.pi3 = q->pi3; ea.m3 = q->m3; ea.codes = codes;
-  ea.code_bytes = (int64_t)q->code_bytes; ea.norms = norms; ea.gammas = gammas; ea.cb = q->cb;
+  ea.x = x; ea.ldx = ldx; ea.T = T; ea.tps = cdiv64(T, EB); ea.ntiles = nseq * ea.tps; ea.t0 = t0;
+  ea.Tstride = Tstride; ea.pi3 = q->pi3; ea.m3 = q->m3;
+  if (layout == TQ_LAYOUT_TILE32) ea.tiles = static_cast<uint32_t *>(codes);
+  else ea.codes = static_cast<uint8_t *>(codes);
+  ea.code_bytes = (int64_t)q->code_bytes; ea.ntile32 = cdiv64(Tstride, 32);
+  ea.norms = norms; ea.gammas = gammas; ea.cb = q->cb;
   ProfScope ps(q->mode == TQ_PROD ? "encode_prod" : "encode_mse", st);
   if (q->mode == TQ_PROD) launch_encode_prod(xt, q->d, q->bmse, ea, st);
   else launch_encode_mse(xt, q->d, q->bmse, ea, st);

@@ -620,6 +620,39 @@ int run_encode(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t 
   return TQ_OK;
 }
 
+int run_encode_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx, int64_t t0,
+                     int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas, hipStream_t st) {
+  const size_t esz = xt == TQ_F32 ? 4 : 2;
+  if (encode_fused_supported(q) && (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx * esz) % 16 == 0)
+    return run_encode_fused_cache(q, x, xt, nseq, T, ldx, t0, Tstride, layout, codes, norms, gammas, st);
+  // other shapes: the rows into a contiguous staging area, then into their cache positions
+  const bool prod = q->mode == TQ_PROD;
+  const int64_t n = nseq * T;
+  const size_t cb = q->code_bytes;
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t off_n = al((size_t)n * cb), off_g = off_n + al((size_t)n * 2);
+  Scratch sc(st);
+  int rc = sc.alloc(off_g + (prod ? al((size_t)n * 2) : 0));
+  if (rc != TQ_OK) return rc;
+  uint8_t *rc_codes = static_cast<uint8_t *>(sc.p);
+  uint16_t *rc_norms = reinterpret_cast<uint16_t *>(static_cast<char *>(sc.p) + off_n);
+  uint16_t *rc_gammas = prod ? reinterpret_cast<uint16_t *>(static_cast<char *>(sc.p) + off_g) : nullptr;
+  rc = run_encode(q, x, xt, n, ldx, rc_codes, rc_norms, rc_gammas, st);
+  if (rc != TQ_OK) return rc;
+  // norms and gammas: nseq rows of T halves into rows of Tstride, from position t0
+  hipError_t e = hipMemcpy2DAsync(norms + t0, (size_t)Tstride * 2, rc_norms, (size_t)T * 2, (size_t)T * 2,
+                                  (size_t)nseq, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && prod)
+    e = hipMemcpy2DAsync(gammas + t0, (size_t)Tstride * 2, rc_gammas, (size_t)T * 2, (size_t)T * 2, (size_t)nseq,
+                         hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (layout == TQ_LAYOUT_TILE32)
+    return run_tile_records_at(q, rc_codes, nseq, T, t0 / 32, (Tstride + 31) / 32, static_cast<uint32_t *>(codes), st);
+  e = hipMemcpy2DAsync(static_cast<uint8_t *>(codes) + (size_t)t0 * cb, (size_t)Tstride * cb, rc_codes, (size_t)T * cb,
+                       (size_t)T * cb, (size_t)nseq, hipMemcpyDeviceToDevice, st);
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
 int run_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas, int64_t n,
                float *out, int64_t ldo, hipStream_t st) {
   // head dims up to 128: one fused kernel on the bf16 matrix cores

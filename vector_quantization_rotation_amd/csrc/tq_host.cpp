@@ -351,6 +351,19 @@ int tq_encode_prod(const tq_quantizer *q, const void *x, int xt, int64_t n, int6
   return tq::run_encode(q, x, xt, n, ldx, codes, norms, gammas, (hipStream_t)stream);
 }
 
+int tq_encode_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx, int64_t t0,
+                    int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas, void *stream) {
+  if (!q || nseq < 0 || T < 0 || t0 < 0 || Tstride < 0 || !valid_dtype(xt) || ldx < q->d) return TQ_ERR_INVALID;
+  if (layout != TQ_LAYOUT_ROWS && layout != TQ_LAYOUT_TILE32) return TQ_ERR_INVALID;
+  if (t0 + T > Tstride || (layout == TQ_LAYOUT_TILE32 && t0 % 32 != 0)) return TQ_ERR_INVALID;
+  if (nseq == 0 || T == 0) return TQ_OK;
+  if (!x || !codes || !norms || (q->mode == TQ_PROD && !gammas)) return TQ_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(codes) || (ldx * (int64_t)dtype_size(xt)) % 16 != 0) return TQ_ERR_INVALID;
+  if (layout == TQ_LAYOUT_TILE32 && nseq > 65535) return TQ_ERR_UNSUPPORTED;
+  return tq::run_encode_cache(q, x, xt, nseq, T, ldx, t0, Tstride, layout, codes, norms,
+                              q->mode == TQ_PROD ? gammas : nullptr, (hipStream_t)stream);
+}
+
 int tq_decode(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas, int64_t n,
               float *out, int64_t ldo, void *stream) {
   if (!q || n < 0 || ldo < (q ? q->d : 0)) return TQ_ERR_INVALID;

@@ -117,6 +117,15 @@ int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
 bool encode_fused_supported(const tq_quantizer *q);
 int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
                      uint16_t *norms, uint16_t *gammas, hipStream_t st);
+// encode into a cache: nseq x T rows of x to positions t0.. of each sequence (layout TQ_LAYOUT_ROWS:
+// records [nseq][Tstride][code_bytes]; TQ_LAYOUT_TILE32: words [nseq][ceil(Tstride/32)][planes][d])
+int run_encode_fused_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx,
+                           int64_t t0, int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas,
+                           hipStream_t st);
+int run_encode_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq, int64_t T, int64_t ldx, int64_t t0,
+                     int64_t Tstride, int layout, void *codes, uint16_t *norms, uint16_t *gammas, hipStream_t st);
+int run_tile_records_at(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, int64_t toff,
+                        int64_t ntile_dst, uint32_t *tiles, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
 int device_cus();  // compute units of the current device (cached)
 bool decode_fused_supported(const tq_quantizer *q);
