@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
     ap.add_argument("--cpu-encode-rows", type=int, default=524288, help="rows per kind the oracle encodes")
-    ap.add_argument("--only", choices=["", "encode", "attention"], default="",
-                    help="a short run of one part (for counter profiles): the one-layer encode, or the timed "
-                         "attention steps")
+    ap.add_argument("--only", choices=["", "encode", "attention", "global"], default="",
+                    help="a short run of one part (for counter profiles): the one-layer encode, the timed "
+                         "attention steps, or the global-layer attention steps")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
@@ -100,6 +100,33 @@ def encode_only(steps: int):
                                  "value": round(2 * K.shape[0] / dt, 1), "unit": "vectors/s"}}), flush=True)
 
 
+def global_only(steps: int, warmup: int):
+    """The global-layer decode attention (batch 4, 32 query heads over 4 KV heads, head_dim 512, 65536
+    tokens) run warmup + steps times, for counter profiles; prints one JSON line."""
+    import torch
+    from vector_quantization_rotation_amd import api, workloads
+    L = workloads.HET_LAYERS["global"]
+    hB, hHq, hHkv, hT, hd = L["B"], L["Hq"], L["Hkv"], L["T"], L["d"]
+    hc = workloads.het_layer_cache("global")
+    lay = api.TQ_LAYOUT_TILE32
+    hseq = torch.full((hB,), hT, dtype=torch.int32, device="cuda")
+    hout = torch.empty((hB, hHq, hd), dtype=torch.float32, device="cuda")
+    hws = torch.empty((api.attn_decode_ws_bytes(hc.kq, hB, hHq, hHkv, hT, lay),), dtype=torch.uint8, device="cuda")
+    step = api.attn_decode_bound(hc.kq, hc.vq, hc.q, hc.kcodes, hc.knorms, hc.vtiles, hc.vnorms, hc.vgammas, hseq,
+                                 1 / math.sqrt(hd), hout, hws, vlayout=lay)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    pk = hc.packed_bytes()
+    print(json.dumps({"global_attention": {"ms_per_step": round(dt * 1e3, 5), "packed_bytes": pk,
+                                           "gbs": round(pk / dt / 1e9, 2)}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -117,6 +144,9 @@ def main():
     torch.cuda.set_device(0)
     if args.only == "encode":
         encode_only(args.steps)
+        return
+    if args.only == "global":
+        global_only(args.steps, args.warmup)
         return
 
     # ---------------- decode attention (timed steps) ----------------

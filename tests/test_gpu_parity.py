@@ -251,6 +251,12 @@ ATTN_FAST_CASES = [
     (2, 16, 2, 700, [700, 333], 512, 2, 2),
     (1, 32, 4, 1100, [1099], 512, 1, 2),
     (1, 4, 4, 300, [300], 512, 3, 2),            # one head per kv head
+    # head_dim 512, sequence strides that are multiples of 8: the eight-wave kernel with LDS-staged steps
+    (2, 16, 2, 704, [704, 333], 512, 2, 2),      # two head groups, a ragged step
+    (1, 32, 4, 1104, [1099], 512, 1, 2),         # 1-bit keys, 8 heads per kv head
+    (1, 4, 4, 304, [300], 512, 3, 2),            # one head per kv head
+    (1, 8, 1, 65536, [65000], 512, 3, 2),        # several ring turns per work-group
+    (2, 8, 2, 128, [1, 127], 512, 3, 2),         # one token; one step short of full
     (1, 4, 1, 400, [399], 256, 3, 2),            # head_dim 256 folded at 3-bit keys
     (1, 4, 1, 400, [399], 128, 4, 3),            # 4-bit keys, 3-bit values: folded, one wave per SIMD
 ]

@@ -295,25 +295,49 @@ __global__ __launch_bounds__(256) void attn_rotate_kernel(const float *merged, i
   }
 }
 
-// head dims above 256: one row per work-group, eight slices of 2d / 8 terms, partially unrolled
-__global__ __launch_bounds__(256) void attn_rotate_generic_kernel(const float *merged, int d, const float *pi,
-                                                                  const float *s, float *out) {
-  __shared__ float red[8][33];
-  const int64_t bh = blockIdx.x;
+// head dims above 256 (multiples of 256): HB rows per work-group, so that each entry of Pi and S read
+// serves all of them; eight slices of 2d / 8 terms (the first four pair with rows of Pi, the rest with
+// rows of S), walked 16 terms at a time (the matrix entries coalesced across the 32 columns, the rows'
+// terms read as 16-byte pieces every lane of a slice shares)
+template <int HB>
+__global__ __launch_bounds__(256) void attn_rotate_wide_kernel(const float *merged, int64_t BH, int d, const float *pi,
+                                                               const float *s, float *out) {
+  __shared__ float red[HB][8][33];
+  const int64_t bh0 = (int64_t)blockIdx.x * HB;
   const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
   const int j = blockIdx.y * 32 + c;
-  const float *A = merged + bh * 2 * d;
   const int per = 2 * d / 8, t0 = sl * per;
   const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
-  float acc = 0.f;
-#pragma unroll 32
-  for (int i = 0; i < per; ++i) acc = fmaf(mrow[(int64_t)i * d], A[t0 + i], acc);
-  red[sl][c] = acc;
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+  for (int i0 = 0; i0 < per; i0 += 16) {
+    float m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = mrow[(int64_t)(i0 + i) * d];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      const float4 *A = reinterpret_cast<const float4 *>(merged + imin64(bh0 + h, BH - 1) * 2 * d + t0 + i0);
+      const float4 a0 = A[0], a1 = A[1], a2 = A[2], a3 = A[3];
+      const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                            a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+      float v = acc[h];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v = fmaf(m[i], av[i], v);
+      acc[h] = v;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) red[h][sl][c] = acc[h];
   __syncthreads();
   if (sl == 0) {
 #pragma unroll
-    for (int q = 1; q < 8; ++q) acc += red[q][c];
-    out[bh * d + j] = acc;
+    for (int h = 0; h < HB; ++h) {
+      float v = acc[h];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) v += red[h][q][c];
+      if (bh0 + h < BH) out[(bh0 + h) * d + j] = v;
+    }
   }
 }
 
@@ -445,10 +469,10 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, 
     case 128: hipLaunchKernelGGL(attn_rotate_kernel<32>, grid, dim3(256), 0, st, merged, (int64_t)BH, d, pi, s, out); break;
     case 256: hipLaunchKernelGGL(attn_rotate_kernel<64>, grid, dim3(256), 0, st, merged, (int64_t)BH, d, pi, s, out); break;
     default: {
-      // larger head dims: slices of 64 terms, launched per 256-term quarter block of... keep one generic form
-      if (d % 256 != 0 && d > 256) return TQ_ERR_UNSUPPORTED;
-      hipLaunchKernelGGL(attn_rotate_generic_kernel, dim3((unsigned)BH, (unsigned)(d / 32)), dim3(256), 0, st, merged,
-                         d, pi, s, out);
+      // larger head dims (multiples of 256): eight rows per work-group
+      if (d % 256 != 0) return TQ_ERR_UNSUPPORTED;
+      hipLaunchKernelGGL(attn_rotate_wide_kernel<8>, dim3((unsigned)cdiv64(BH, 8), (unsigned)(d / 32)), dim3(256), 0,
+                         st, merged, (int64_t)BH, d, pi, s, out);
     }
   }
   return launch_check();

@@ -183,6 +183,7 @@ constexpr float FA_NCAP = 1.25f;   // norm and gamma caps: this times the larges
 constexpr float FA_HEADROOM = 2.f;  // 2^FA_SLACK
 constexpr int FA_MINSEG = 2;        // fold segment length (256-token steps) before a downward move, at first
 constexpr int FA_MAXSEG = 32;       // ... and at most
+constexpr int FA_FOLDMAX = 512;     // steps between folds at most: the int32 digit sums stay below 2^30
 
 // D: head dim; KB: key index bits; VB: value index bits (Algorithm-2 records hold VB+1 planes)
 //
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
     ++since_fold;
     ++since_down;
     const bool low = whole && since_fold >= down_seg && ((flags >> 1) & ((1 << gw) - 1)) != ((1 << gw) - 1);
-    if ((flags & 33) || low) {
+    if ((flags & 33) || low || since_fold >= FA_FOLDMAX) {
       if ((flags & 1) && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, FA_MAXSEG);
       if (low) since_down = 0;
       // ---- rare: move the reference to this step's maxima and fold the int32 accumulators ----
@@ -968,6 +969,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       body(std::false_type{}, s_ring1, s_ring2, s + 1);
       body(std::false_type{}, s_ring2, s_ring0, s + 2);
     }
+    wv_wait_vm<0>();  // the stages past the chunk have landed before the wave ends
   }
   // ---- final fold and partial record: m, l, acc_mse[D], acc_qjl[D] ----
   {
@@ -989,6 +991,384 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       const int col = 64 * (c >> 2) + 4 * ln + (c & 3);
       dst[2 + col] = a.vbeta[0] * (2.f * accf[0][c] - ym_run);
       dst[2 + D + col] = a.vqjl * (2.f * accf[1][c] - yq_run);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Head dim 512 with 1-bit value indices (the global-layer shape): a work-group of eight waves walks
+// 128-token steps of one (batch, KV head, four-head group, chunk).
+//
+// * Each step is staged in LDS by direct-to-LDS loads issued two steps ahead into a three-slot ring:
+//   the step's key records as they lie in HBM, its four token-tiled value words per plane and
+//   coordinate, and the three fp16 arrays.  Nothing in flight occupies registers, so two waves share
+//   each SIMD (the register-prefetching attn_fast_kernel runs one).  Every wave loads an equal share
+//   of each stage and waits for its own loads; a work-group barrier then makes the stage visible.
+// * Wave w scores tokens 16 w .. 16 w + 15 of the step on the fp8 x fp4 matrix cores, one query image
+//   per 128-coordinate block with the key codebook's Walsh coefficients applied to the per-plane sums
+//   (at 1-bit keys, one plane, folded into the image), as attn_fast_kernel at this head dim.  Lane group g of block wb carries key word 4 g + wb of a
+//   plane, so a lane reads the four blocks' words of a plane as one 16-byte piece of the record; the
+//   query images follow the same order.
+// * Each lane weighs one (head, token): p n and p gamma as 28-bit integers in four 7-bit digits written
+//   to the byte of the value operand's contraction slot that holds the token's bit, then all 128
+//   tokens are aggregated by every wave for its 64 value columns on the int8 matrix cores.
+// * The softmax reference (running maximum per head, value norm and gamma caps, headroom, downward
+//   moves behind a dominant token) is shared by the work-group as in attn_fast_kernel.
+// ---------------------------------------------------------------------------
+constexpr int WD_D = 512;
+constexpr int WD_STEP = 128;     // tokens per step: eight waves x 16
+constexpr int WD_WAVES = 8;
+constexpr int WD_THREADS = 64 * WD_WAVES;
+constexpr int WD_FOLDMAX = 1024; // steps between folds at most: the int32 digit sums stay below 2^31
+
+template <int KB>
+struct WideStage {
+  static constexpr int KCB = KB * WD_D / 8;                    // key record bytes
+  static constexpr int KEYS = WD_STEP * KCB;                   // the step's key records
+  static constexpr int VALS = (WD_STEP / 32) * 2 * WD_D * 4;   // four tile words x two planes x 512 coordinates
+  static constexpr int NORMS = 4 * WD_STEP * 2;                // n_K, n_V, gamma_V, and a landing zone
+  static constexpr int BYTES = KEYS + VALS + NORMS;
+  static constexpr int KLOADS = KEYS / 1024 / WD_WAVES;        // 1 KiB direct-to-LDS loads per wave
+  static constexpr int VLOADS = VALS / 1024 / WD_WAVES;
+  static constexpr int NLOAD = KLOADS + VLOADS + 1;            // (+ one fp16 array, or a load of nothing)
+  static_assert(KEYS % (1024 * WD_WAVES) == 0 && VALS % (1024 * WD_WAVES) == 0, "stage split");
+};
+
+// this wave's share of the loads of one stage (tokens t0 .. t0 + 127).  Waves 0..2 fetch the three fp16
+// arrays; the others aim past every buffer (zeros into the stage's landing zone, no memory touched), so
+// every wave issues the same number of loads, all into the one LDS object of the slot.  Reads past the
+// chunk return zeros.
+template <int KB>
+__device__ __forceinline__ void wd_stage_load(uint8_t *stage, __amdgpu_buffer_rsrc_t rk,
+                                              __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rkn,
+                                              __amdgpu_buffer_rsrc_t rvn, __amdgpu_buffer_rsrc_t rvg, int wave,
+                                              int lane, int64_t t0) {
+  using S = WideStage<KB>;
+  const int sk = __builtin_amdgcn_readfirstlane((int)(t0 * S::KCB));
+#pragma unroll
+  for (int i = 0; i < S::KLOADS; ++i) {
+    const int e = wave * S::KLOADS + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(stage + e * 1024), 16, lane * 16 + e * 1024, sk, 0, 0);
+  }
+  const int sv = __builtin_amdgcn_readfirstlane((int)((t0 >> 5) * 2 * WD_D * 4));
+#pragma unroll
+  for (int i = 0; i < S::VLOADS; ++i) {
+    const int e = wave * S::VLOADS + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(stage + S::KEYS + e * 1024), 16, lane * 16 + e * 1024,
+                                             sv, 0, 0);
+  }
+  const int sn = __builtin_amdgcn_readfirstlane((int)(t0 * 2));
+  const bool real = wave < 3;
+  const __amdgpu_buffer_rsrc_t rn = wave == 0 ? rkn : (wave == 1 ? rvn : rvg);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void_t *)(stage + S::KEYS + S::VALS + (real ? wave : 3) * 256), 4,
+                                           real ? lane * 4 : 0x7FFFFF00, real ? sn : 0, 0, 0);
+}
+
+// every LDS access of this wave issued before has completed, then a work-group barrier (the
+// wavefront-scope fences order the compiler's own LDS accesses around it without making it wait for the
+// direct-to-LDS loads still in flight)
+__device__ __forceinline__ void wd_barrier() {
+  __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KB>
+__global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
+  constexpr int D = WD_D;
+  constexpr int KP = walsh_count(KB);
+  constexpr int NB = D / 128;        // 128-coordinate blocks
+  constexpr bool FOLD = fold_beta(D, KB);  // one image per block, Walsh coefficients after the MFMA (2-3-bit keys)
+  constexpr int NI8 = (FOLD ? 1 : KP) * NB;  // query images (1-bit keys: one per block, 2 beta folded in)
+  constexpr int NTC = 4;             // value columns of a lane: 64 w + 4 ln + c
+  constexpr float WMAX = 268435328.f;  // 2^28 - 128 (see attn_fast_kernel)
+  using S = WideStage<KB>;
+
+  // one object per ring slot, so the compiler's waits for the direct-to-LDS loads stay per slot
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring0[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring1[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring2[S::BYTES];
+  // weight digits [token tile][row][slot] of p n (s_wm) and p gamma (s_wq), two objects so that the compiler
+  // keeps their accesses apart from the loads in flight
+  __shared__ __attribute__((aligned(16))) uint8_t s_wm[2][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_wq[2][16][64];
+  __shared__ int s_flag[WD_WAVES];
+  __shared__ float s_max[WD_WAVES][FA_GMAX + 2];
+  __shared__ float s_merge[WD_WAVES][FA_GMAX][3];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 4, ln = lane & 15;
+  const int kofs = (hl & 1) * 4;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int nbg = (int)gridDim.x / a.nsub;
+  const int sub = unit / nbg, bg = unit % nbg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int h0 = g * a.G + sub * FA_GMAX;
+  const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
+  const bool head_ok = hl < gw;
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
+  const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = imin64(T, c0 + a.chunk);
+  const int nvalid = c0 < c1 ? (int)((c1 - c0 + WD_STEP - 1) / WD_STEP) : 0;
+  const int nsteps = (nvalid + 2) / 3 * 3;  // whole ring turns (steps past the chunk hold no valid token)
+
+  intx8 qa[NI8];
+  {
+    const intx8 *img = reinterpret_cast<const intx8 *>(a.qimg) + (int64_t)unit * NI8 * 64;
+#pragma unroll
+    for (int i = 0; i < NI8; ++i) qa[i] = img[i * 64 + lane];
+  }
+  const float qinv2 = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 0] * a.scale_log2;
+  const float qconst2 = a.qinfo[((int64_t)unit * FA_GMAX + hl) * 2 + 1] * a.scale_log2;
+  for (int i = tid; i < (int)sizeof(s_wm) / 4; i += WD_THREADS) {
+    reinterpret_cast<uint32_t *>(&s_wm[0][0][0])[i] = 0u;
+    reinterpret_cast<uint32_t *>(&s_wq[0][0][0])[i] = 0u;
+  }
+
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.kcodes + seq * a.Tstride * S::KCB, c1 * S::KCB);
+  const int64_t nbytes = (c1 * 2 + 3) & ~(int64_t)3;
+  const __amdgpu_buffer_rsrc_t rkn = uniform_rsrc(a.knorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvn = uniform_rsrc(a.vnorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvg = uniform_rsrc(a.vgammas + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.vtiles + seq * a.ntile * 2 * D, ((c1 + 31) >> 5) * 2 * D * 4);
+
+  float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f, m_top = -INFINITY;
+  int since_fold = 0, down_seg = FA_MINSEG, since_down = 1 << 30;
+  float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;
+  float accf[2][NTC];
+  intx4 vacc[2][NTC];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int c = 0; c < NTC; ++c) {
+      accf[p][c] = 0.f;
+      vacc[p][c] = intx4{0, 0, 0, 0};
+    }
+
+  // this lane's token in a step and its place in the value operand: token tile tt, contraction slot
+  // `slot` (lane group 2 (word) + (bit 2 of the token's bit), byte 4 (bit % 4) + bit / 8), byte value
+  // 2^value_kexp(bit % 8), undone by kscale
+  const int tw = 16 * wave + ln;
+  const int tt = tw >> 6, tau = tw & 63, bitw = tau & 31, r8 = bitw & 7;
+  const int slot = 16 * (2 * (tau >> 5) + (r8 >> 2)) + 4 * (r8 & 3) + (bitw >> 3);
+  const float kscale = __builtin_amdgcn_ldexpf(1.f, -value_kexp(r8));
+  const uint32_t f4_ones = f4_ones_reg();
+
+  auto body = [&, rk, rv, rkn, rvn, rvg](uint8_t *st, uint8_t *stl, int s) {
+    const int64_t t0 = c0 + (int64_t)s * WD_STEP;
+    // this wave's loads of stage s have landed (stage s + 1 may still be in flight); after the barrier
+    // everyone's have, and every wave is done with step s - 1, whose slot the loads of s + 2 take
+    wv_wait_vm<S::NLOAD>();
+    __builtin_amdgcn_sched_barrier(0);
+    wd_barrier();
+    // every read of the stage first (its key words, value words and fp16 values into registers), then the
+    // loads of step s + 2: no LDS read of a ring slot follows a load in flight
+    uint4 kw4[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) kw4[p] = *reinterpret_cast<const uint4 *>(st + tw * S::KCB + p * (D / 8) + 16 * hl);
+    uint4 vw4[2][2];  // [token tile][plane]: columns 64 w + 4 ln .. + 3 of this lane group's tile word
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        vw4[t2][p] = *reinterpret_cast<const uint4 *>(st + S::KEYS +
+                                                      ((2 * (2 * t2 + (hl >> 1)) + p) * D + 64 * wave + 4 * ln) * 4);
+    const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
+    const uint32_t hk = nrm[tw], hv = nrm[WD_STEP + tw], hg = nrm[2 * WD_STEP + tw];
+    __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0): the reads are done
+    __builtin_amdgcn_sched_barrier(0);
+    wd_stage_load<KB>(stl, rk, rv, rkn, rvn, rvg, wave, lane, t0 + 2 * WD_STEP);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- key pass: token tw against the four heads' query digits ----
+    floatx4 cacc[FOLD ? KP : 1];
+#pragma unroll
+    for (int p = 0; p < (FOLD ? KP : 1); ++p) cacc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+#pragma unroll
+      for (int wb = 0; wb < NB; ++wb) {
+        uint32_t w[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) w[p] = wb == 0 ? kw4[p].x : wb == 1 ? kw4[p].y : wb == 2 ? kw4[p].z : kw4[p].w;
+        uint32_t wp[KP];
+        walsh_planes<KB>(w, wp);
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+          const uint32_t x = wp[p];
+          intx8 bb;
+          bb[0] = (int)(x & 0x11111111u);
+          bb[1] = (int)(x & 0x22222222u);
+          bb[2] = (int)(x & 0x44444444u);
+          bb[3] = f4_sign_half(x, f4_ones);
+          bb[4] = bb[5] = bb[6] = bb[7] = 0;
+          const int ai = FOLD ? wb : p * NB + wb;
+          cacc[FOLD ? p : 0] =
+              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ai], bb, cacc[FOLD ? p : 0], 0, 4, 0, 0, 0, 0);
+        }
+      }
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < (FOLD ? KP : 1); ++p) {  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
+      const float x = cacc[p][0] + (cacc[p][1] * 0.0625f + (cacc[p][2] * (1.f / 512.f) + cacc[p][3] * (1.f / 16384.f)));
+      v = FOLD ? fmaf(2.f * a.kbeta[p], x, v) : x;
+    }
+    const bool tvalid = t0 + tw < c1;
+    const float fvn = tvalid ? f16_to_f32((uint16_t)hv) : 0.f;
+    const float fvg = tvalid ? f16_to_f32((uint16_t)hg) : 0.f;
+    float sc = (head_ok && tvalid) ? fmaf(v, qinv2, -qconst2) * f16_to_f32((uint16_t)hk) : -INFINITY;
+    // ---- reference test (the work-group's flags) ----
+    {
+      const bool over = sc > m_ref + FA_SLACK;
+      const bool near = sc >= m_ref - REF_DROP;
+      const bool over_n = fvn > vn_ref || fvg > vg_ref;
+      const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0ull;
+      const bool wave_over_n = __builtin_amdgcn_ballot_w64(over_n) != 0ull;
+      const uint64_t wave_near = __builtin_amdgcn_ballot_w64(near);
+      int flag = (wave_over ? 1 : 0) | (wave_over_n ? 32 : 0);
+#pragma unroll
+      for (int h = 0; h < FA_GMAX; ++h) flag |= ((wave_near >> (16 * h)) & 0xFFFFull) != 0 ? 2 << h : 0;
+      if (lane == 0) s_flag[wave] = flag;
+    }
+    wd_barrier();  // flags visible
+    int flags = 0;
+#pragma unroll
+    for (int w = 0; w < WD_WAVES; ++w) flags |= s_flag[w];
+    const bool whole = t0 + WD_STEP <= c1;
+    ++since_fold;
+    ++since_down;
+    const bool low = whole && since_fold >= down_seg && ((flags >> 1) & ((1 << gw) - 1)) != ((1 << gw) - 1);
+    if ((flags & 33) || low || since_fold >= WD_FOLDMAX) {
+      if ((flags & 1) && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, FA_MAXSEG);
+      if (low) since_down = 0;
+      // rare: move the reference to this step's maxima and fold the int32 accumulators
+      const float smax = rows16_max(sc);
+      const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
+      if (ln == 0) s_max[wave][hl] = smax;
+      if (lane == 0) { s_max[wave][FA_GMAX] = vnm; s_max[wave][FA_GMAX + 1] = vgm; }
+      wd_barrier();
+      float step_m = -INFINITY, step_vn = 0.f, step_vg = 0.f;
+#pragma unroll
+      for (int w = 0; w < WD_WAVES; ++w) {
+        step_m = fmaxf(step_m, s_max[w][hl]);
+        step_vn = fmaxf(step_vn, s_max[w][FA_GMAX]);
+        step_vg = fmaxf(step_vg, s_max[w][FA_GMAX + 1]);
+      }
+      m_top = fmaxf(m_top, step_m);
+      const float m_new = moved_reference(m_ref, step_m, m_top, low);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float isc = p == 0 ? im : iq;
+#pragma unroll
+        for (int c = 0; c < NTC; ++c) {
+          const float x = (((float)vacc[p][c][0] * 128.f + (float)vacc[p][c][1]) * 128.f + (float)vacc[p][c][2]) *
+                              128.f + (float)vacc[p][c][3];
+          accf[p][c] = (accf[p][c] + x * isc) * alpha;
+          vacc[p][c] = intx4{0, 0, 0, 0};
+        }
+      }
+      l_run *= alpha;
+      ym_run *= alpha;
+      yq_run *= alpha;
+      m_ref = m_new;
+      vn_ref = fmaxf(vn_ref, FA_NCAP * step_vn);
+      vg_ref = fmaxf(vg_ref, FA_NCAP * step_vg);
+      since_fold = 0;
+    }
+    // ---- weight of (head hl, token tw): p n and p gamma as four 7-bit digits ----
+    {
+      const float sm = vn_ref > 0.f ? WMAX * kscale / (vn_ref * FA_HEADROOM) : 0.f;
+      const float sq = vg_ref > 0.f ? WMAX * kscale / (vg_ref * FA_HEADROOM) : 0.f;
+      const float ism = sm > 0.f ? 1.f / sm : 0.f, isq = sq > 0.f ? 1.f / sq : 0.f;
+      const float p = sc == -INFINITY ? 0.f : exp2f(sc - m_ref);
+      l_run += p;
+      const uint32_t um = __float2uint_rn(p * fvn * sm), uq = __float2uint_rn(p * fvg * sq);
+      ym_run = fmaf((float)um, ism, ym_run);
+      yq_run = fmaf((float)uq, isq, yq_run);
+      if (head_ok) {
+        s_wm[tt][4 * hl + 0][slot] = (uint8_t)(um >> 21);
+        s_wm[tt][4 * hl + 1][slot] = (uint8_t)((um >> 14) & 127u);
+        s_wm[tt][4 * hl + 2][slot] = (uint8_t)((um >> 7) & 127u);
+        s_wm[tt][4 * hl + 3][slot] = (uint8_t)(um & 127u);
+        s_wq[tt][4 * hl + 0][slot] = (uint8_t)(uq >> 21);
+        s_wq[tt][4 * hl + 1][slot] = (uint8_t)((uq >> 14) & 127u);
+        s_wq[tt][4 * hl + 2][slot] = (uint8_t)((uq >> 7) & 127u);
+        s_wq[tt][4 * hl + 3][slot] = (uint8_t)(uq & 127u);
+      }
+    }
+    wd_barrier();  // weight digits of the step's 128 tokens visible
+    // ---- value pass: 128 tokens x this wave's 64 columns, both kinds ----
+    {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_wm[t2][ln][16 * hl]);
+        const intx4 wa_q = *reinterpret_cast<const intx4 *>(&s_wq[t2][ln][16 * hl]);
+        const uint4 w0 = vw4[t2][0], w1 = vw4[t2][1];
+        const uint32_t x0[4] = {w0.x, w0.y, w0.z, w0.w}, x1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int c = 0; c < NTC; ++c) {
+          vacc[0][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m, value_bits(x0[c], kofs), vacc[0][c], 0, 0, 0);
+          vacc[1][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q, value_bits(x1[c], kofs), vacc[1][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    wd_stage_load<KB>(s_ring0, rk, rv, rkn, rvn, rvg, wave, lane, c0);
+    wd_stage_load<KB>(s_ring1, rk, rv, rkn, rvn, rvg, wave, lane, c0 + WD_STEP);
+    // the query images and offsets (loaded before the stages; loads complete in order) are in registers
+    // before the loop, so no wait inside it has to cover them
+    wv_wait_vm<2 * S::NLOAD>();
+    for (int s = 0; s < nsteps; s += 3) {
+      body(s_ring0, s_ring2, s);
+      body(s_ring1, s_ring0, s + 1);
+      body(s_ring2, s_ring1, s + 2);
+    }
+    wv_wait_vm<0>();  // the last two stages' loads (past the chunk) have landed before the work-group ends
+  }
+  // ---- final fold, reductions, partial record: m, l, acc_mse[D], acc_qjl[D] ----
+  {
+    const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float isc = p == 0 ? im : iq;
+#pragma unroll
+      for (int c = 0; c < NTC; ++c) {
+        const float x = (((float)vacc[p][c][0] * 128.f + (float)vacc[p][c][1]) * 128.f + (float)vacc[p][c][2]) *
+                            128.f + (float)vacc[p][c][3];
+        accf[p][c] += x * isc;
+      }
+    }
+  }
+  l_run = rows16_sum(l_run);
+  ym_run = rows16_sum(ym_run);
+  yq_run = rows16_sum(yq_run);
+  if (ln == 0) {
+    s_merge[wave][hl][0] = l_run;
+    s_merge[wave][hl][1] = ym_run;
+    s_merge[wave][hl][2] = yq_run;
+  }
+  wd_barrier();
+  if (head_ok) {
+    float L = 0.f, YM = 0.f, YQ = 0.f;
+#pragma unroll
+    for (int w = 0; w < WD_WAVES; ++w) {
+      L += s_merge[w][hl][0];
+      YM += s_merge[w][hl][1];
+      YQ += s_merge[w][hl][2];
+    }
+    float *dst = a.part + (((int64_t)b * a.Hq + h0 + hl) * a.nsplit + split) * (2 + 2 * (int64_t)D);
+    if (wave == 0 && ln == 0) { dst[0] = m_ref; dst[1] = L; }
+#pragma unroll
+    for (int c = 0; c < NTC; ++c) {
+      const int col = 64 * wave + 4 * ln + c;
+      dst[2 + col] = a.vbeta[0] * (2.f * accf[0][c] - YM);
+      dst[2 + D + col] = a.vqjl * (2.f * accf[1][c] - YQ);
     }
   }
 }
@@ -1031,9 +1411,99 @@ __device__ __forceinline__ float split_fix4_e4m3(float u, float f, uint8_t (&o)[
   return v;
 }
 
+// the images and offsets of head h of a unit from its rotated query q' (qp, D floats in LDS), by 256
+// threads (tid, their waves wv); red: 4 x 2 floats of LDS for this head's reductions.  Every thread of
+// the work-group calls it the same number of times (it holds barriers).
+// PERM: the word order of the head-dim-512 kernel, where lane group g of block wb's image holds key word
+// 4 g + wb of a plane (so a lane reads the four blocks' words of a plane as one 16-byte piece) instead
+// of word 4 wb + g
+template <int D, int KB, bool PERM>
+__device__ __forceinline__ void prep_images(const PrepArgs &a, int unit, int h, bool present, const float *qp,
+                                            float (*red)[2], int tid) {
+  constexpr int KP = walsh_count(KB);
+  constexpr bool FOLD = fold_beta(D, KB);
+  const int wv = tid >> 6, lane = tid & 63;
+  // sum q' and max |q'_j|
+  {
+    float sm = 0.f, mx = 0.f;
+    for (int j = tid; j < D; j += 256) {
+      sm += qp[j];
+      mx = fmaxf(mx, fabsf(qp[j]));
+    }
+    sm = wave_sum_f32(sm);
+    mx = wave_max_f32(mx);
+    if (lane == 0) { red[wv][0] = sm; red[wv][1] = mx; }
+  }
+  __syncthreads();
+  const float qsum = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+  float bmax = 0.f;
+#pragma unroll
+  for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
+  if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
+  const float mxs = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1])) * bmax;
+  const float sq = mxs > 0.f ? 224.f / mxs : 0.f;
+  // image ii (FOLD: the 128-coordinate block ii, coefficients applied after the matrix cores; else
+  // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
+  // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
+  // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
+  // t = (k % 32) / 8, which carries bit b = bit 4 n + t of the block's key word k / 32 as the value
+  // 2^(t - 1) b for t < 3 and 0.5 - b for t = 3 (bit b in the nibble's sign, 0.5 always set): coordinate
+  // 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - t), or by -1 for t = 3, whose sums then fall
+  // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
+  // taken off the score's offset below).  This work-group writes the 16 lanes of its head (rows 4 h ..
+  // 4 h + 3 of the four lane groups) in every image.
+  constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
+  for (int e = tid; e < NI8 * 16 * 8; e += 256) {
+    const int w = e & 7, r = (e >> 3) & 15, ii = e >> 7;
+    const int wb = ii % (D / 128), p = ii / (D / 128);
+    const int dg = r & 3, gg = r >> 2, il = 16 * gg + 4 * h + dg;
+    uint32_t word = 0;
+    if (present) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int i = 4 * w + bb;
+        const int k = i < 16 ? 16 * gg + i : 64 + 16 * gg + (i - 16);
+        const int t = (k & 31) >> 3, n = k & 7;
+        const int j = (PERM ? 32 * (4 * (k >> 5) + wb) : 128 * wb + 32 * (k >> 5)) + 4 * n + t;
+        const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
+        uint8_t o[4];
+        split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), f, o);
+        word |= (uint32_t)o[dg] << (8 * bb);
+      }
+    }
+    a.qimg[(((int64_t)unit * NI8 + ii) * 64 + il) * 8 + w] = (int)word;
+  }
+  // half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
+  float cs = 0.f;
+  if (present) {
+    for (int e = tid; e < (FOLD ? 1 : KP) * (D / 4); e += 256) {
+      const int p = e / (D / 4), j = 4 * (e % (D / 4)) + 3;
+      uint8_t o[4];
+      cs += split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), -1.f, o);
+    }
+  }
+  cs = wave_sum_f32(cs);
+  __syncthreads();  // every read of red above is done
+  if (lane == 0) red[wv][0] = cs;
+  __syncthreads();
+  if (tid == 0) {
+    float c = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+    if (FOLD) {
+      float bs = 0.f;
+#pragma unroll
+      for (int p = 0; p < KP; ++p) bs += 2.f * a.kbeta[p];
+      c *= bs;
+    }
+    c *= 0.5f;
+    const float qinv = (present && sq > 0.f) ? 1.f / sq : 0.f;
+    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = qinv;
+    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = present ? a.ctop * qsum - c * qinv : 0.f;
+  }
+}
+
 // images for the fp8 x fp4 matrix-core key passes: one work-group per (unit, head of its group), so the
 // four heads' images are made in parallel
-template <int D, int KB>
+template <int D, int KB, bool PERM = false>
 __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   constexpr int KP = walsh_count(KB);
   constexpr bool FOLD = fold_beta(D, KB);
@@ -1087,82 +1557,77 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
     }
   }
   __syncthreads();
-  // sum q' and max |q'_j|
-  {
-    float sm = 0.f, mx = 0.f;
-    for (int j = tid; j < D; j += 256) {
-      sm += qp[j];
-      mx = fmaxf(mx, fabsf(qp[j]));
+  prep_images<D, KB, PERM>(a, unit, h, present, qp, red, tid);
+}
+
+// the same for head dims of 256 and more, where one work-group per head would read the whole d x d
+// matrix once per head: 1024 threads per unit rotate its four heads' queries together (each entry of
+// Pi^T read serves the four), then four groups of 256 threads make one head's images each.  (The
+// decode-step append keeps the one-work-group-per-head form.)
+template <int D, int KB, bool PERM = false>
+__global__ __launch_bounds__(1024) void attn_fast_prep_wide_kernel(PrepArgs a) {
+  static_assert(D >= 256 && D <= 1024 && D % 256 == 0, "wide prep: head dims 256 .. 1024");
+  constexpr int NT = 1024, SL = NT / D;  // k slices per column
+  __shared__ float4 qs[D];                // q of the four heads, [k][head]
+  __shared__ float qp[FA_GMAX][D];
+  __shared__ float qpart[SL > 1 ? SL - 1 : 1][FA_GMAX][D];
+  __shared__ float red[FA_GMAX][4][2];
+  const int unit = blockIdx.x;
+  const int nbg = (int)gridDim.x / a.nsub;
+  const int sub = unit / nbg, bg = unit % nbg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int h0 = g * a.G + sub * FA_GMAX;
+  const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < FA_GMAX * D; e += NT) {
+    const int h = e / D, j = e % D;
+    float v = 0.f;
+    if (h < gw) {
+      const int64_t off = ((int64_t)b * a.Hq + h0 + h) * D + j;
+      if (a.qt == TQ_F32) v = static_cast<const float *>(a.q)[off];
+      else if (a.qt == TQ_BF16) v = bf16_to_f32(static_cast<const uint16_t *>(a.q)[off]);
+      else v = f16_to_f32(static_cast<const uint16_t *>(a.q)[off]);
     }
-    sm = wave_sum_f32(sm);
-    mx = wave_max_f32(mx);
-    if (lane == 0) { red[wv][0] = sm; red[wv][1] = mx; }
+    reinterpret_cast<float *>(qs)[4 * j + h] = v;
   }
   __syncthreads();
-  const float qsum = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
-  float bmax = 0.f;
+  // q'_j = sum_k Pi^T[k][j] q_k for the four heads: thread (slice, j) sums a slice of k for column j,
+  // 32 loads in flight at a time; the slices are added through LDS
+  {
+    const int j = tid % D, sl = tid / D;
+    constexpr int KS = D / SL, KU = 32;
+    float acc[FA_GMAX] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = sl * KS; k0 < (sl + 1) * KS; k0 += KU) {
+      float pv[KU];
 #pragma unroll
-  for (int p = 0; p < KP; ++p) bmax = fmaxf(bmax, fabsf(2.f * a.kbeta[p]));
-  if (FOLD) bmax = 1.f;  // the coefficients are applied to the kernel's per-plane results
-  const float mxs = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1])) * bmax;
-  const float sq = mxs > 0.f ? 224.f / mxs : 0.f;
-  // image ii (FOLD: the 128-coordinate block ii, coefficients applied after the matrix cores; else
-  // Walsh plane ii / (D / 128) of block ii % (D / 128), 2 beta folded in), lane (row m = 4 h + digit,
-  // k-group g), byte i of its 32: contraction index k = 16 g + i (i < 16) or 64 + 16 g + i - 16; the key
-  // operand holds k as nibble k % 32 of lane group k / 32, i.e. nibble position n = k % 8 of dword
-  // t = (k % 32) / 8, which carries bit b = bit 4 n + t of the block's key word k / 32 as the value
-  // 2^(t - 1) b for t < 3 and 0.5 - b for t = 3 (bit b in the nibble's sign, 0.5 always set): coordinate
-  // 128 block + 32 (k / 32) + 4 n + t, scaled by 2^(1 - t), or by -1 for t = 3, whose sums then fall
-  // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
-  // taken off the score's offset below).  This work-group writes the 16 lanes of its head (rows 4 h ..
-  // 4 h + 3 of the four lane groups) in every image.
-  constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
-  for (int e = tid; e < NI8 * 16 * 8; e += 256) {
-    const int w = e & 7, r = (e >> 3) & 15, ii = e >> 7;
-    const int wb = ii % (D / 128), p = ii / (D / 128);
-    const int dg = r & 3, gg = r >> 2, il = 16 * gg + 4 * h + dg;
-    uint32_t word = 0;
-    if (present) {
+      for (int i = 0; i < KU; ++i) pv[i] = a.piT[(int64_t)(k0 + i) * D + j];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int i = 4 * w + bb;
-        const int k = i < 16 ? 16 * gg + i : 64 + 16 * gg + (i - 16);
-        const int t = (k & 31) >> 3, n = k & 7;
-        const int j = 128 * wb + 32 * (k >> 5) + 4 * n + t;
-        const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
-        uint8_t o[4];
-        split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), f, o);
-        word |= (uint32_t)o[dg] << (8 * bb);
+      for (int i = 0; i < KU; ++i) {
+        const float4 q4 = qs[k0 + i];
+        acc[0] = fmaf(pv[i], q4.x, acc[0]);
+        acc[1] = fmaf(pv[i], q4.y, acc[1]);
+        acc[2] = fmaf(pv[i], q4.z, acc[2]);
+        acc[3] = fmaf(pv[i], q4.w, acc[3]);
       }
     }
-    a.qimg[(((int64_t)unit * NI8 + ii) * 64 + il) * 8 + w] = (int)word;
-  }
-  // half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
-  float cs = 0.f;
-  if (present) {
-    for (int e = tid; e < (FOLD ? 1 : KP) * (D / 4); e += 256) {
-      const int p = e / (D / 4), j = 4 * (e % (D / 4)) + 3;
-      uint8_t o[4];
-      cs += split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), -1.f, o);
-    }
-  }
-  cs = wave_sum_f32(cs);
-  __syncthreads();  // every read of red above is done
-  if (lane == 0) red[wv][0] = cs;
-  __syncthreads();
-  if (tid == 0) {
-    float c = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
-    if (FOLD) {
-      float bs = 0.f;
+    if (sl > 0) {
 #pragma unroll
-      for (int p = 0; p < KP; ++p) bs += 2.f * a.kbeta[p];
-      c *= bs;
+      for (int h = 0; h < FA_GMAX; ++h) qpart[sl - 1][h][j] = acc[h];
     }
-    c *= 0.5f;
-    const float qinv = (present && sq > 0.f) ? 1.f / sq : 0.f;
-    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 0] = qinv;
-    a.qinfo[((int64_t)unit * FA_GMAX + h) * 2 + 1] = present ? a.ctop * qsum - c * qinv : 0.f;
+    __syncthreads();
+    if (sl == 0) {
+#pragma unroll
+      for (int h = 0; h < FA_GMAX; ++h) {
+        float v = acc[h];
+#pragma unroll
+        for (int q = 0; q < SL - 1; ++q) v += qpart[q][h][j];
+        qp[h][j] = v;
+      }
+    }
   }
+  __syncthreads();
+  const int hh = tid >> 8;
+  prep_images<D, KB, PERM>(a, unit, hh, hh < gw, qp[hh], red[hh], tid & 255);
 }
 
 // ---------------------------------------------------------------------------
@@ -1310,6 +1775,42 @@ WavePlan wave_plan(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+bool wide_supported(int D, int KB, int VB) { return D == WD_D && VB == 1 && KB >= 1 && KB <= 3; }
+
+// resident work-groups of attn_wide_kernel<KB> on the current device (cached per device)
+int wide_slots(int KB) {
+  static int cache[64][4] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int &slot = cache[dev][KB];
+  if (slot > 0) return slot;
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (KB == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide_kernel<1>, WD_THREADS, 0);
+  if (KB == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide_kernel<2>, WD_THREADS, 0);
+  if (KB == 3) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide_kernel<3>, WD_THREADS, 0);
+  if (e != hipSuccess || blocks <= 0) blocks = 1;
+  slot = device_cus() * blocks;
+  return slot;
+}
+
+// the head-dim-512 plan: the query images and offsets as fast_plan lays them out, chunks of whole ring
+// turns (three 128-token steps), one per resident work-group
+FastPlan wide_plan(int KB, int B, int Hq, int Hkv, int64_t T) {
+  FastPlan p = fast_plan(WD_D, KB, 1, B, Hq, Hkv, T);
+  const int64_t units = (int64_t)B * Hkv * p.nsub;
+  const int64_t want = std::max<int64_t>(1, wide_slots(KB) / std::max<int64_t>(units, 1));
+  const int64_t turn = 3 * (int64_t)WD_STEP;
+  int64_t chunk = (T + want - 1) / want;
+  chunk = std::max<int64_t>(turn, (chunk + turn - 1) / turn * turn);
+  p.chunk = (int)std::min<int64_t>(chunk, 1 << 30);
+  p.nsplit = (int)std::max<int64_t>(1, (T + p.chunk - 1) / p.chunk);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.merge_off = p.part_off + al((size_t)B * Hq * p.nsplit * (2 + 2 * (size_t)WD_D) * 4);
+  p.total = p.merge_off + (size_t)B * Hq * 2 * (size_t)WD_D * 4;
+  return p;
+}
+
 bool fast_supported(int D, int KB, int VB) {
   if (D != 128 && D != 256 && D != 512) return false;
   if (KB < 1 || KB > 4 || VB < 1 || VB > 3) return false;
@@ -1320,7 +1821,12 @@ template <int D, int KB, int VB>
 int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, int units, hipStream_t st) {
   {
     ProfScope ps("attn_prep", st);
-    hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+    if constexpr (D >= 256) {
+      if (!pa.app.on) hipLaunchKernelGGL((attn_fast_prep_wide_kernel<D, KB>), dim3(units), dim3(1024), 0, st, pa);
+      else hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+    } else {
+      hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+    }
   }
   int rc = launch_check();
   if (rc != TQ_OK) return rc;
@@ -1335,6 +1841,7 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   size_t n = 0;
   for (int vb = 1; vb <= 3; ++vb) n = std::max(n, fast_plan(D, KB, vb, B, Hq, Hkv, T).total);
   if (wave_supported(D, KB, 1)) n = std::max(n, wave_plan(D, KB, B, Hq, Hkv, T).total);
+  if (wide_supported(D, KB, 1)) n = std::max(n, wide_plan(KB, B, Hq, Hkv, T).total);
   return n;
 }
 
@@ -1351,6 +1858,11 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   // the wave-streaming kernel stages 16-byte pieces: sequence rows of the fp16 arrays must stay aligned
   const bool wave = wave_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) && aligned16(knorms) &&
                     aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas);
+  // head dim 512 with 1-bit value indices: the eight-wave kernel (16-byte staged pieces, int32 stage offsets)
+  const bool widek = !wave && wide_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) &&
+                     aligned16(knorms) && aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas) &&
+                     Tstride * (int64_t)(KB * D / 8) < (int64_t(1) << 31);
+  if (widek) fp = wide_plan(KB, B, Hq, Hkv, Tstride);
   if (wave) {
     const WavePlan wp = wave_plan(D, KB, B, Hq, Hkv, Tstride);
     fp.nsplit = wp.nsplit;
@@ -1399,6 +1911,35 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       if (KB == 1) hipLaunchKernelGGL(attn_wave_kernel<1>, grid, dim3(64), 0, st, fa);
       if (KB == 2) hipLaunchKernelGGL(attn_wave_kernel<2>, grid, dim3(64), 0, st, fa);
       if (KB == 3) hipLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, fa);
+    }
+    if ((rc = launch_check()) != TQ_OK) return rc;
+    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+                        st);
+  }
+  if (widek) {
+    {
+      ProfScope ps("attn_prep", st);
+      const bool app_on = app && app->on;
+      if (KB == 1) {
+        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 1, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 1, true>), dim3(units), dim3(1024), 0, st, pa);
+      }
+      if (KB == 2) {
+        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 2, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 2, true>), dim3(units), dim3(1024), 0, st, pa);
+      }
+      if (KB == 3) {
+        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 3, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 3, true>), dim3(units), dim3(1024), 0, st, pa);
+      }
+    }
+    if ((rc = launch_check()) != TQ_OK) return rc;
+    {
+      ProfScope ps("attn_wide", st);
+      const dim3 grid((unsigned)units, (unsigned)fp.nsplit);
+      if (KB == 1) hipLaunchKernelGGL(attn_wide_kernel<1>, grid, dim3(WD_THREADS), 0, st, fa);
+      if (KB == 2) hipLaunchKernelGGL(attn_wide_kernel<2>, grid, dim3(WD_THREADS), 0, st, fa);
+      if (KB == 3) hipLaunchKernelGGL(attn_wide_kernel<3>, grid, dim3(WD_THREADS), 0, st, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
