@@ -286,7 +286,9 @@ int tq_attn_decode_noalloc(const tq_quantizer *kq, const tq_quantizer *vq, const
  *     returns the summed elapsed time and number of launches whose name
  *     contains `name` (NULL or "" = all).  Launch names: attn_prep, attn_wave
  *     (the wave-streaming attention kernel), attn_fast (the 4-wave one),
- *     attn_qrot, attn_split (row records), attn_combine, encode_mse,
+ *     attn_wide (the eight-wave head-dim-512 one), attn_qrot_rows (query
+ *     rotation at head dim 512), attn_qrot, attn_split (row records),
+ *     attn_combine, encode_mse,
  *     encode_prod, encode_norm, encode_rotate, encode_qjl, decode, score_qrot,
  *     score_prep, score_scan, topk, tile_records.
  *   tq_profile_select(name): while enabled, records only the launches whose

@@ -296,46 +296,59 @@ __global__ __launch_bounds__(256) void attn_rotate_kernel(const float *merged, i
 }
 
 // head dims above 256 (multiples of 256): HB rows per work-group, so that each entry of Pi and S read
-// serves all of them; eight slices of 2d / 8 terms (the first four pair with rows of Pi, the rest with
-// rows of S), walked 16 terms at a time (the matrix entries coalesced across the 32 columns, the rows'
-// terms read as 16-byte pieces every lane of a slice shares)
+// serves all of them; 512 threads = 16 slices of 2d / 16 terms (the first half pair with rows of Pi, the
+// rest with rows of S) x 32 columns.  A thread loads its slice's matrix entries (coalesced across the 32
+// columns) all at once, so one memory round trip covers them; the rows' terms are staged in LDS.
 template <int HB>
-__global__ __launch_bounds__(256) void attn_rotate_wide_kernel(const float *merged, int64_t BH, int d, const float *pi,
+__global__ __launch_bounds__(512) void attn_rotate_wide_kernel(const float *merged, int64_t BH, int d, const float *pi,
                                                                const float *s, float *out) {
-  __shared__ float red[HB][8][33];
+  constexpr int NSL = 16, PER = 64;  // slices and terms per slice (2d = 1024 at head dim 512)
+  extern __shared__ __attribute__((aligned(16))) float arows[];  // [HB][2d]
+  __shared__ float red[HB][NSL][33];
   const int64_t bh0 = (int64_t)blockIdx.x * HB;
-  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int tid = threadIdx.x, c = tid & 31, sl = tid >> 5;
   const int j = blockIdx.y * 32 + c;
-  const int per = 2 * d / 8, t0 = sl * per;
-  const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
-  float acc[HB];
+  // the rows' terms into LDS, 16 unconditional loads per thread at a time (clamped indices)
+  for (int e0 = 0; e0 < HB * 2 * d; e0 += 512 * 16) {
+    float v[16];
 #pragma unroll
-  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
-  for (int i0 = 0; i0 < per; i0 += 16) {
-    float m[16];
+    for (int u = 0; u < 16; ++u) {
+      const int e = imin32(e0 + 512 * u + tid, HB * 2 * d - 1);
+      v[u] = merged[imin64(bh0 + e / (2 * d), BH - 1) * 2 * d + e % (2 * d)];
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m[i] = mrow[(int64_t)(i0 + i) * d];
+    for (int u = 0; u < 16; ++u)
+      if (e0 + 512 * u + tid < HB * 2 * d) arows[e0 + 512 * u + tid] = v[u];
+  }
+  for (int t0 = sl * PER; t0 < 2 * d; t0 += NSL * PER) {  // one pass at head dim 512
+    const float *mrow = t0 < d ? pi + (int64_t)t0 * d + j : s + (int64_t)(t0 - d) * d + j;
+    float m[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m[i] = mrow[(int64_t)i * d];
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
+    __syncthreads();  // (first pass) the rows are staged
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
-      const float4 *A = reinterpret_cast<const float4 *>(merged + imin64(bh0 + h, BH - 1) * 2 * d + t0 + i0);
-      const float4 a0 = A[0], a1 = A[1], a2 = A[2], a3 = A[3];
-      const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                            a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-      float v = acc[h];
+      const float4 *A = reinterpret_cast<const float4 *>(arows + h * 2 * d + t0);
+      float v = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v = fmaf(m[i], av[i], v);
-      acc[h] = v;
+      for (int i = 0; i < PER / 4; ++i) {
+        const float4 a4 = A[i];
+        v = fmaf(m[4 * i], a4.x, v);
+        v = fmaf(m[4 * i + 1], a4.y, v);
+        v = fmaf(m[4 * i + 2], a4.z, v);
+        v = fmaf(m[4 * i + 3], a4.w, v);
+      }
+      red[h][sl][c] = (t0 == sl * PER ? 0.f : red[h][sl][c]) + v;
     }
   }
-#pragma unroll
-  for (int h = 0; h < HB; ++h) red[h][sl][c] = acc[h];
   __syncthreads();
   if (sl == 0) {
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
-      float v = acc[h];
+      float v = 0.f;
 #pragma unroll
-      for (int q = 1; q < 8; ++q) v += red[h][q][c];
+      for (int q = 0; q < NSL; ++q) v += red[h][q][c];
       if (bh0 + h < BH) out[(bh0 + h) * d + j] = v;
     }
   }
@@ -471,8 +484,8 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, 
     default: {
       // larger head dims (multiples of 256): eight rows per work-group
       if (d % 256 != 0) return TQ_ERR_UNSUPPORTED;
-      hipLaunchKernelGGL(attn_rotate_wide_kernel<8>, dim3((unsigned)cdiv64(BH, 8), (unsigned)(d / 32)), dim3(256), 0,
-                         st, merged, (int64_t)BH, d, pi, s, out);
+      hipLaunchKernelGGL(attn_rotate_wide_kernel<8>, dim3((unsigned)cdiv64(BH, 8), (unsigned)(d / 32)), dim3(512),
+                         (size_t)8 * 2 * d * 4, st, merged, (int64_t)BH, d, pi, s, out);
     }
   }
   return launch_check();

@@ -1137,6 +1137,7 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
 
   float m_ref = -INFINITY, vn_ref = 0.f, vg_ref = 0.f, m_top = -INFINITY;
   int since_fold = 0, down_seg = FA_MINSEG, since_down = 1 << 30;
+  float sm = 0.f, sq = 0.f, ism = 0.f, isq = 0.f;  // weight scales (set at each fold) and their inverses
   float l_run = 0.f, ym_run = 0.f, yq_run = 0.f;
   float accf[2][NTC];
   intx4 vacc[2][NTC];
@@ -1219,7 +1220,9 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
     const float fvn = tvalid ? f16_to_f32((uint16_t)hv) : 0.f;
     const float fvg = tvalid ? f16_to_f32((uint16_t)hg) : 0.f;
     float sc = (head_ok && tvalid) ? fmaf(v, qinv2, -qconst2) * f16_to_f32((uint16_t)hk) : -INFINITY;
-    // ---- reference test (the work-group's flags) ----
+    // ---- reference test (the work-group's flags) and the weight of (head hl, token tw) against the current
+    // reference, p n and p gamma as four 7-bit digits each; one barrier publishes both.  When the flags
+    // call for a fold (rare after the first step) the reference moves and the weight is made again. ----
     {
       const bool over = sc > m_ref + FA_SLACK;
       const bool near = sc >= m_ref - REF_DROP;
@@ -1232,7 +1235,25 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
       for (int h = 0; h < FA_GMAX; ++h) flag |= ((wave_near >> (16 * h)) & 0xFFFFull) != 0 ? 2 << h : 0;
       if (lane == 0) s_flag[wave] = flag;
     }
-    wd_barrier();  // flags visible
+    float p;
+    uint32_t um, uq;
+    auto weigh = [&]() {
+      p = sc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc - m_ref);
+      um = __float2uint_rn(p * fvn * sm);
+      uq = __float2uint_rn(p * fvg * sq);
+      if (head_ok) {
+        s_wm[tt][4 * hl + 0][slot] = (uint8_t)(um >> 21);
+        s_wm[tt][4 * hl + 1][slot] = (uint8_t)((um >> 14) & 127u);
+        s_wm[tt][4 * hl + 2][slot] = (uint8_t)((um >> 7) & 127u);
+        s_wm[tt][4 * hl + 3][slot] = (uint8_t)(um & 127u);
+        s_wq[tt][4 * hl + 0][slot] = (uint8_t)(uq >> 21);
+        s_wq[tt][4 * hl + 1][slot] = (uint8_t)((uq >> 14) & 127u);
+        s_wq[tt][4 * hl + 2][slot] = (uint8_t)((uq >> 7) & 127u);
+        s_wq[tt][4 * hl + 3][slot] = (uint8_t)(uq & 127u);
+      }
+    };
+    weigh();
+    wd_barrier();  // flags and weight digits visible
     int flags = 0;
 #pragma unroll
     for (int w = 0; w < WD_WAVES; ++w) flags |= s_flag[w];
@@ -1243,7 +1264,7 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
     if ((flags & 33) || low || since_fold >= WD_FOLDMAX) {
       if ((flags & 1) && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, FA_MAXSEG);
       if (low) since_down = 0;
-      // rare: move the reference to this step's maxima and fold the int32 accumulators
+      // move the reference to this step's maxima and fold the int32 accumulators
       const float smax = rows16_max(sc);
       const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
       if (ln == 0) s_max[wave][hl] = smax;
@@ -1261,14 +1282,14 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
       const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
       const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float isc = p == 0 ? im : iq;
+      for (int pl = 0; pl < 2; ++pl) {
+        const float isc = pl == 0 ? im : iq;
 #pragma unroll
         for (int c = 0; c < NTC; ++c) {
-          const float x = (((float)vacc[p][c][0] * 128.f + (float)vacc[p][c][1]) * 128.f + (float)vacc[p][c][2]) *
-                              128.f + (float)vacc[p][c][3];
-          accf[p][c] = (accf[p][c] + x * isc) * alpha;
-          vacc[p][c] = intx4{0, 0, 0, 0};
+          const float x = (((float)vacc[pl][c][0] * 128.f + (float)vacc[pl][c][1]) * 128.f + (float)vacc[pl][c][2]) *
+                              128.f + (float)vacc[pl][c][3];
+          accf[pl][c] = (accf[pl][c] + x * isc) * alpha;
+          vacc[pl][c] = intx4{0, 0, 0, 0};
         }
       }
       l_run *= alpha;
@@ -1277,30 +1298,18 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
       m_ref = m_new;
       vn_ref = fmaxf(vn_ref, FA_NCAP * step_vn);
       vg_ref = fmaxf(vg_ref, FA_NCAP * step_vg);
+      // p <= 2^FA_SLACK and n <= vn_ref, so p n sm <= WMAX kscale
+      sm = vn_ref > 0.f ? WMAX * kscale / (vn_ref * FA_HEADROOM) : 0.f;
+      sq = vg_ref > 0.f ? WMAX * kscale / (vg_ref * FA_HEADROOM) : 0.f;
+      ism = sm > 0.f ? 1.f / sm : 0.f;
+      isq = sq > 0.f ? 1.f / sq : 0.f;
       since_fold = 0;
+      weigh();       // against the moved reference
+      wd_barrier();  // the new digits visible
     }
-    // ---- weight of (head hl, token tw): p n and p gamma as four 7-bit digits ----
-    {
-      const float sm = vn_ref > 0.f ? WMAX * kscale / (vn_ref * FA_HEADROOM) : 0.f;
-      const float sq = vg_ref > 0.f ? WMAX * kscale / (vg_ref * FA_HEADROOM) : 0.f;
-      const float ism = sm > 0.f ? 1.f / sm : 0.f, isq = sq > 0.f ? 1.f / sq : 0.f;
-      const float p = sc == -INFINITY ? 0.f : exp2f(sc - m_ref);
-      l_run += p;
-      const uint32_t um = __float2uint_rn(p * fvn * sm), uq = __float2uint_rn(p * fvg * sq);
-      ym_run = fmaf((float)um, ism, ym_run);
-      yq_run = fmaf((float)uq, isq, yq_run);
-      if (head_ok) {
-        s_wm[tt][4 * hl + 0][slot] = (uint8_t)(um >> 21);
-        s_wm[tt][4 * hl + 1][slot] = (uint8_t)((um >> 14) & 127u);
-        s_wm[tt][4 * hl + 2][slot] = (uint8_t)((um >> 7) & 127u);
-        s_wm[tt][4 * hl + 3][slot] = (uint8_t)(um & 127u);
-        s_wq[tt][4 * hl + 0][slot] = (uint8_t)(uq >> 21);
-        s_wq[tt][4 * hl + 1][slot] = (uint8_t)((uq >> 14) & 127u);
-        s_wq[tt][4 * hl + 2][slot] = (uint8_t)((uq >> 7) & 127u);
-        s_wq[tt][4 * hl + 3][slot] = (uint8_t)(uq & 127u);
-      }
-    }
-    wd_barrier();  // weight digits of the step's 128 tokens visible
+    l_run += p;
+    ym_run = fmaf((float)um, ism, ym_run);
+    yq_run = fmaf((float)uq, isq, yq_run);
     // ---- value pass: 128 tokens x this wave's 64 columns, both kinds ----
     {
 #pragma unroll
@@ -1385,6 +1394,7 @@ struct PrepArgs {
   float ctop;
   int *qimg;
   float *qinfo;
+  const float *qp_in;  // rotated queries [B * Hq][D] fp32 made by attn_qrot_rows_kernel (null: rotate here)
   AppendArgs app;  // the decode step's new token (app.on): key and value encoded by the work-groups of heads 0
                    // and 1 of subgroup 0
 };
@@ -1501,6 +1511,77 @@ __device__ __forceinline__ void prep_images(const PrepArgs &a, int unit, int h, 
   }
 }
 
+// rotated queries q' = Pi q (q'_j = sum_k Pi^T[k][j] q_k) of R rows at head dims of 512 and more, into
+// q' [R][d] fp32: HB rows per work-group (their q staged in LDS), 32 columns, eight slices of the terms
+// added through LDS, so each Pi^T entry read serves HB rows and the d x d matrix is spread over many
+// work-groups (a work-group per head would stream the whole matrix through one compute unit); a thread
+// loads the 64 matrix entries of a pass at once, so one memory round trip covers them
+template <int HB>
+__global__ __launch_bounds__(256) void attn_qrot_rows_kernel(const void *q, int qt, int64_t R, int d,
+                                                             const float *piT, float *out) {
+  extern __shared__ __attribute__((aligned(16))) float qrows[];  // [HB][d]
+  __shared__ float red[HB][8][33];
+  const int64_t r0 = (int64_t)blockIdx.x * HB;
+  const int tid = threadIdx.x, c = tid & 31, sl = tid >> 5;
+  // (the element type is uniform: one branch around the whole staging; 16 unconditional loads per thread
+  // at a time, at clamped indices, so they are in flight together)
+  auto stage = [&](auto conv, auto ptr) {
+    const int n = HB * d;
+    for (int e0 = 0; e0 < n; e0 += 256 * 16) {
+      decltype(conv(ptr[0])) v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = imin32(e0 + 256 * u + tid, n - 1);
+        v[u] = conv(ptr[imin64(r0 + e / d, R - 1) * d + e % d]);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (e0 + 256 * u + tid < n) qrows[e0 + 256 * u + tid] = v[u];
+    }
+  };
+  if (qt == TQ_F32) stage([](float x) { return x; }, static_cast<const float *>(q));
+  else if (qt == TQ_BF16) stage([](uint16_t x) { return bf16_to_f32(x); }, static_cast<const uint16_t *>(q));
+  else stage([](uint16_t x) { return f16_to_f32(x); }, static_cast<const uint16_t *>(q));
+  __syncthreads();
+  const int j = blockIdx.y * 32 + c;
+  constexpr int PER = 64;  // terms per pass: a thread's 64 matrix entries are loaded at once
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+  for (int k0 = sl * PER; k0 < d; k0 += 8 * PER) {  // one pass at head dim 512
+    float m[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m[i] = piT[(int64_t)(k0 + i) * d + j];
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      const float4 *qv = reinterpret_cast<const float4 *>(qrows + h * d + k0);
+      float v = acc[h];
+#pragma unroll
+      for (int i = 0; i < PER / 4; ++i) {
+        const float4 a4 = qv[i];
+        v = fmaf(m[4 * i], a4.x, v);
+        v = fmaf(m[4 * i + 1], a4.y, v);
+        v = fmaf(m[4 * i + 2], a4.z, v);
+        v = fmaf(m[4 * i + 3], a4.w, v);
+      }
+      acc[h] = v;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) red[h][sl][c] = acc[h];
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      float v = acc[h];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) v += red[h][t][c];
+      if (r0 + h < R) out[(r0 + h) * d + j] = v;
+    }
+  }
+}
+
 // images for the fp8 x fp4 matrix-core key passes: one work-group per (unit, head of its group), so the
 // four heads' images are made in parallel
 template <int D, int KB, bool PERM = false>
@@ -1521,6 +1602,12 @@ __global__ __launch_bounds__(256) void attn_fast_prep_kernel(PrepArgs a) {
   if (a.app.on && sub == 0 && h < 2) {  // the key by head 0's work-group, the value by head 1's
     __shared__ AppendShared app_sh;
     append_token(a.app, b, g, h, app_sh);
+  }
+  if (a.qp_in) {  // rotated by attn_qrot_rows_kernel
+    for (int j = tid; j < D; j += 256) qp[j] = present ? a.qp_in[((int64_t)b * a.Hq + h0 + h) * D + j] : 0.f;
+    __syncthreads();
+    prep_images<D, KB, PERM>(a, unit, h, present, qp, red, tid);
+    return;
   }
   for (int j = tid; j < D; j += 256) {
     float v = 0.f;
@@ -1822,7 +1909,7 @@ int launch_fast(const FastPlan &fp, const FastAttnArgs &fa, const PrepArgs &pa, 
   {
     ProfScope ps("attn_prep", st);
     if constexpr (D >= 256) {
-      if (!pa.app.on) hipLaunchKernelGGL((attn_fast_prep_wide_kernel<D, KB>), dim3(units), dim3(1024), 0, st, pa);
+      if (!pa.app.on && !pa.qp_in) hipLaunchKernelGGL((attn_fast_prep_wide_kernel<D, KB>), dim3(units), dim3(1024), 0, st, pa);
       else hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
     } else {
       hipLaunchKernelGGL((attn_fast_prep_kernel<D, KB>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
@@ -1885,6 +1972,19 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   pa.qimg = reinterpret_cast<int *>(w + fp.img_off);
   pa.qinfo = reinterpret_cast<float *>(w + fp.info_off);
   if (app) pa.app = *app;
+  int rc = TQ_ERR_UNSUPPORTED;
+  if (D >= 512 && B > 0) {
+    // the rotated queries of all B * Hq heads first, spread over many work-groups (into the merge area,
+    // which the split merge uses only after the attention kernel)
+    float *qp = reinterpret_cast<float *>(w + fp.merge_off);
+    {
+      ProfScope ps("attn_qrot_rows", st);
+      hipLaunchKernelGGL(attn_qrot_rows_kernel<8>, dim3((unsigned)cdiv64((int64_t)B * Hq, 8), (unsigned)(D / 32)),
+                         dim3(256), (size_t)8 * D * 4, st, q, qt, (int64_t)B * Hq, D, kq->piT, qp);
+    }
+    if ((rc = launch_check()) != TQ_OK) return rc;
+    pa.qp_in = qp;
+  }
   FastAttnArgs fa{};
   fa.qimg = pa.qimg; fa.qinfo = pa.qinfo; fa.kcodes = kcodes; fa.knorms = knorms; fa.vtiles = vtiles;
   fa.vnorms = vnorms; fa.vgammas = vgammas; fa.seq_len = seq_len;
@@ -1896,7 +1996,6 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   fa.vqjl = vq->qjl_scale;
   for (int i = 0; i < 4; ++i) fa.vbeta[i] = (float)vb64[i];
   for (int i = 0; i < 8; ++i) fa.kbeta[i] = (float)kb64[i];
-  int rc = TQ_ERR_UNSUPPORTED;
   if (wave) {
     {
       ProfScope ps("attn_prep", st);
@@ -1921,15 +2020,15 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       ProfScope ps("attn_prep", st);
       const bool app_on = app && app->on;
       if (KB == 1) {
-        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 1, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        if (app_on || pa.qp_in) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 1, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
         else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 1, true>), dim3(units), dim3(1024), 0, st, pa);
       }
       if (KB == 2) {
-        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 2, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        if (app_on || pa.qp_in) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 2, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
         else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 2, true>), dim3(units), dim3(1024), 0, st, pa);
       }
       if (KB == 3) {
-        if (app_on) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 3, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
+        if (app_on || pa.qp_in) hipLaunchKernelGGL((attn_fast_prep_kernel<WD_D, 3, true>), dim3(units, FA_GMAX), dim3(256), 0, st, pa);
         else hipLaunchKernelGGL((attn_fast_prep_wide_kernel<WD_D, 3, true>), dim3(units), dim3(1024), 0, st, pa);
       }
     }
