@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
     ap.add_argument("--cpu-encode-rows", type=int, default=524288, help="rows per kind the oracle encodes")
-    ap.add_argument("--only", choices=["", "encode", "attention", "global"], default="",
+    ap.add_argument("--only", choices=["", "encode", "attention", "global", "search"], default="",
                     help="a short run of one part (for counter profiles): the one-layer encode, the timed "
-                         "attention steps, or the global-layer attention steps")
+                         "attention steps, the global-layer attention steps, or the search scan")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
@@ -127,6 +127,36 @@ def global_only(steps: int, warmup: int):
                                            "gbs": round(pk / dt / 1e9, 2)}}), flush=True)
 
 
+def search_only(steps: int):
+    """The search workload (10^6 records of d 1536, prod 4-bit, 1000 queries, top-10): encode once, then the
+    scan + top-k `steps` times, for counter profiles; prints one JSON line."""
+    import torch
+    from vector_quantization_rotation_amd import _lib, api, synth, workloads
+    SS = workloads.SEARCH
+    X = workloads.search_database()
+    sq = api.Quantizer(SS["d"], SS["bits"], api.TQ_PROD, synth.haar_rotation(SS["d"], SS["seeds"]["pi"]),
+                       synth.gaussian_projection(SS["d"], SS["seeds"]["s"]))
+    sc, sn, sg = sq.encode(X)
+    del X
+    torch.cuda.empty_cache()
+    Qs = torch.from_numpy(workloads.search_queries()).cuda()
+    sq.score(Qs, sc, sn, sg, k=SS["k"])
+    torch.cuda.synchronize()
+    _lib.profile_reset()
+    _lib.profile_select("score_scan")
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sq.score(Qs, sc, sn, sg, k=SS["k"])
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    _lib.profile_enable(False)
+    _lib.profile_select("")
+    scan_ms, scan_n = _lib.profile_query("score_scan")
+    print(json.dumps({"search": {"scan_topk_ms": round(dt * 1e3, 4),
+                                 "scan_kernel_ms": round(scan_ms / max(scan_n, 1), 4)}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -147,6 +177,9 @@ def main():
         return
     if args.only == "global":
         global_only(args.steps, args.warmup)
+        return
+    if args.only == "search":
+        search_only(args.steps)
         return
 
     # ---------------- decode attention (timed steps) ----------------
