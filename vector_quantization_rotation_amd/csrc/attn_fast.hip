@@ -996,37 +996,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 }
 
 // ---------------------------------------------------------------------------
-// Head dim 512 with 1-bit value indices (the global-layer shape): a work-group of eight waves walks
-// 128-token steps of one (batch, KV head, four-head group, chunk).
+// Head dim 512 with 1-bit value indices (the global-layer shape): a work-group of WD_WAVES (four) waves
+// walks steps of 16 tokens per wave (64) of one (batch, KV head, four-head group, chunk).
 //
 // * Each step is staged in LDS by direct-to-LDS loads issued two steps ahead into a three-slot ring:
-//   the step's key records as they lie in HBM, its four token-tiled value words per plane and
-//   coordinate, and the three fp16 arrays.  Nothing in flight occupies registers, so two waves share
-//   each SIMD (the register-prefetching attn_fast_kernel runs one).  Every wave loads an equal share
-//   of each stage and waits for its own loads; a work-group barrier then makes the stage visible.
+//   the step's key records as they lie in HBM, its token-tiled value words per plane and coordinate,
+//   and the three fp16 arrays.  Nothing in flight occupies registers, and the ring of a four-wave
+//   work-group is small enough (67 KB at 3-bit keys) for two work-groups per CU: the two waves that share
+//   a SIMD belong to different work-groups and are not held in step by barriers, so one's vector work
+//   overlaps the other's matrix-core work.  Every wave loads an equal share of each stage and waits for
+//   its own loads; a work-group barrier then makes the stage visible.
 // * Wave w scores tokens 16 w .. 16 w + 15 of the step on the fp8 x fp4 matrix cores, one query image
 //   per 128-coordinate block with the key codebook's Walsh coefficients applied to the per-plane sums
-//   (at 1-bit keys, one plane, folded into the image), as attn_fast_kernel at this head dim.  Lane group g of block wb carries key word 4 g + wb of a
-//   plane, so a lane reads the four blocks' words of a plane as one 16-byte piece of the record; the
-//   query images follow the same order.
+//   (at 1-bit keys, one plane, folded into the image), as attn_fast_kernel at this head dim.  Lane
+//   group g of block wb carries key word 4 g + wb of a plane, so a lane reads the four blocks' words of
+//   a plane as one 16-byte piece of the record; the query images follow the same order.
 // * Each lane weighs one (head, token): p n and p gamma as 28-bit integers in four 7-bit digits written
-//   to the byte of the value operand's contraction slot that holds the token's bit, then all 128
-//   tokens are aggregated by every wave for its 64 value columns on the int8 matrix cores.
+//   to the byte of the value operand's contraction slot that holds the token's bit, then the step's
+//   tokens are aggregated by every wave for its 128 value columns on the int8 matrix cores.
 // * The softmax reference (running maximum per head, value norm and gamma caps, headroom, downward
 //   moves behind a dominant token) is shared by the work-group as in attn_fast_kernel.
 // ---------------------------------------------------------------------------
 constexpr int WD_D = 512;
-constexpr int WD_STEP = 128;     // tokens per step: eight waves x 16
-constexpr int WD_WAVES = 8;
+constexpr int WD_WAVES = 4;
+constexpr int WD_STEP = 16 * WD_WAVES;  // tokens per step: 16 per wave
 constexpr int WD_THREADS = 64 * WD_WAVES;
+constexpr int WD_TT = WD_STEP / 64;     // 64-token tiles of the value operand per step
+constexpr int WD_COLS = WD_D / WD_WAVES;  // value columns per wave
+constexpr int WD_NH = WD_COLS / 64;     // 16-byte reads of a value word row per lane (4 columns each)
 constexpr int WD_FOLDMAX = 1024; // steps between folds at most: the int32 digit sums stay below 2^31
 
 template <int KB>
 struct WideStage {
   static constexpr int KCB = KB * WD_D / 8;                    // key record bytes
   static constexpr int KEYS = WD_STEP * KCB;                   // the step's key records
-  static constexpr int VALS = (WD_STEP / 32) * 2 * WD_D * 4;   // four tile words x two planes x 512 coordinates
-  static constexpr int NORMS = 4 * WD_STEP * 2;                // n_K, n_V, gamma_V, and a landing zone
+  static constexpr int VALS = (WD_STEP / 32) * 2 * WD_D * 4;   // tile words x two planes x 512 coordinates
+  static constexpr int NORMS = 4 * 256;                        // n_K, n_V, gamma_V (256 B each), a landing zone
   static constexpr int BYTES = KEYS + VALS + NORMS;
   static constexpr int KLOADS = KEYS / 1024 / WD_WAVES;        // 1 KiB direct-to-LDS loads per wave
   static constexpr int VLOADS = VALS / 1024 / WD_WAVES;
@@ -1034,10 +1039,11 @@ struct WideStage {
   static_assert(KEYS % (1024 * WD_WAVES) == 0 && VALS % (1024 * WD_WAVES) == 0, "stage split");
 };
 
-// this wave's share of the loads of one stage (tokens t0 .. t0 + 127).  Waves 0..2 fetch the three fp16
-// arrays; the others aim past every buffer (zeros into the stage's landing zone, no memory touched), so
-// every wave issues the same number of loads, all into the one LDS object of the slot.  Reads past the
-// chunk return zeros.
+// this wave's share of the loads of one stage (tokens t0 .. t0 + WD_STEP - 1).  Waves 0..2 fetch the three
+// fp16 arrays, a dword (two tokens) per lane into 256-byte regions (lanes past the step's tokens, and the
+// other waves, aim past every buffer: zeros into the region's tail or the stage's landing zone, no memory
+// touched), so every wave issues the same number of loads, all into the one LDS object of the slot.  Reads
+// past the chunk return zeros.
 template <int KB>
 __device__ __forceinline__ void wd_stage_load(uint8_t *stage, __amdgpu_buffer_rsrc_t rk,
                                               __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rkn,
@@ -1060,8 +1066,9 @@ __device__ __forceinline__ void wd_stage_load(uint8_t *stage, __amdgpu_buffer_rs
   const int sn = __builtin_amdgcn_readfirstlane((int)(t0 * 2));
   const bool real = wave < 3;
   const __amdgpu_buffer_rsrc_t rn = wave == 0 ? rkn : (wave == 1 ? rvn : rvg);
+  const bool fetch = real && lane < WD_STEP / 2;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void_t *)(stage + S::KEYS + S::VALS + (real ? wave : 3) * 256), 4,
-                                           real ? lane * 4 : 0x7FFFFF00, real ? sn : 0, 0, 0);
+                                           fetch ? lane * 4 : 0x7FFFFF00, real ? sn : 0, 0, 0);
 }
 
 // every LDS access of this wave issued before has completed, then a work-group barrier (the
@@ -1075,13 +1082,13 @@ __device__ __forceinline__ void wd_barrier() {
 }
 
 template <int KB>
-__global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
+__global__ __launch_bounds__(WD_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attn_wide_kernel(FastAttnArgs a) {
   constexpr int D = WD_D;
   constexpr int KP = walsh_count(KB);
   constexpr int NB = D / 128;        // 128-coordinate blocks
   constexpr bool FOLD = fold_beta(D, KB);  // one image per block, Walsh coefficients after the MFMA (2-3-bit keys)
   constexpr int NI8 = (FOLD ? 1 : KP) * NB;  // query images (1-bit keys: one per block, 2 beta folded in)
-  constexpr int NTC = 4;             // value columns of a lane: 64 w + 4 ln + c
+  constexpr int NTC = 4 * WD_NH;     // value columns of a lane: WD_COLS w + 64 (c / 4) + 4 ln + c % 4
   constexpr float WMAX = 268435328.f;  // 2^28 - 128 (see attn_fast_kernel)
   using S = WideStage<KB>;
 
@@ -1091,8 +1098,8 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_ring2[S::BYTES];
   // weight digits [token tile][row][slot] of p n (s_wm) and p gamma (s_wq), two objects so that the compiler
   // keeps their accesses apart from the loads in flight
-  __shared__ __attribute__((aligned(16))) uint8_t s_wm[2][16][64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_wq[2][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_wm[WD_TT][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_wq[WD_TT][16][64];
   __shared__ int s_flag[WD_WAVES];
   __shared__ float s_max[WD_WAVES][FA_GMAX + 2];
   __shared__ float s_merge[WD_WAVES][FA_GMAX][3];
@@ -1170,15 +1177,17 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
     uint4 kw4[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) kw4[p] = *reinterpret_cast<const uint4 *>(st + tw * S::KCB + p * (D / 8) + 16 * hl);
-    uint4 vw4[2][2];  // [token tile][plane]: columns 64 w + 4 ln .. + 3 of this lane group's tile word
+    uint4 vw4[WD_TT][2][WD_NH];  // [token tile][plane][half]: 4 columns of this lane group's tile word each
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < WD_TT; ++t2)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        vw4[t2][p] = *reinterpret_cast<const uint4 *>(st + S::KEYS +
-                                                      ((2 * (2 * t2 + (hl >> 1)) + p) * D + 64 * wave + 4 * ln) * 4);
+#pragma unroll
+        for (int hh = 0; hh < WD_NH; ++hh)
+          vw4[t2][p][hh] = *reinterpret_cast<const uint4 *>(
+              st + S::KEYS + ((2 * (2 * t2 + (hl >> 1)) + p) * D + WD_COLS * wave + 64 * hh + 4 * ln) * 4);
     const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
-    const uint32_t hk = nrm[tw], hv = nrm[WD_STEP + tw], hg = nrm[2 * WD_STEP + tw];
+    const uint32_t hk = nrm[tw], hv = nrm[128 + tw], hg = nrm[256 + tw];
     __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0): the reads are done
     __builtin_amdgcn_sched_barrier(0);
     wd_stage_load<KB>(stl, rk, rv, rkn, rvn, rvg, wave, lane, t0 + 2 * WD_STEP);
@@ -1310,14 +1319,19 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
     l_run += p;
     ym_run = fmaf((float)um, ism, ym_run);
     yq_run = fmaf((float)uq, isq, yq_run);
-    // ---- value pass: 128 tokens x this wave's 64 columns, both kinds ----
+    // ---- value pass: the step's tokens x this wave's columns, both kinds ----
     {
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
+      for (int t2 = 0; t2 < WD_TT; ++t2) {
         const intx4 wa_m = *reinterpret_cast<const intx4 *>(&s_wm[t2][ln][16 * hl]);
         const intx4 wa_q = *reinterpret_cast<const intx4 *>(&s_wq[t2][ln][16 * hl]);
-        const uint4 w0 = vw4[t2][0], w1 = vw4[t2][1];
-        const uint32_t x0[4] = {w0.x, w0.y, w0.z, w0.w}, x1[4] = {w1.x, w1.y, w1.z, w1.w};
+        uint32_t x0[NTC], x1[NTC];
+#pragma unroll
+        for (int hh = 0; hh < WD_NH; ++hh) {
+          const uint4 w0 = vw4[t2][0][hh], w1 = vw4[t2][1][hh];
+          x0[4 * hh] = w0.x; x0[4 * hh + 1] = w0.y; x0[4 * hh + 2] = w0.z; x0[4 * hh + 3] = w0.w;
+          x1[4 * hh] = w1.x; x1[4 * hh + 1] = w1.y; x1[4 * hh + 2] = w1.z; x1[4 * hh + 3] = w1.w;
+        }
 #pragma unroll
         for (int c = 0; c < NTC; ++c) {
           vacc[0][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m, value_bits(x0[c], kofs), vacc[0][c], 0, 0, 0);
@@ -1375,7 +1389,7 @@ __global__ __launch_bounds__(WD_THREADS) void attn_wide_kernel(FastAttnArgs a) {
     if (wave == 0 && ln == 0) { dst[0] = m_ref; dst[1] = L; }
 #pragma unroll
     for (int c = 0; c < NTC; ++c) {
-      const int col = 64 * wave + 4 * ln + c;
+      const int col = WD_COLS * wave + 64 * (c >> 2) + 4 * ln + (c & 3);
       dst[2 + col] = a.vbeta[0] * (2.f * accf[0][c] - YM);
       dst[2 + D + col] = a.vqjl * (2.f * accf[1][c] - YQ);
     }
@@ -1882,7 +1896,7 @@ int wide_slots(int KB) {
 }
 
 // the head-dim-512 plan: the query images and offsets as fast_plan lays them out, chunks of whole ring
-// turns (three 128-token steps), one per resident work-group
+// turns (three steps), one per resident work-group
 FastPlan wide_plan(int KB, int B, int Hq, int Hkv, int64_t T) {
   FastPlan p = fast_plan(WD_D, KB, 1, B, Hq, Hkv, T);
   const int64_t units = (int64_t)B * Hkv * p.nsub;
@@ -1945,7 +1959,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   // the wave-streaming kernel stages 16-byte pieces: sequence rows of the fp16 arrays must stay aligned
   const bool wave = wave_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) && aligned16(knorms) &&
                     aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas);
-  // head dim 512 with 1-bit value indices: the eight-wave kernel (16-byte staged pieces, int32 stage offsets)
+  // head dim 512 with 1-bit value indices: attn_wide_kernel (16-byte staged pieces, int32 stage offsets)
   const bool widek = !wave && wide_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) &&
                      aligned16(knorms) && aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas) &&
                      Tstride * (int64_t)(KB * D / 8) < (int64_t(1) << 31);
