@@ -163,6 +163,10 @@ struct EpiQuant {
     for (int k = 0; k < L; ++k) cc[k] = cb.c[k];
     const int nblk = d >> 6;
     float sq[16];  // r^2 of this lane's column, per row (summed over the block below)
+    // lane rr keeps row rr's 64 plane bits, so each plane is stored by 16 lanes at once after the rows
+    unsigned long long pm[BM > 0 ? BM : 1];
+#pragma unroll
+    for (int p = 0; p < (BM > 0 ? BM : 1); ++p) pm[p] = 0ull;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       sq[rr] = 0.f;
@@ -183,11 +187,10 @@ struct EpiQuant {
           if (idx == 2 * s * c) t = tb[2 * s * c + s - 1];
         idx += (yq > t * nq) ? s : 0;
       }
-      uint8_t *dst = codes + row * code_bytes + (col0 >> 3);
 #pragma unroll
       for (int p = 0; p < BM; ++p) {
         const unsigned long long m = __ballot(((idx >> p) & 1) != 0);
-        if (lane == 0) *reinterpret_cast<unsigned long long *>(dst + p * (d >> 3)) = m;
+        pm[p] = lane == rr ? m : pm[p];
       }
       if (resid) {
         float cv = cc[0];
@@ -198,6 +201,11 @@ struct EpiQuant {
         resid[row * d + col0 + lane] = rv;
         sq[rr] = rv * rv;
       }
+    }
+    if (BM > 0 && lane < 16 && row0 + rb + lane < M) {
+      uint8_t *dst = codes + (row0 + rb + lane) * code_bytes + (col0 >> 3);
+#pragma unroll
+      for (int p = 0; p < BM; ++p) *reinterpret_cast<unsigned long long *>(dst + p * (d >> 3)) = pm[p];
     }
     if (resid) {
       // the 16 row sums over the lanes at once (independent shuffles in flight together)
@@ -221,14 +229,16 @@ struct EpiSign {
   // rows rb..rb+15 of the tile by the calling wave (lane = column)
   __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
     const int lane = threadIdx.x & 63;
+    unsigned long long pm = 0ull;  // lane rr keeps row rr's 64 sign bits; 16 lanes store them at once
+#pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int r = rb + rr;
-      const int64_t row = row0 + r;
-      if (row >= M) break;
-      unsigned long long m = __ballot(Cs[r][lane] >= 0.0f);
-      if (lane == 0)
-        *reinterpret_cast<unsigned long long *>(codes + row * code_bytes + plane * (d >> 3) + (col0 >> 3)) = m;
+      if (row0 + rb + rr >= M) break;
+      const unsigned long long m = __ballot(Cs[rb + rr][lane] >= 0.0f);
+      pm = lane == rr ? m : pm;
     }
+    if (lane < 16 && row0 + rb + lane < M)
+      *reinterpret_cast<unsigned long long *>(codes + (row0 + rb + lane) * code_bytes + plane * (d >> 3) + (col0 >> 3)) =
+          pm;
   }
 };
 
