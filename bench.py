@@ -100,7 +100,19 @@ def encode_only(steps: int):
                                  "value": round(2 * K.shape[0] / dt, 1), "unit": "vectors/s"}}), flush=True)
 
 
-def global_only(steps: int, warmup: int):
+def copy_calibration():
+    """A plain streaming kernel of known size (reads 1 GiB, writes 1 GiB), run three times: its FETCH_SIZE
+    and WRITE_SIZE in a counter profile calibrate the HBM byte counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def global_only(steps: int, warmup: int, calib: bool = False):
     """The global-layer decode attention (batch 4, 32 query heads over 4 KV heads, head_dim 512, 65536
     tokens) run warmup + steps times, for counter profiles; prints one JSON line."""
     import torch
@@ -114,6 +126,8 @@ def global_only(steps: int, warmup: int):
     hws = torch.empty((api.attn_decode_ws_bytes(hc.kq, hB, hHq, hHkv, hT, lay),), dtype=torch.uint8, device="cuda")
     step = api.attn_decode_bound(hc.kq, hc.vq, hc.q, hc.kcodes, hc.knorms, hc.vtiles, hc.vnorms, hc.vgammas, hseq,
                                  1 / math.sqrt(hd), hout, hws, vlayout=lay)
+    if calib:
+        copy_calibration()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -176,7 +190,7 @@ def main():
         encode_only(args.steps)
         return
     if args.only == "global":
-        global_only(args.steps, args.warmup)
+        global_only(args.steps, args.warmup, args.copy_calib)
         return
     if args.only == "search":
         search_only(args.steps)
@@ -203,14 +217,7 @@ def main():
     step = api.attn_decode_bound(kq, vq, q, kc, kn, vt, vn, vg, seq, scale, out, ws, vlayout=layout)
 
     if args.copy_calib:
-        # a plain streaming kernel of known size (reads 1 GiB, writes 1 GiB): its FETCH_SIZE and
-        # WRITE_SIZE calibrate the HBM byte counters
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.add(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     for _ in range(args.warmup):
         step()
@@ -366,7 +373,8 @@ def main():
                      "encode_ms": round(het_enc * 1e3, 4), "encode_vectors_per_s": round(2 * hn / het_enc, 1),
                      "attn_ms": round(het_att * 1e3, 4), "attn_packed_bytes": hpk,
                      "attn_gbs": round(hpk / het_att / 1e9, 2),
-                     "attn_kernel": "attn_fast_kernel (token-tiled values)" if tiled else "attn_split_kernel (row records)"}
+                     "attn_kernel": ("attn_wide_kernel" if hd == 512 else "attn_fast_kernel") + " (token-tiled values)"
+                     if tiled else "attn_split_kernel (row records)"}
         log(f"{kind} layer: encode {het_enc * 1e3:.3f} ms ({2 * hn} vectors), attention {het_att * 1e3:.4f} ms "
             f"({hpk / het_att / 1e9:.1f} GB/s)")
         del hc, hout, hws

@@ -34,6 +34,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "append.cuh"
 #include "common.cuh"
 
@@ -2019,11 +2021,11 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {
-      ProfScope ps("attn_wave", st);
+      ProfKernel pk("attn_wave");
       const dim3 grid((unsigned)units, (unsigned)fp.nsplit);
-      if (KB == 1) hipLaunchKernelGGL(attn_wave_kernel<1>, grid, dim3(64), 0, st, fa);
-      if (KB == 2) hipLaunchKernelGGL(attn_wave_kernel<2>, grid, dim3(64), 0, st, fa);
-      if (KB == 3) hipLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, fa);
+      if (KB == 1) hipExtLaunchKernelGGL(attn_wave_kernel<1>, grid, dim3(64), 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 2) hipExtLaunchKernelGGL(attn_wave_kernel<2>, grid, dim3(64), 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 3) hipExtLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, pk.start, pk.stop, 0, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
@@ -2048,11 +2050,11 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     {
-      ProfScope ps("attn_wide", st);
-      const dim3 grid((unsigned)units, (unsigned)fp.nsplit);
-      if (KB == 1) hipLaunchKernelGGL(attn_wide_kernel<1>, grid, dim3(WD_THREADS), 0, st, fa);
-      if (KB == 2) hipLaunchKernelGGL(attn_wide_kernel<2>, grid, dim3(WD_THREADS), 0, st, fa);
-      if (KB == 3) hipLaunchKernelGGL(attn_wide_kernel<3>, grid, dim3(WD_THREADS), 0, st, fa);
+      ProfKernel pk("attn_wide");
+      const dim3 grid((unsigned)units, (unsigned)fp.nsplit), blk(WD_THREADS);
+      if (KB == 1) hipExtLaunchKernelGGL(attn_wide_kernel<1>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 2) hipExtLaunchKernelGGL(attn_wide_kernel<2>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 3) hipExtLaunchKernelGGL(attn_wide_kernel<3>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
     return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,

@@ -50,6 +50,18 @@ void *prof_begin(const char *name, hipStream_t st) {
   return reinterpret_cast<void *>(g_recs.size());
 }
 
+void prof_kernel_events(const char *name, hipEvent_t *start, hipEvent_t *stop) {
+  *start = *stop = nullptr;
+  if (!profiling()) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_select.empty() && std::strstr(name, g_select.c_str()) == nullptr) return;
+  hipEvent_t a = get_event(), b = get_event();
+  if (!a || !b) return;
+  g_recs.push_back(Rec{name, a, b});
+  *start = a;
+  *stop = b;
+}
+
 void prof_end(void *tok, hipStream_t st) {
   if (!tok) return;
   std::lock_guard<std::mutex> lk(g_mu);

@@ -80,6 +80,13 @@ namespace tq {
 bool profiling();
 void *prof_begin(const char *name, hipStream_t st);
 void prof_end(void *tok, hipStream_t st);
+// events that the launch itself stamps (hipExtLaunchKernel): they time the dispatch alone, not the packets
+// around it; both null when the name is not recorded
+void prof_kernel_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
+struct ProfKernel {
+  hipEvent_t start, stop;
+  explicit ProfKernel(const char *name) { prof_kernel_events(name, &start, &stop); }
+};
 struct ProfScope {
   void *tok;
   hipStream_t st;
