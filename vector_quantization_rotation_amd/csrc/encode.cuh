@@ -17,6 +17,22 @@
 //   fp32 a:  a_hi b_hi + a_hi b_mid + a_mid b_hi + a_hi b_lo +
 //            a_lo b_hi + a_mid b_mid                                    (6 MFMAs)
 // (the dropped cross terms are below 2^-23 of the product).
+// bf16 and fp16 rows take fp16 operands instead, two pieces where one is not
+// exact: each row is scaled by a power of two 2^kx so that its norm lies in
+// [2^13, 2^14) (then every coordinate converts to fp16 exactly; what falls below
+// the fp16 normal range is below 2^-38 of the norm), and the matrices are held as
+// hi + lo fp16 pieces of A 2^k (round to nearest, 2^-23 of each entry left out;
+// k puts the largest entry, or a bound on it, just under 2^14):
+//   rows:      x (Pi_hi + Pi_lo)                                       (2 MFMAs)
+//   residual:  r_hi M_hi + r_hi M_lo + r_lo M_hi                       (3 MFMAs)
+// Two rounded fp16 pieces hold an entry to 2^-22 of itself, so a coordinate of
+// Pi x carries at most 2^-22 n of representation error (2.7e-6 of the
+// coordinate scale n / sqrt(d) at d = 128) and a projection of S r at most
+// 3 2^-22 ||S_i|| ||r|| (8.1e-6 ||r|| at d = 128 with ||S_i|| ~ sqrt(d)), both
+// below the 1e-5 tie zone, beside the fp32 accumulation error of either form,
+// with 5 MFMAs where the bf16 pieces take 9.  Every power-of-two scale is undone
+// exactly: the cell boundaries and n_hat take the row's scale, gamma divides it
+// out in fp64.
 //
 // Work split.  A persistent work-group of NW waves (4; 8 for Algorithm 2 at
 // d = 128) walks 64-row tiles.  Wave w owns output columns [w d/NW, (w+1) d/NW):
@@ -33,6 +49,8 @@
 // in fp64 (the fp16 norm must round exactly as the fp64 value does).
 #pragma once
 
+#include <type_traits>
+
 #include "common.cuh"
 
 namespace tq {
@@ -40,6 +58,7 @@ namespace tq {
 constexpr int EB = 64;  // rows per tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Rows of x are nseq sequences of T tokens (a plain encode: one sequence of n rows); token t of sequence s
 // is written to position t0 + t of that sequence's cache row of Tstride positions: records (row layout)
@@ -53,6 +72,9 @@ struct EncArgs {
   int64_t t0, Tstride;   // first cache position written, positions per sequence in the cache
   const uint16_t *pi3;   // [3][D][D] pieces of Pi (row j, column k)
   const uint16_t *m3;    // [3][D][D] pieces of S Pi^T (Algorithm 2)
+  const uint16_t *pih;   // [2][D][D] fp16 pieces of Pi 2^kp (bf16 and fp16 rows)
+  const uint16_t *mh;    // [2][D][D] fp16 pieces of S Pi^T 2^km (Algorithm 2)
+  int kp, km;
   uint8_t *codes;        // row layout
   uint32_t *tiles;       // token-tiled layout (codes unused)
   int64_t code_bytes, ntile32;  // ntile32: 32-token words per sequence in the tiled cache
@@ -79,7 +101,10 @@ __device__ __forceinline__ uint32_t transpose32_bits(uint32_t a, int lane) {
 
 template <int XT>
 struct EncIn {
-  static constexpr int NPA = XT == TQ_BF16 ? 1 : (XT == TQ_F16 ? 2 : 3);  // bf16 pieces per element
+  static constexpr bool HP = XT != TQ_F32;                                // fp16 operands (one piece per row element)
+  static constexpr int NPA = HP ? 1 : 3;                                  // pieces per row element
+  static constexpr int NPB = HP ? 2 : 3;                                  // pieces per matrix entry
+  static constexpr int NPR = HP ? 2 : 3;                                  // pieces per residual element
   static constexpr int ESZ = XT == TQ_F32 ? 4 : 2;
 };
 
@@ -90,15 +115,16 @@ struct EncIn {
 // the other's matrix-core work); otherwise 4 waves
 __host__ __device__ constexpr int enc_waves(int D, bool PROD) { return PROD && D == 128 ? 8 : 4; }
 
-template <int D, int NPA, bool PROD>
+template <int D, int NPA, int NPR, bool PROD>
 struct __attribute__((aligned(16))) EncLds {
   static constexpr int NW = enc_waves(D, PROD);
   static constexpr int CW = D / NW;
   uint16_t a[NPA][EB][D + 8];          // row pieces of the tile
   float cw[NW][EB][CW + 4];            // per-wave transpose: MFMA layout -> lane = row
-  uint16_t rp[PROD ? 3 : 1][PROD ? EB : 1][D + 16];  // residual pieces (Algorithm 2; this stride measured 5 % faster than D + 8)
+  uint16_t rp[PROD ? NPR : 1][PROD ? EB : 1][D + 16];  // residual pieces (Algorithm 2; this stride measured 5 % faster than D + 8)
   float gpart[PROD ? NW : 1][EB];      // per-wave partial ||r||^2
-  float n32[2][EB], nh[2][EB];         // norms by tile parity
+  float n32[2][EB], nh[2][EB];         // norms by tile parity (times the row's scale 2^(kx + kp) for fp16 operands)
+  int ksc[2][EB];                      // kx + kp of the row (fp16 operands)
 };
 
 __device__ __forceinline__ float trunc_bf16(float x) { return __uint_as_float(__float_as_uint(x) & 0xFFFF0000u); }
@@ -125,6 +151,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ floatx4 mfma_bf16(const f16x8 &a, const f16x8 &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// two fp32 values as packed fp16, truncating (exact for the scaled row elements, see the header)
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+// x = hi + lo as fp16 pieces, each rounded to nearest
+__device__ __forceinline__ void split_f16(float x, uint16_t &hi, uint16_t &lo) {
+  const _Float16 h = (_Float16)x;
+  const _Float16 l = (_Float16)(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
 
 // the exact-piece products (A piece, B piece), smallest terms first
 template <int NPA>
@@ -144,9 +185,29 @@ struct PieceTerms<3> {
   static constexpr int N = 6;
   static constexpr int A[N] = {1, 2, 0, 1, 0, 0}, B[N] = {1, 0, 2, 0, 1, 0};
 };
+// fp16 operands: one row piece against the matrix's two
+struct PieceTermsH1 {
+  static constexpr int N = 2;
+  static constexpr int A[N] = {0, 0}, B[N] = {1, 0};
+};
+// fp16 operands: two residual pieces against the matrix's two (lo x lo left out)
+struct PieceTermsH2 {
+  static constexpr int N = 3;
+  static constexpr int A[N] = {1, 0, 0}, B[N] = {0, 1, 0};
+};
 
 // acc[rt][ct] += A rows (16 rt ..) x B columns (16 ct ..) over one 32-deep k-step,
 // term-major so that consecutive MFMAs write different accumulators
+template <typename TT, int NCT, typename V, int NA, int NB>
+__device__ __forceinline__ void contract_terms(const V (&af)[4][NA], const V (&bf)[NCT][NB], floatx4 (&acc)[4][NCT]) {
+#pragma unroll
+  for (int t = 0; t < TT::N; ++t)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = mfma_bf16(af[rt][TT::A[t]], bf[ct][TT::B[t]], acc[rt][ct]);
+}
+
 template <int NPA, int NCT>
 __device__ __forceinline__ void contract_kstep(const bf16x8 (&af)[4][3], const bf16x8 (&bf)[NCT][3],
                                                floatx4 (&acc)[4][NCT]) {
@@ -281,7 +342,9 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t w, bool b) { return (w << 
 
 template <int XT, int D, bool PROD, int BM>
 __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs a) {
-  constexpr int NPA = EncIn<XT>::NPA, ESZ = EncIn<XT>::ESZ;
+  constexpr bool HP = EncIn<XT>::HP;
+  constexpr int NPA = EncIn<XT>::NPA, NPB = EncIn<XT>::NPB, NPR = EncIn<XT>::NPR, ESZ = EncIn<XT>::ESZ;
+  using MT = std::conditional_t<HP, f16x8, bf16x8>;  // matrix-core operand type
   constexpr int NW = enc_waves(D, PROD);
   constexpr int CW = D / NW;       // columns per wave
   constexpr int NCT = CW / 16;     // 16-column MFMA tiles per wave
@@ -290,23 +353,24 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
   constexpr int PER = D / NW;      // staged elements per thread (NW threads per row)
   constexpr int RAW = PER * ESZ / 16;
   static_assert(RAW >= 1, "tile staging");
-  __shared__ EncLds<D, NPA, PROD> sh;
+  __shared__ EncLds<D, NPA, NPR, PROD> sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, g4 = lane >> 4;
 
   // ---- register-resident matrix pieces of this wave's columns ----
-  bf16x8 bpi[NKS][NCT][3];
-  bf16x8 bmq[PROD ? NKS : 1][NCT][3];
+  MT bpi[NKS][NCT][NPB];
+  MT bmq[PROD ? NKS : 1][NCT][NPB];
+  const uint16_t *pisrc = HP ? a.pih : a.pi3, *msrc = HP ? a.mh : a.m3;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
+      for (int p = 0; p < NPB; ++p) {
         const int64_t off = ((int64_t)p * D + CW * wave + 16 * ct + j16) * D + 32 * ks + 8 * g4;
-        bpi[ks][ct][p] = *reinterpret_cast<const bf16x8 *>(a.pi3 + off);
-        if (PROD) bmq[ks][ct][p] = *reinterpret_cast<const bf16x8 *>(a.m3 + off);
+        bpi[ks][ct][p] = *reinterpret_cast<const MT *>(pisrc + off);
+        if (PROD) bmq[ks][ct][p] = *reinterpret_cast<const MT *>(msrc + off);
       }
   float tb[L - 1], cc[L];
 #pragma unroll
@@ -361,9 +425,21 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       double ssq = 0.0;
 #pragma unroll
       for (int i = 0; i < PER; ++i) ssq = fma((double)v[i], (double)v[i], ssq);
-      if (XT == TQ_BF16) {
+      int kx = 0;  // the row's scale 2^kx (fp16 operands)
+      if (HP) {
 #pragma unroll
-        for (int i = 0; i < RAW; ++i) *reinterpret_cast<uint4 *>(&sh.a[0][sr][sk + 8 * i]) = raw[i];
+        for (int o = 1; o < NW; o <<= 1) ssq += __shfl_xor(ssq, o, 64);
+        const double nn = sqrt(ssq);
+        // nn = m 2^E with m in [0.5, 1): nn 2^(14 - E) lies in [2^13, 2^14), and so does no |x_i| 2^kx exceed 2^14
+        kx = nn > 0.0 ? 14 - ((int)((__double_as_longlong(nn) >> 52) & 0x7FF) - 1022) : 0;
+#pragma unroll
+        for (int i = 0; i < PER; i += 8) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pk[q] = pack_f16x2_rtz(__builtin_amdgcn_ldexpf(v[i + 2 * q], kx), __builtin_amdgcn_ldexpf(v[i + 2 * q + 1], kx));
+          *reinterpret_cast<uint4 *>(&sh.a[0][sr][sk + i]) = uint4{pk[0], pk[1], pk[2], pk[3]};
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < PER; i += 8) {
@@ -381,13 +457,17 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
             *reinterpret_cast<uint4 *>(&sh.a[p][sr][sk + i]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
         }
       }
+      if (!HP) {
 #pragma unroll
-      for (int o = 1; o < NW; o <<= 1) ssq += __shfl_xor(ssq, o, 64);
+        for (int o = 1; o < NW; o <<= 1) ssq += __shfl_xor(ssq, o, 64);
+      }
       if (tid % NW == 0) {
         const double nn = sqrt(ssq);
         const uint16_t h = f64_to_f16_rne_sat(nn);
-        sh.n32[buf][sr] = (float)nn;
-        sh.nh[buf][sr] = f16_to_f32(h);
+        const int ks = HP ? kx + a.kp : 0;
+        sh.n32[buf][sr] = __builtin_amdgcn_ldexpf((float)nn, ks);
+        sh.nh[buf][sr] = __builtin_amdgcn_ldexpf(f16_to_f32(h), ks);
+        sh.ksc[buf][sr] = ks;
         if (sr < rows) a.norms[row0 + sr] = h;
       }
     }
@@ -405,13 +485,20 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 af[4][3];
+      if constexpr (HP) {
+        f16x8 af[4][1];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) af[rt][0] = *reinterpret_cast<const f16x8 *>(&sh.a[0][16 * rt + j16][32 * ks + 8 * g4]);
+        contract_terms<PieceTermsH1, NCT>(af, bpi[ks], acc);
+      } else {
+        bf16x8 af[4][3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          af[rt][p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[rt][0];
-      contract_kstep<NPA, NCT>(af, bpi[ks], acc);
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            af[rt][p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[rt][0];
+        contract_kstep<NPA, NCT>(af, bpi[ks], acc);
+      }
     }
     lds_barrier();  // row pieces consumed
 
@@ -433,6 +520,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
 #pragma unroll
     for (int p = 0; p < BM; ++p) plane[p] = 0u;
     float rs = 0.f;  // ||r||^2 over this wave's columns (fp32: gamma is checked to 1e-5 of a midpoint)
+    const float rdn = HP ? __builtin_amdgcn_ldexpf(1.f, -a.kp) : 1.f;
 #pragma unroll
     for (int c8 = CW / 8 - 1; c8 >= 0; --c8) {
       const float4 y0 = *reinterpret_cast<const float4 *>(&cw[lane][8 * c8]);
@@ -448,7 +536,21 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
           rs = fmaf(rv[e], rv[e], rs);
         }
       }
-      if (PROD) {
+      if (PROD && HP) {
+        // r 2^(kx + kp) 2^-kp: at most 2^14 and a little (|r_i| <= max(|y_i|, n_hat |c|))
+        uint32_t pk[2][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint16_t h0, l0, h1, l1;
+          split_f16(rv[2 * q] * rdn, h0, l0);
+          split_f16(rv[2 * q + 1] * rdn, h1, l1);
+          pk[0][q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          pk[1][q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          *reinterpret_cast<uint4 *>(&sh.rp[p][lane][CW * wave + 8 * c8]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+      } else if (PROD) {
         uint32_t pk[3][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -494,6 +596,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       double g2 = 0.0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) g2 += (double)sh.gpart[w][lane];
+      if (HP) g2 = ldexp(g2, -2 * sh.ksc[buf][lane]);
       a.gammas[row0 + lane] = f64_to_f16_rne_sat(sqrt(g2));
     }
 #pragma unroll
@@ -502,12 +605,13 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 af[4][3];
+      MT af[4][NPR];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) af[rt][p] = *reinterpret_cast<const bf16x8 *>(&sh.rp[p][16 * rt + j16][32 * ks + 8 * g4]);
-      contract_kstep<3, NCT>(af, bmq[ks], acc);
+        for (int p = 0; p < NPR; ++p) af[rt][p] = *reinterpret_cast<const MT *>(&sh.rp[p][16 * rt + j16][32 * ks + 8 * g4]);
+      if constexpr (HP) contract_terms<PieceTermsH2, NCT>(af, bmq[ks], acc);
+      else contract_kstep<3, NCT>(af, bmq[ks], acc);
     }
     wave_lds_order();
 #pragma unroll

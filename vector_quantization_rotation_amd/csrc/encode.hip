@@ -20,6 +20,18 @@ int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st) {
   return launch_check();
 }
 
+// pieces [2][n] of src 2^k as fp16 hi + lo, each rounded to nearest (|src| 2^k below 2^14)
+__global__ void split2h_kernel(const float *src, int64_t n, int k, uint16_t *dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  split_f16(__builtin_amdgcn_ldexpf(src[i], k), dst[i], dst[n + i]);
+}
+
+int make_pieces_f16(const float *src, int64_t n, int k, uint16_t *dst, hipStream_t st) {
+  hipLaunchKernelGGL(split2h_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, src, n, k, dst);
+  return launch_check();
+}
+
 // compute units of the current device (cached per device)
 int device_cus() {
   static int cache[64] = {};
@@ -33,7 +45,8 @@ int device_cus() {
 }
 
 bool encode_fused_supported(const tq_quantizer *q) {
-  return (q->d == 64 || q->d == 128) && q->pi3 && q->bmse >= 1 && q->bmse <= 4 && (q->mode != TQ_PROD || q->m3);
+  return (q->d == 64 || q->d == 128) && q->pi3 && q->pih && q->bmse >= 1 && q->bmse <= 4 &&
+         (q->mode != TQ_PROD || (q->m3 && q->mh));
 }
 
 int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
@@ -48,6 +61,7 @@ int run_encode_fused_cache(const tq_quantizer *q, const void *x, int xt, int64_t
   EncArgs ea{};
   ea.x = x; ea.ldx = ldx; ea.T = T; ea.tps = cdiv64(T, EB); ea.ntiles = nseq * ea.tps; ea.t0 = t0;
   ea.Tstride = Tstride; ea.pi3 = q->pi3; ea.m3 = q->m3;
+  ea.pih = q->pih; ea.mh = q->mh; ea.kp = q->kp; ea.km = q->km;
   if (layout == TQ_LAYOUT_TILE32) ea.tiles = static_cast<uint32_t *>(codes);
   else ea.codes = static_cast<uint8_t *>(codes);
   ea.code_bytes = (int64_t)q->code_bytes; ea.ntile32 = cdiv64(Tstride, 32);

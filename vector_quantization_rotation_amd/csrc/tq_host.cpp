@@ -173,6 +173,8 @@ void free_q(tq_quantizer *q) {
   hipFree(q->m);
   hipFree(q->pi3);
   hipFree(q->m3);
+  hipFree(q->pih);
+  hipFree(q->mh);
   hipFree(q->pit3);
   hipFree(q->st3);
   if (prev >= 0) hipSetDevice(prev);
@@ -296,6 +298,33 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
   }
   if (rc == TQ_OK) rc = dev_upload<uint16_t>(&q->pi3, nullptr, 3 * dd);
   if (rc == TQ_OK) rc = tq::make_pieces(q->pi, (int64_t)dd, q->pi3, nullptr);
+  if (rc == TQ_OK && d <= 128) {  // the fused encode's fp16 pieces
+    // exponent e of v = m 2^e, m in [0.5, 1): v 2^(14 - e) < 2^14
+    auto scale_exp = [](double v) {
+      int e = 0;
+      std::frexp(v, &e);
+      return v > 0.0 ? 14 - e : 0;
+    };
+    double pmax = 0.0, prow = 0.0, srow = 0.0;
+    for (int i = 0; i < d; ++i) {
+      double r2 = 0.0, s2 = 0.0;
+      for (int j = 0; j < d; ++j) {
+        const double v = pi[(size_t)i * d + j];
+        pmax = std::max(pmax, std::fabs(v));
+        r2 += v * v;
+        if (mode == TQ_PROD) s2 += (double)s[(size_t)i * d + j] * s[(size_t)i * d + j];
+      }
+      prow = std::max(prow, std::sqrt(r2));
+      srow = std::max(srow, std::sqrt(s2));
+    }
+    q->kp = scale_exp(pmax);
+    // |(S Pi^T)_ij| = |S_i . Pi_j| <= ||S_i|| ||Pi_j|| (with room for the fp32 rounding of the product)
+    q->km = scale_exp(srow * prow * (1.0 + 1e-4));
+    rc = dev_upload<uint16_t>(&q->pih, nullptr, 2 * dd);
+    if (rc == TQ_OK) rc = tq::make_pieces_f16(q->pi, (int64_t)dd, q->kp, q->pih, nullptr);
+    if (rc == TQ_OK && mode == TQ_PROD) rc = dev_upload<uint16_t>(&q->mh, nullptr, 2 * dd);
+    if (rc == TQ_OK && mode == TQ_PROD) rc = tq::make_pieces_f16(q->m, (int64_t)dd, q->km, q->mh, nullptr);
+  }
   if (rc == TQ_OK && d <= 128) {  // the fused decode's register-resident matrices
     rc = dev_upload<uint16_t>(&q->pit3, nullptr, 3 * dd);
     if (rc == TQ_OK) rc = tq::make_pieces(q->piT, (int64_t)dd, q->pit3, nullptr);

@@ -72,6 +72,11 @@ struct tq_quantizer {
   uint16_t *m3 = nullptr;   // of S Pi^T (TQ_PROD)
   uint16_t *pit3 = nullptr; // of Pi^T (decode, head dims up to 128)
   uint16_t *st3 = nullptr;  // of S^T (decode, TQ_PROD, head dims up to 128)
+  // fp16 pieces [2][d][d] (hi, lo) of Pi 2^kp and S Pi^T 2^km (fused encode of bf16 / fp16 rows, head dims up
+  // to 128); the exponents put the largest entry (Pi) or a bound on it (S Pi^T) just under 2^14
+  uint16_t *pih = nullptr;
+  uint16_t *mh = nullptr;
+  int kp = 0, km = 0;
 };
 
 namespace tq {
@@ -121,6 +126,7 @@ int run_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void 
 int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
                      hipStream_t st);
 int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
+int make_pieces_f16(const float *src, int64_t n, int k, uint16_t *dst, hipStream_t st);
 bool encode_fused_supported(const tq_quantizer *q);
 int run_encode_fused(const tq_quantizer *q, const void *x, int xt, int64_t n, int64_t ldx, uint8_t *codes,
                      uint16_t *norms, uint16_t *gammas, hipStream_t st);
