@@ -444,17 +444,75 @@ def test_encode_zero_and_empty(api):
 
 
 def test_bf16_and_f16_inputs_match_f32(api):
+    """The same values given as bf16 / fp16 rows (fp16 matrix-core operands) and as fp32 rows (exact bf16
+    pieces): the norms agree exactly, the codes wherever the oracle's decision is outside the tie zone."""
     d = 128
     x = synth.round_bf16(synth.unit_test_vectors(512, d, 41, 42))
     pi = synth.haar_rotation(d, 43)
     qz = api.Quantizer(d, 3, api.TQ_MSE, pi)
-    c32, n32, _ = qz.encode(_dev(x))
-    cbf, nbf, _ = qz.encode(_dev(x).to(torch.bfloat16))
-    assert torch.equal(c32, cbf) and torch.equal(n32, nbf)
-    x16 = x.astype(np.float16).astype(np.float32)
-    c32, n32, _ = qz.encode(_dev(x16))
-    c16, n16, _ = qz.encode(_dev(x16).to(torch.float16))
-    assert torch.equal(c32, c16) and torch.equal(n32, n16)
+    _, t = oracle.lloyd_max(d, 3)
+    for xs, dt in ((x, torch.bfloat16), (x.astype(np.float16).astype(np.float32), torch.float16)):
+        c32, n32, _ = qz.encode(_dev(xs))
+        ch, nh, _ = qz.encode(_dev(xs).to(dt))
+        assert torch.equal(n32, nh)
+        i32, _ = _idx_of(c32, d, 3, False)
+        ih, _ = _idx_of(ch, d, 3, False)
+        bad = i32 != ih
+        assert not np.any(bad & (oracle.code_margins(xs, pi, t) > parity.TIE))
+
+
+def _half_rows(n, d, seed, dt):
+    """Rows of the benchmark law plus rows that stress the per-row power-of-two scale: norms near 1e-30
+    and 1e30 (bf16) or near the fp16 range's ends, a row with one large coordinate over tiny ones, and a
+    zero row; returned as the rows' exact float64 values (what the oracle encodes)."""
+    x = synth.unit_test_vectors(n, d, seed, seed + 1).astype(np.float64)
+    rng = np.random.default_rng(seed + 2)
+    if dt == "bf16":
+        x[0] *= 1e-30
+        x[1] *= 1e30
+        x[2] = rng.standard_normal(d) * 1e-20
+        x[2, 5] = 3.0
+        x[3] = 0.0
+        x = synth.round_bf16(x.astype(np.float32)).astype(np.float64)
+    else:
+        x[0] *= 2e-3
+        x[1] *= 90000.0 / np.linalg.norm(x[1])  # coordinates in the fp16 range, the norm beyond it
+        x[2] = rng.standard_normal(d) * 1e-3
+        x[2, 5] = 60000.0
+        x[3] = 0.0
+        x = x.astype(np.float16).astype(np.float64)
+    return x
+
+
+@pytest.mark.parametrize("d,mode,bits,dt", [(128, "mse", 3, "bf16"), (128, "prod", 3, "f16"), (64, "prod", 2, "bf16"),
+                                            (128, "prod", 4, "bf16"), (256, "mse", 4, "bf16"), (256, "prod", 3, "f16"),
+                                            (512, "mse", 3, "bf16"), (512, "prod", 2, "bf16")])
+def test_encode_half_rows_parity(api, d, mode, bits, dt):
+    """bf16 / fp16 rows (fp16 operands: row-scaled rows, two-piece matrices) against the oracle's encoding
+    of the same values in fp64: codes outside the tie zone exact, fp16 norms exact, gammas within the
+    midpoint rule; rows at extreme scales included."""
+    n = 1000 if d <= 256 else 300
+    x = _half_rows(n, d, 800 + d + bits, dt)
+    pi = synth.haar_rotation(d, 810 + d)
+    prod = mode == "prod"
+    s = synth.gaussian_projection(d, 811 + d) if prod else None
+    qz = api.Quantizer(d, bits, api.TQ_PROD if prod else api.TQ_MSE, pi, s)
+    xt = _dev(x.astype(np.float32)).to(torch.bfloat16 if dt == "bf16" else torch.float16)
+    assert np.array_equal(xt.float().cpu().numpy().astype(np.float64), x)  # the rows are exact in their dtype
+    codes, norms, gammas = qz.encode(xt)
+    torch.cuda.synchronize()
+    assert parity.check_norms(norms.cpu().numpy(), x) == 0
+    if prod:
+        enc = parity.oracle_prod(x, pi, s, bits)
+        idx, sb = _idx_of(codes, d, bits, True)
+        parity.check_codes(idx, enc["idx"], oracle.code_margins(x, pi, enc["t"]))
+        _, _, same = parity.check_prod_signs(sb, idx, enc, x, pi, s)
+        rn = np.linalg.norm(parity.residual_given_index(x, enc["idx"], enc["n_hat"], pi, enc["c"]), axis=1)
+        parity.check_gammas(gammas.cpu().numpy()[same], rn[same])
+    else:
+        enc = parity.oracle_mse(x, pi, bits)
+        idx, _ = _idx_of(codes, d, bits, False)
+        parity.check_codes(idx, enc["idx"], oracle.code_margins(x, pi, enc["t"]))
 
 
 def test_profile_select_brackets_named_kernels(api):

@@ -18,6 +18,9 @@
 namespace tq {
 
 constexpr int GBM = 64, GBN = 64, GBK = 16, GPAD = 16;
+// head dims up to which bf16 / fp16 rows rotate on fp16 operands (the 2^-22 sqrt(d) bound of a rotated
+// coordinate's representation error, relative to n / sqrt(d), stays at half the 1e-5 tie zone or less)
+constexpr int kHalfRotateMaxD = 512;
 
 // ----------------------------------------------------------------------------
 // operand loaders: fill v[0..3] with elements k..k+3 of row r (k % 4 == 0)
@@ -60,6 +63,25 @@ struct LoadF16 {
   }
   __device__ void operator()(int64_t r, int k, float *v) const { unpack(fetch(r, k), v); }
 };
+
+// bf16 / fp16 rows taken as fp16 matrix-core operands, each row scaled by 2^kx (kx from the row's fp32
+// norm, so that every |x_i| 2^kx stays under 2^14 and converts to fp16 exactly)
+template <class Base>
+struct LoadHalfScaled {
+  Base base;
+  const float *n32;  // the rows' norms (chunk-relative)
+  static constexpr bool kHalf = true;
+  using Raw = typename Base::Raw;
+  __device__ Raw fetch(int64_t r, int k) const { return base.fetch(r, k); }
+  __device__ void unpack(const Raw &t, float *v) const { base.unpack(t, v); }
+};
+template <class T, class = void>
+struct is_half_loader : std::false_type {};
+template <class T>
+struct is_half_loader<T, std::void_t<decltype(T::kHalf)>> : std::bool_constant<T::kHalf> {};
+
+// the row scale exponent: n = m 2^e with m in [0.5, 1), kx = 14 - e (0 for a zero row)
+__device__ __forceinline__ int row_scale_exp(float n) { return n > 0.f ? 14 - __builtin_amdgcn_frexp_expf(n) : 0; }
 
 // rows [0, split) from a, rows [split, ...) from b (same row length ld)
 struct LoadRows2 {
@@ -146,6 +168,7 @@ struct EpiQuant {
   float *resid;            // [rows, d] rotated residual, or null (Algorithm 1)
   float *rsq;              // [rows, d / 64] partial ||r||^2, or null
   Codebook cb;
+  int kp;                  // >= 0: the tile holds y 2^(kx + kp) (fp16 operands; kx from the row's norm)
   // rows rb..rb+15 of the tile by the calling wave (lane = column)
   __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
     constexpr int L = 1 << BM;
@@ -173,8 +196,9 @@ struct EpiQuant {
       const int r = rb + rr;
       const int64_t row = row0 + r;
       if (row >= M) continue;
-      const float y = Cs[r][lane];
       const float n = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nl), rr));
+      // the scale undone exactly (a power of two)
+      const float y = kp >= 0 ? __builtin_amdgcn_ldexpf(Cs[r][lane], -(row_scale_exp(n) + kp)) : Cs[r][lane];
       const float yq = n == 0.0f ? 0.0f : y, nq = n == 0.0f ? 1.0f : n;
       // binary search: bit s of idx decided against the one boundary the higher bits leave
       int idx = 0;
@@ -350,11 +374,24 @@ __device__ __forceinline__ floatx4 g_terms(const gbf16x8 (&a)[3], const gbf16x8 
   return c;
 }
 
+typedef _Float16 gf16x8 __attribute__((ext_vector_type(8)));
+
+// fp16 operands (row-scaled bf16 / fp16 rows): the row against the matrix's hi and lo fp16 pieces
+__device__ __forceinline__ floatx4 g_terms_half(const gf16x8 &a, const gf16x8 (&b)[3], floatx4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[1], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[0], c, 0, 0, 0);
+}
+
 template <int NPA, class LA, class EP>
 __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N,
                                                           int K) {
+  // fp16 operands: one row piece (scaled), two matrix pieces [2][N][K]; else NPA bf16 row pieces, three
+  // matrix pieces [3][N][K]
+  constexpr bool HP = is_half_loader<LA>::value;
+  static_assert(!HP || NPA == 1, "fp16 operands: one row piece");
+  constexpr int NB = HP ? 2 : 3;
   // one buffer: the staged pieces during the contraction, then each wave's 64 x 64 result tile
-  constexpr size_t AB = (size_t)(NPA + 3) * PBM * PKP * 2, CT = (size_t)4 * GBM * (GBN + 1) * 4;
+  constexpr size_t AB = (size_t)(NPA + NB) * PBM * PKP * 2, CT = (size_t)4 * (GBM / 2) * (GBN + 1) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[AB > CT ? AB : CT];
   uint16_t(*As)[PBM][PKP] = reinterpret_cast<uint16_t(*)[PBM][PKP]>(lds);
   uint16_t(*Bs)[PBN][PKP] = reinterpret_cast<uint16_t(*)[PBN][PKP]>(lds + (size_t)NPA * PBM * PKP * 2);
@@ -363,6 +400,8 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
   const int64_t row0 = (int64_t)blockIdx.x * PBM, col0 = (int64_t)blockIdx.y * PBN;
   const int ar = tid >> 1, ak = (tid & 1) * 16;  // A staging: row ar, k ak..ak+15
   const bool arow_ok = row0 + ar < M;
+  int kx = 0;  // fp16 operands: the staged row's scale 2^kx
+  if constexpr (HP) kx = arow_ok ? row_scale_exp(la.n32[row0 + ar]) : 0;
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -372,14 +411,14 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
   // the next step's A and B elements are loaded into registers before this step's MFMAs and converted
   // to pieces only when they are stored, so the loads are in flight under the MFMAs
   typename LA::Raw rr[4];
-  uint4 rb[6];
+  uint4 rb[2 * NB];
   auto gload = [&](int k0) {
     if (arow_ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) rr[i] = la.fetch(row0 + ar, k0 + ak + 4 * i);
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 2 * NB; ++i) {
       const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
       const int64_t col = col0 + br;
       rb[i] = col < N ? *reinterpret_cast<const uint4 *>(b3 + ((int64_t)p * N + col) * K + k0 + kk)
@@ -397,20 +436,29 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t w[3][4];
+      if constexpr (HP) {
+        uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float p0[3], p1[3];
-        g_split<NPA>(v[8 * h + 2 * q], p0);
-        g_split<NPA>(v[8 * h + 2 * q + 1], p1);
+        for (int q = 0; q < 4; ++q)
+          w[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_ldexpf(v[8 * h + 2 * q], kx),
+                                                                         __builtin_amdgcn_ldexpf(v[8 * h + 2 * q + 1], kx)));
+        *reinterpret_cast<uint4 *>(&As[0][ar][ak + 8 * h]) = uint4{w[0], w[1], w[2], w[3]};
+      } else {
+        uint32_t w[3][4];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) w[p][q] = g_pack2(p0[p], p1[p]);
+        for (int q = 0; q < 4; ++q) {
+          float p0[3], p1[3];
+          g_split<NPA>(v[8 * h + 2 * q], p0);
+          g_split<NPA>(v[8 * h + 2 * q + 1], p1);
+#pragma unroll
+          for (int p = 0; p < 3; ++p) w[p][q] = g_pack2(p0[p], p1[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < NPA; ++p) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
       }
-#pragma unroll
-      for (int p = 0; p < NPA; ++p) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 2 * NB; ++i) {
       const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
       *reinterpret_cast<uint4 *>(&Bs[p][br][kk]) = rb[i];
     }
@@ -423,38 +471,61 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
     lstore();
     __syncthreads();
     if (k0 + PBK < K) gload(k0 + PBK);  // in flight during this step's MFMAs
-    gbf16x8 af[4][3];
+    if constexpr (HP) {
+      gf16x8 af[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt) af[rt] = *reinterpret_cast<const gf16x8 *>(&As[0][64 * wm + 16 * rt + fr][fk]);
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
-        af[rt][p] = p < NPA ? *reinterpret_cast<const gbf16x8 *>(&As[p][64 * wm + 16 * rt + fr][fk]) : af[rt][0];
+      for (int ct = 0; ct < 4; ++ct) {
+        gf16x8 bf[3];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      gbf16x8 bf[3];
+        for (int p = 0; p < 2; ++p) bf[p] = *reinterpret_cast<const gf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+        bf[2] = bf[1];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) bf[p] = *reinterpret_cast<const gbf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms_half(af[rt], bf, acc[rt][ct]);
+      }
+    } else {
+      gbf16x8 af[4][3];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms<NPA>(af[rt], bf, acc[rt][ct]);
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          af[rt][p] = p < NPA ? *reinterpret_cast<const gbf16x8 *>(&As[p][64 * wm + 16 * rt + fr][fk]) : af[rt][0];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        gbf16x8 bf[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) bf[p] = *reinterpret_cast<const gbf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms<NPA>(af[rt], bf, acc[rt][ct]);
+      }
     }
   }
-  // every wave turns its own 64 x 64 quadrant to row-major in its part of the buffer and runs the
-  // epilogue on it, 16 rows at a time (no work-group barrier after the first)
+  // every wave turns its own 64 x 64 quadrant to row-major in its part of the buffer, 32 rows at a time,
+  // and runs the epilogue on them 16 rows at a time (no work-group barrier after the first; the half
+  // quadrants keep the buffer at 33 KB, so the fp16-operand form fits four work-groups per CU)
   __syncthreads();  // every read of the staged pieces done
-  CTile *Cw = reinterpret_cast<CTile *>(lds + (size_t)wave * GBM * (GBN + 1) * 4);
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Cw[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[rt][ct][e];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  CTile *Cw = reinterpret_cast<CTile *>(lds + (size_t)wave * (GBM / 2) * (GBN + 1) * 4);
   const int64_t qr0 = row0 + 64 * wm, qc0 = col0 + 64 * wn;
-  if (qr0 < M && qc0 < N) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Cw[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[2 * h + rt][ct][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (qr0 + 32 * h < M && qc0 < N) {
 #pragma unroll 1
-    for (int rb = 0; rb < GBM; rb += 16) ep(Cw, qr0, qc0, M, N, rb);
+      for (int rb = 0; rb < GBM / 2; rb += 16) ep(Cw, qr0 + 32 * h, qc0, M, N, rb);
+    }
+    // this half's reads of the buffer done before the next half overwrites it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -567,17 +638,29 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
   }
   if ((rc = launch_check()) != TQ_OK) return rc;
   const bool prod = q->mode == TQ_PROD;
-  // exact bf16 pieces on the matrix cores: bf16 rows are one piece, fp16 two, fp32 three
+  // bf16 / fp16 rows up to d = 512: fp16 operands (row-scaled rows, two fp16 pieces of Pi: a rotated
+  // coordinate carries at most 2^-22 n of representation error, 5.4e-6 of n / sqrt(d) at d = 512); other
+  // rows: exact bf16 pieces (bf16 rows are one piece, fp16 two, fp32 three)
+  constexpr bool HALF_IN = !std::is_same<LX, LoadF32>::value;
   constexpr int NPA = std::is_same<LX, LoadBF16>::value ? 1 : std::is_same<LX, LoadF16>::value ? 2 : 3;
-  auto rotate = [&](auto eq) { return gemm_pieces<NPA>("encode_rotate", lx, q->pi3, eq, cn, d, d, st); };
+  const bool half = HALF_IN && q->pih && d <= kHalfRotateMaxD;
+  auto rotate = [&](auto eq) {
+    if constexpr (HALF_IN) {
+      if (half) {
+        eq.kp = q->kp;
+        return gemm_pieces<1>("encode_rotate", LoadHalfScaled<LX>{lx, n32}, q->pih, eq, cn, d, d, st);
+      }
+    }
+    return gemm_pieces<NPA>("encode_rotate", lx, q->pi3, eq, cn, d, d, st);
+  };
   float *rs = prod ? resid : nullptr, *rq = prod ? rsq : nullptr;
   const int64_t cbytes = (int64_t)q->code_bytes;
   switch (q->bmse) {
-    case 0: rc = rotate(EpiQuant<0>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
-    case 1: rc = rotate(EpiQuant<1>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
-    case 2: rc = rotate(EpiQuant<2>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
-    case 3: rc = rotate(EpiQuant<3>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
-    case 4: rc = rotate(EpiQuant<4>{codes, cbytes, d, n32, norms, rs, rq, q->cb}); break;
+    case 0: rc = rotate(EpiQuant<0>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 1: rc = rotate(EpiQuant<1>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 2: rc = rotate(EpiQuant<2>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 3: rc = rotate(EpiQuant<3>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 4: rc = rotate(EpiQuant<4>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
     default: rc = TQ_ERR_UNSUPPORTED;
   }
   if (rc != TQ_OK) return rc;

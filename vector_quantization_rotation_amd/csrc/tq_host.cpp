@@ -298,7 +298,7 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
   }
   if (rc == TQ_OK) rc = dev_upload<uint16_t>(&q->pi3, nullptr, 3 * dd);
   if (rc == TQ_OK) rc = tq::make_pieces(q->pi, (int64_t)dd, q->pi3, nullptr);
-  if (rc == TQ_OK && d <= 128) {  // the fused encode's fp16 pieces
+  if (rc == TQ_OK && d <= 512) {  // fp16 pieces: the fused encode (d <= 128) and the bf16 / fp16 row rotation
     // exponent e of v = m 2^e, m in [0.5, 1): v 2^(14 - e) < 2^14
     auto scale_exp = [](double v) {
       int e = 0;
@@ -322,8 +322,8 @@ int tq_quantizer_create(tq_quantizer **out, int d, int bits, int mode, const flo
     q->km = scale_exp(srow * prow * (1.0 + 1e-4));
     rc = dev_upload<uint16_t>(&q->pih, nullptr, 2 * dd);
     if (rc == TQ_OK) rc = tq::make_pieces_f16(q->pi, (int64_t)dd, q->kp, q->pih, nullptr);
-    if (rc == TQ_OK && mode == TQ_PROD) rc = dev_upload<uint16_t>(&q->mh, nullptr, 2 * dd);
-    if (rc == TQ_OK && mode == TQ_PROD) rc = tq::make_pieces_f16(q->m, (int64_t)dd, q->km, q->mh, nullptr);
+    if (rc == TQ_OK && mode == TQ_PROD && d <= 128) rc = dev_upload<uint16_t>(&q->mh, nullptr, 2 * dd);
+    if (rc == TQ_OK && mode == TQ_PROD && d <= 128) rc = tq::make_pieces_f16(q->m, (int64_t)dd, q->km, q->mh, nullptr);
   }
   if (rc == TQ_OK && d <= 128) {  // the fused decode's register-resident matrices
     rc = dev_upload<uint16_t>(&q->pit3, nullptr, 3 * dd);

@@ -72,8 +72,8 @@ struct tq_quantizer {
   uint16_t *m3 = nullptr;   // of S Pi^T (TQ_PROD)
   uint16_t *pit3 = nullptr; // of Pi^T (decode, head dims up to 128)
   uint16_t *st3 = nullptr;  // of S^T (decode, TQ_PROD, head dims up to 128)
-  // fp16 pieces [2][d][d] (hi, lo) of Pi 2^kp and S Pi^T 2^km (fused encode of bf16 / fp16 rows, head dims up
-  // to 128); the exponents put the largest entry (Pi) or a bound on it (S Pi^T) just under 2^14
+  // fp16 pieces [2][d][d] (hi, lo) of Pi 2^kp (head dims up to 512) and S Pi^T 2^km (up to 128) for bf16 /
+  // fp16 rows; the exponents put the largest entry (Pi) or a bound on it (S Pi^T) just under 2^14
   uint16_t *pih = nullptr;
   uint16_t *mh = nullptr;
   int kp = 0, km = 0;
