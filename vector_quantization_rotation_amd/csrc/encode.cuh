@@ -35,7 +35,7 @@
 // out in fp64.
 //
 // Work split.  A persistent work-group of NW waves (4; 8 for Algorithm 2 at
-// d = 128) walks 64-row tiles.  Wave w owns output columns [w d/NW, (w+1) d/NW):
+// d = 128 on fp32 rows) walks 64-row tiles.  Wave w owns output columns [w d/NW, (w+1) d/NW):
 // its pieces of Pi (and of S Pi^T) stay in registers for the whole launch, so
 // the matrices cross L2 once per work-group.  The row tile is staged whole in
 // LDS (NW threads per row, fp64 norm on the way, the next tile's loads in
@@ -110,17 +110,38 @@ struct EncIn {
 
 // 16-byte alignment lets every fragment access be one ds_read/ds_write_b128 (8 lanes a cycle, conflict-free
 // at the padded strides below) instead of b64 pairs (16 lanes a cycle, two-way conflicts)
-// waves per work-group: Algorithm 2 at d = 128 splits the columns over 8 waves (16 each), which halves
-// the register-resident matrix pieces and lets two waves share each SIMD (one wave's quantizer overlaps
-// the other's matrix-core work); otherwise 4 waves
-__host__ __device__ constexpr int enc_waves(int D, bool PROD) { return PROD && D == 128 ? 8 : 4; }
+// waves per work-group: Algorithm 2 at d = 128 on the bf16 pieces (fp32 rows) splits the columns over
+// 8 waves (16 each), which halves the register-resident matrix pieces so two waves share each SIMD;
+// otherwise 4 waves (the fp16 pieces of both matrices fit one wave of 32 columns in 128 registers, and two
+// work-groups share a CU, so the two waves on a SIMD come from different work-groups and are not held in
+// step by barriers: one's quantizer overlaps the other's matrix-core work)
+__host__ __device__ constexpr int enc_waves(int D, bool PROD, bool HP) { return PROD && D == 128 && !HP ? 8 : 4; }
 
-template <int D, int NPA, int NPR, bool PROD>
+// the tile's row pieces and the per-wave transpose area share storage when ALIAS (Algorithm 2 on fp16
+// operands: 76 KB instead of 113 KB, two work-groups per CU); the next tile is then staged only after
+// every wave has finished reading its transpose area
+template <bool ALIAS, class A, class C>
+struct EncAC;
+template <class A, class C>
+struct EncAC<true, A, C> {
+  union {
+    A a;
+    C cw;
+  };
+};
+template <class A, class C>
+struct EncAC<false, A, C> {
+  A a;
+  C cw;
+};
+
+template <int D, int NPA, int NPR, bool PROD, bool HP>
 struct __attribute__((aligned(16))) EncLds {
-  static constexpr int NW = enc_waves(D, PROD);
+  static constexpr int NW = enc_waves(D, PROD, HP);
   static constexpr int CW = D / NW;
-  uint16_t a[NPA][EB][D + 8];          // row pieces of the tile
-  float cw[NW][EB][CW + 4];            // per-wave transpose: MFMA layout -> lane = row
+  static constexpr bool ALIAS = PROD && HP;
+  // a: row pieces of the tile; cw: per-wave transpose, MFMA layout -> lane = row
+  EncAC<ALIAS, uint16_t[NPA][EB][D + 8], float[NW][EB][CW + 4]> ac;
   uint16_t rp[PROD ? NPR : 1][PROD ? EB : 1][D + 16];  // residual pieces (Algorithm 2; this stride measured 5 % faster than D + 8)
   float gpart[PROD ? NW : 1][EB];      // per-wave partial ||r||^2
   float n32[2][EB], nh[2][EB];         // norms by tile parity (times the row's scale 2^(kx + kp) for fp16 operands)
@@ -341,11 +362,12 @@ __device__ __forceinline__ void quant_coord(float y, const float (&T)[(1 << BM) 
 __device__ __forceinline__ uint32_t shift_in(uint32_t w, bool b) { return (w << 1) | (b ? 1u : 0u); }
 
 template <int XT, int D, bool PROD, int BM>
-__global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(enc_waves(D, PROD, XT != TQ_F32) * 64) __attribute__((amdgpu_waves_per_eu(2))) void
+encode_kernel(EncArgs a) {
   constexpr bool HP = EncIn<XT>::HP;
   constexpr int NPA = EncIn<XT>::NPA, NPB = EncIn<XT>::NPB, NPR = EncIn<XT>::NPR, ESZ = EncIn<XT>::ESZ;
   using MT = std::conditional_t<HP, f16x8, bf16x8>;  // matrix-core operand type
-  constexpr int NW = enc_waves(D, PROD);
+  constexpr int NW = enc_waves(D, PROD, HP);
   constexpr int CW = D / NW;       // columns per wave
   constexpr int NCT = CW / 16;     // 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;      // 32-deep k-steps
@@ -353,7 +375,8 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
   constexpr int PER = D / NW;      // staged elements per thread (NW threads per row)
   constexpr int RAW = PER * ESZ / 16;
   static_assert(RAW >= 1, "tile staging");
-  __shared__ EncLds<D, NPA, NPR, PROD> sh;
+  using Lds = EncLds<D, NPA, NPR, PROD, HP>;
+  __shared__ Lds sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, g4 = lane >> 4;
@@ -404,6 +427,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
     const int buf = it & 1;
 
     // ---- stage the tile: pieces into LDS, fp64 norm ----
+    if (Lds::ALIAS && it > 0) lds_barrier();  // every wave's reads of the shared transpose area done
     {
       float v[PER];
 #pragma unroll
@@ -438,7 +462,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             pk[q] = pack_f16x2_rtz(__builtin_amdgcn_ldexpf(v[i + 2 * q], kx), __builtin_amdgcn_ldexpf(v[i + 2 * q + 1], kx));
-          *reinterpret_cast<uint4 *>(&sh.a[0][sr][sk + i]) = uint4{pk[0], pk[1], pk[2], pk[3]};
+          *reinterpret_cast<uint4 *>(&sh.ac.a[0][sr][sk + i]) = uint4{pk[0], pk[1], pk[2], pk[3]};
         }
       } else {
 #pragma unroll
@@ -454,7 +478,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
           }
 #pragma unroll
           for (int p = 0; p < NPA; ++p)
-            *reinterpret_cast<uint4 *>(&sh.a[p][sr][sk + i]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+            *reinterpret_cast<uint4 *>(&sh.ac.a[p][sr][sk + i]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
         }
       }
       if (!HP) {
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
       if constexpr (HP) {
         f16x8 af[4][1];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) af[rt][0] = *reinterpret_cast<const f16x8 *>(&sh.a[0][16 * rt + j16][32 * ks + 8 * g4]);
+        for (int rt = 0; rt < 4; ++rt) af[rt][0] = *reinterpret_cast<const f16x8 *>(&sh.ac.a[0][16 * rt + j16][32 * ks + 8 * g4]);
         contract_terms<PieceTermsH1, NCT>(af, bpi[ks], acc);
       } else {
         bf16x8 af[4][3];
@@ -496,14 +520,14 @@ __global__ __launch_bounds__(enc_waves(D, PROD) * 64) void encode_kernel(EncArgs
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int p = 0; p < 3; ++p)
-            af[rt][p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[rt][0];
+            af[rt][p] = p < NPA ? *reinterpret_cast<const bf16x8 *>(&sh.ac.a[p][16 * rt + j16][32 * ks + 8 * g4]) : af[rt][0];
         contract_kstep<NPA, NCT>(af, bpi[ks], acc);
       }
     }
     lds_barrier();  // row pieces consumed
 
     // ---- to lane = row ----
-    float(*cw)[CW + 4] = sh.cw[wave];
+    float(*cw)[CW + 4] = sh.ac.cw[wave];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -646,7 +670,8 @@ int enc_blocks_per_cu() {
   static int cache = 0;
   if (cache > 0) return cache;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, encode_kernel<XT, D, PROD, BM>, enc_waves(D, PROD) * 64,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, encode_kernel<XT, D, PROD, BM>,
+                                                   enc_waves(D, PROD, XT != TQ_F32) * 64,
                                                    0) != hipSuccess ||
       blocks <= 0)
     blocks = 1;
@@ -660,7 +685,8 @@ template <int XT, int D, bool PROD, int BM>
 void launch_encode(EncArgs ea, hipStream_t st) {
   const int64_t slots = (int64_t)device_cus() * enc_blocks_per_cu<XT, D, PROD, BM>();
   const unsigned grid = (unsigned)imin64(ea.ntiles, slots);
-  hipLaunchKernelGGL((encode_kernel<XT, D, PROD, BM>), dim3(grid), dim3(enc_waves(D, PROD) * 64), 0, st, ea);
+  hipLaunchKernelGGL((encode_kernel<XT, D, PROD, BM>), dim3(grid), dim3(enc_waves(D, PROD, XT != TQ_F32) * 64), 0, st,
+                     ea);
 }
 
 // instantiated per (mode) in the encode translation units
