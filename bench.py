@@ -535,7 +535,7 @@ def main():
 
     # ---------------- chunked prefill: 512 query tokens against a 4096-token cache ----------------
     pB, pM, pT = 1, 512, 4096
-    pc = workloads.build_attention_cache(pB, Hq, Hkv, pT, d, tiles=False)
+    pc = workloads.build_attention_cache(pB, Hq, Hkv, pT, d, tiles=True)
     pq = torch.randn((pB, pM, Hq, d), generator=torch.Generator("cuda").manual_seed(721), device="cuda").to(torch.bfloat16)
     qpos = torch.full((pB,), pT - pM, dtype=torch.int32, device="cuda")
     pout = torch.empty((pB, pM, Hq, d), dtype=torch.float32, device="cuda")
@@ -543,12 +543,21 @@ def main():
                       device="cuda")
     pre_dt = timed(lambda: api.attn_prefill(pc.kq, pc.vq, pq, pc.kcodes, pc.knorms, pc.vcodes, pc.vnorms, pc.vgammas,
                                             qpos, scale, out=pout, ws=pws), reps=5)
-    prefill = {"ms": round(pre_dt * 1e3, 4), "query_tokens_per_s": round(pB * pM / pre_dt, 1),
-               "workload": f"{pM} query tokens (causal, positions {pT - pM}..{pT - 1}) x {Hq} heads over {Hkv} kv heads, "
-                           f"d{d}, against a {pT}-token row-record cache (keys mse 3-bit, values prod 2-bit)",
-               "kernel": "attn_split_kernel (row records, one wave per 16 query rows)"}
-    log(f"prefill: {pre_dt * 1e3:.3f} ms for {pM} query tokens")
-    del pc, pq, pout, pws
+    # the same chunk over token-tiled values: every query token a row of the decode kernels
+    ptws = torch.empty((_lib.load().tq_attn_prefill_ws_bytes(pc.kq.handle, pB, pM, Hq, Hkv, pT, 1),),
+                       dtype=torch.uint8, device="cuda")
+    pre_t_dt = timed(lambda: api.attn_prefill(pc.kq, pc.vq, pq, pc.kcodes, pc.knorms, pc.vtiles, pc.vnorms, pc.vgammas,
+                                              qpos, scale, out=pout, ws=ptws, vlayout=api.TQ_LAYOUT_TILE32), reps=5)
+    wl = (f"{pM} query tokens (causal, positions {pT - pM}..{pT - 1}) x {Hq} heads over {Hkv} kv heads, d{d}, "
+          f"against a {pT}-token cache (keys mse 3-bit, values prod 2-bit)")
+    prefill = {"ms": round(pre_t_dt * 1e3, 4), "query_tokens_per_s": round(pB * pM / pre_t_dt, 1),
+               "workload": wl + ", token-tiled values",
+               "kernel": "attn_wave_kernel (one row per query token)",
+               "rows_layout": {"ms": round(pre_dt * 1e3, 4), "query_tokens_per_s": round(pB * pM / pre_dt, 1),
+                               "kernel": "attn_split_kernel (row records, one wave per 16 query rows)"}}
+    log(f"prefill: {pre_t_dt * 1e3:.3f} ms for {pM} query tokens over token-tiled values "
+        f"({pre_dt * 1e3:.3f} ms over row records)")
+    del pc, pq, pout, pws, ptws
 
     res = {
         "metric": "packed-KV GB/s in compressed decode attention (% HBM peak); encode vectors/s",

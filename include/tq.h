@@ -231,9 +231,11 @@ size_t tq_attn_decode_ws_bytes(const tq_quantizer *kq, int B, int Hq, int Hkv, i
  *   q:     device [B, M, Hq, d] of type qt;  out: device [B, M, Hq, d] fp32
  *   q_pos: device [B] int32, q_pos[b] >= 0 and q_pos[b] + M <= Tstride (a query token past Tstride
  *          attends the Tstride cached tokens)
- *   cache arguments as tq_attn_decode; vlayout must be TQ_LAYOUT_ROWS (TQ_LAYOUT_TILE32:
- *          TQ_ERR_UNSUPPORTED)
- *   ws:    device workspace of at least tq_attn_prefill_ws_bytes(...) bytes */
+ *   cache arguments as tq_attn_decode, with the same layouts and limits: TQ_LAYOUT_ROWS takes any d
+ *          and bit widths (one wave per 16 query rows); TQ_LAYOUT_TILE32 runs the decode kernels
+ *          over B * M rows, one per query token (row b m attends tokens 0 .. q_pos[b] + m and reads
+ *          the cache row of sequence b), with TQ_MSE keys only
+ *   ws:    device workspace of at least tq_attn_prefill_ws_bytes(...) bytes (per layout) */
 int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
                     int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,

@@ -88,3 +88,50 @@ def test_prefill_one_token_equals_decode_step(api):
     dec = api.attn_decode(kq, vq, q, c["kcodes"], c["knorms"], c["vcodes"], c["vnorms"], c["vgammas"], qpos + 1,
                           1.0 / math.sqrt(d))
     assert torch.equal(pre.view(B, Hq, d), dec)
+
+
+@pytest.mark.parametrize("d,kb,vb,B,M,Hq,Hkv,T,qpos", [
+    (128, 3, 2, 2, 37, 8, 2, 304, [100, 250]),     # the wave-streaming kernel (stride a multiple of 8)
+    (128, 3, 2, 1, 64, 32, 8, 200, [0]),           # the first chunk of a prompt
+    (128, 2, 3, 1, 20, 8, 2, 301, [270]),          # 2-bit value indices: the four-wave kernel
+    (256, 3, 2, 1, 12, 16, 4, 160, [140]),         # head_dim 256
+    (512, 3, 2, 2, 9, 8, 1, 200, [150, 40]),       # head_dim 512: the global-layer kernel
+])
+def test_attn_prefill_tiled(api, d, kb, vb, B, M, Hq, Hkv, T, qpos):
+    """Token-tiled values: every query token becomes a row of the decode kernels, reading its sequence's
+    cache row; checked against the oracle's attention of each token over its causal prefix."""
+    rng = np.random.default_rng(700 + d + M)
+    kq, vq, Kt, Vt, c = _cache(api, d, "mse", kb, vb, B, Hkv, T, 710)
+    vrec = c["vcodes"].cpu().numpy().reshape(B * Hkv, T, -1)
+    tiles = _dev(np.stack([oracle.tile_records(vrec[i], d, vq.planes) for i in range(B * Hkv)]).view(np.int32))
+    tiles = tiles.view(B, Hkv, (T + 31) // 32, vq.planes, d)
+    q = synth.round_bf16(rng.standard_normal((B, M, Hq, d)).astype(np.float32))
+    print(f"tiled prefill d={d} keys {kb}-bit values {vb}-bit B={B} M={M} Hq={Hq} Hkv={Hkv} T={T} q_pos={qpos}",
+          flush=True)
+    out = api.attn_prefill(kq, vq, _dev(q).to(torch.bfloat16), c["kcodes"], c["knorms"], tiles, c["vnorms"],
+                           c["vgammas"], torch.tensor(qpos, dtype=torch.int32, device="cuda"), 1.0 / math.sqrt(d),
+                           vlayout=api.TQ_LAYOUT_TILE32).cpu().numpy()
+    worst = 0.0
+    for m in range(M):
+        lens = np.minimum(np.array(qpos) + m + 1, T)
+        ref = oracle.decode_attention(q[:, m], Kt, Vt, lens, 1.0 / math.sqrt(d))
+        err = parity.rel_rows(out[:, m], ref)
+        worst = max(worst, float(err.max()))
+        assert np.all(err <= parity.RTOL), (m, err.max())
+    print(f"tiled prefill d={d}: max rel err {worst:.2e}")
+
+
+def test_prefill_tiled_one_token_equals_decode_step(api):
+    """M = 1 over token-tiled values: the same kernels as the decode step over q_pos + 1 tokens."""
+    d, B, Hq, Hkv, T = 128, 2, 8, 2, 512
+    kq, vq, _, _, c = _cache(api, d, "mse", 3, 2, B, Hkv, T, 720)
+    vrec = c["vcodes"].cpu().numpy().reshape(B * Hkv, T, -1)
+    tiles = _dev(np.stack([oracle.tile_records(vrec[i], d, vq.planes) for i in range(B * Hkv)]).view(np.int32))
+    tiles = tiles.view(B, Hkv, T // 32, vq.planes, d)
+    q = _dev(synth.round_bf16(np.random.default_rng(721).standard_normal((B, Hq, d)).astype(np.float32))).to(torch.bfloat16)
+    qpos = torch.tensor([400, 33], dtype=torch.int32, device="cuda")
+    pre = api.attn_prefill(kq, vq, q.view(B, 1, Hq, d), c["kcodes"], c["knorms"], tiles, c["vnorms"], c["vgammas"],
+                           qpos, 1.0 / math.sqrt(d), vlayout=api.TQ_LAYOUT_TILE32)
+    dec = api.attn_decode(kq, vq, q, c["kcodes"], c["knorms"], tiles, c["vnorms"], c["vgammas"], qpos + 1,
+                          1.0 / math.sqrt(d), vlayout=api.TQ_LAYOUT_TILE32)
+    assert torch.equal(pre.view(B, Hq, d), dec)

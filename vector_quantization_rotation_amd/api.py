@@ -290,9 +290,9 @@ def attn_decode(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, v
 
 
 def attn_prefill(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, vcodes, vnorms, vgammas,
-                 q_pos: torch.Tensor, scale: float, out=None, ws=None, kgammas=None):
+                 q_pos: torch.Tensor, scale: float, out=None, ws=None, kgammas=None, vlayout: int = TQ_LAYOUT_ROWS):
     """Causal attention of M query tokens per sequence, q [B, M, Hq, d] (token m at position q_pos[b] + m),
-    against the row-record cache that already holds them -> out [B, M, Hq, d] fp32."""
+    against the cache that already holds them (value records in `vlayout`) -> out [B, M, Hq, d] fp32."""
     lib = load()
     _dev(q, "q")
     if q.dim() != 4:
@@ -301,19 +301,19 @@ def attn_prefill(kq: Quantizer, vq: Quantizer, q: torch.Tensor, kcodes, knorms, 
     dev = q.device
     _need(q, "q", tuple(_DT), device=dev)
     _attn_args(kq, vq, q.reshape(B, M * Hq, d), kcodes, knorms, vcodes, vnorms, vgammas, q_pos, None,
-               TQ_LAYOUT_ROWS, kgammas)
+               vlayout, kgammas)
     Hkv, Tstride = kcodes.shape[1], kcodes.shape[2]
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     if out is None:
         out = torch.empty((B, M, Hq, d), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, (B, M, Hq, d), dev)
-    ws_b = lib.tq_attn_prefill_ws_bytes(kq.handle, B, M, Hq, Hkv, Tstride, TQ_LAYOUT_ROWS)
+    ws_b = lib.tq_attn_prefill_ws_bytes(kq.handle, B, M, Hq, Hkv, Tstride, vlayout)
     if ws is None:
         ws = torch.empty((max(ws_b, 1),), dtype=torch.uint8, device=dev)
     _need(ws, "ws", torch.uint8, device=dev)
     rc = lib.tq_attn_prefill(kq.handle, vq.handle, _ptr(q), _DT[q.dtype], B, M, Hq, Hkv, _ptr(kcodes), _ptr(knorms),
-                             _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), TQ_LAYOUT_ROWS, Tstride,
+                             _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), _ptr(vgammas), vlayout, Tstride,
                              _ptr(q_pos), float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream())
     _lib._check("tq_attn_prefill", rc)
     return out

@@ -494,8 +494,8 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, 
 size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T);
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
-                  const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                  void *ws, const AppendArgs *app, hipStream_t st);
+                  const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, int kv_div, float scale,
+                  float *out, void *ws, const AppendArgs *app, hipStream_t st);
 
 // workspace of the row-record path: rotated queries, split partials, merged rows (M query tokens per sequence)
 size_t rows_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride) {
@@ -591,7 +591,7 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
     // the matrix-core kernels take Algorithm-1 keys and values with at least one index bit
     if (kprod || vq->bmse < 1) return TQ_ERR_UNSUPPORTED;
     return run_attn_fast(kq, vq, q, qt, B, Hq, Hkv, kcodes, knorms, reinterpret_cast<const uint32_t *>(vcodes), vnorms,
-                         vgammas, Tstride, seq_len, scale, out, ws, app, st);
+                         vgammas, Tstride, seq_len, 1, scale, out, ws, app, st);
   }
   AppendArgs ap{};
   if (app) ap = *app;
@@ -599,14 +599,45 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
                        ap.on ? 1 : 0, scale, out, ws, ap, st);
 }
 
-size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride) {
+// token-tiled prefill: every query token is a row of its own (B * M rows, row b m of sequence b attending
+// the tokens 0 .. q_pos[b] + m), all rows of a sequence reading its one cache row; the rows' lengths go
+// after the decode kernels' workspace
+static size_t prefill_tiled_lens_off(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride) {
+  return (attn_fast_ws_bytes(kq->d, kq->bits, B * M, Hq, Hkv, Tstride) + 255) & ~(size_t)255;
+}
+
+size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride, int vlayout) {
+  if (vlayout == TQ_LAYOUT_TILE32)
+    return prefill_tiled_lens_off(kq, B, M, Hq, Hkv, Tstride) + (((size_t)B * M * 4 + 255) & ~(size_t)255);
   return rows_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
+}
+
+__global__ void prefill_lens_kernel(const int32_t *q_pos, int B, int M, int64_t Tstride, int32_t *lens) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * M) return;
+  const int64_t b = i / M, m = i - b * M;
+  const int64_t pos = (int64_t)(q_pos[b] > 0 ? q_pos[b] : 0) + m + 1;
+  lens[i] = (int32_t)(pos < Tstride ? pos : Tstride);
 }
 
 int run_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
                      int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
-                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride,
-                     const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st) {
+                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                     int64_t Tstride, const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st) {
+  if (vlayout == TQ_LAYOUT_TILE32) {
+    // the decode kernels over B * M rows (the matrix-core kernels take Algorithm-1 keys and values with at
+    // least one index bit)
+    if (kq->mode == TQ_PROD || vq->bmse < 1) return TQ_ERR_UNSUPPORTED;
+    int32_t *lens = reinterpret_cast<int32_t *>(static_cast<char *>(ws) +
+                                                prefill_tiled_lens_off(kq, B, M, Hq, Hkv, Tstride));
+    const int64_t rows = (int64_t)B * M;
+    hipLaunchKernelGGL(prefill_lens_kernel, dim3((unsigned)cdiv64(rows, 256)), dim3(256), 0, st, q_pos, B, M, Tstride,
+                       lens);
+    int rc = launch_check();
+    if (rc != TQ_OK) return rc;
+    return run_attn_fast(kq, vq, q, qt, B * M, Hq, Hkv, kcodes, knorms, reinterpret_cast<const uint32_t *>(vcodes),
+                         vnorms, vgammas, Tstride, lens, M, scale, out, ws, nullptr, st);
+  }
   AppendArgs ap{};
   return run_attn_rows(kq, vq, q, qt, B, M, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, vgammas, Tstride, q_pos,
                        1, scale, out, ws, ap, st);

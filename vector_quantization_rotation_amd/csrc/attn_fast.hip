@@ -57,6 +57,8 @@ struct FastAttnArgs {
   int64_t Tstride, ntile;
   int Hq, Hkv, G, nsub, chunk, nsplit;
   int seq_add;              // 1 when the step appended a token at seq_len[b] (it is attended too)
+  int kv_div;               // query rows per cache row: row b reads the keys and values of sequence b / kv_div
+                            // (1 for decode; M for a prefill chunk of M query tokens, each its own row)
   float scale_log2, vqjl;
   float vbeta[4];           // Walsh coefficients of the value codebook (odd subsets)
   float kbeta[8];           // Walsh coefficients of the key codebook (applied after the MFMA when folded)
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(FA_THREADS) __attribute__((amdgpu_waves_per_eu(fa_w
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   // sequence length is wave-uniform: keep it (and everything derived) in scalar registers
   const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
-  const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t seq = (int64_t)(b / a.kv_div) * a.Hkv + g;
   const int64_t c0 = (int64_t)split * a.chunk;
   const int64_t c1 = imin64(T, c0 + a.chunk);
 
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   const bool head_ok = hl < gw;
   const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
-  const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t seq = (int64_t)(b / a.kv_div) * a.Hkv + g;
   const int64_t c0 = (int64_t)split * a.chunk;
   const int64_t c1 = imin64(T, c0 + a.chunk);
   // steps, padded to whole ring turns (padding steps hold no valid token and add nothing)
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(WD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
   const int gw = imin32(FA_GMAX, a.G - sub * FA_GMAX);
   const bool head_ok = hl < gw;
   const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
-  const int64_t seq = (int64_t)b * a.Hkv + g;
+  const int64_t seq = (int64_t)(b / a.kv_div) * a.Hkv + g;
   const int64_t c0 = (int64_t)split * a.chunk;
   const int64_t c1 = imin64(T, c0 + a.chunk);
   const int nvalid = c0 < c1 ? (int)((c1 - c0 + WD_STEP - 1) / WD_STEP) : 0;
@@ -1953,8 +1955,8 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, 
 
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
-                  const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, float scale, float *out,
-                  void *ws, const AppendArgs *app, hipStream_t st) {
+                  const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, int kv_div, float scale,
+                  float *out, void *ws, const AppendArgs *app, hipStream_t st) {
   const int D = kq->d, KB = kq->bits, VB = vq->bmse;
   if (!fast_supported(D, KB, VB)) return TQ_ERR_UNSUPPORTED;
   FastPlan fp = fast_plan(D, KB, VB, B, Hq, Hkv, Tstride);
@@ -2008,6 +2010,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   fa.Tstride = Tstride; fa.ntile = (Tstride + 31) / 32;
   fa.Hq = Hq; fa.Hkv = Hkv; fa.G = Hq / Hkv; fa.nsub = fp.nsub; fa.chunk = fp.chunk; fa.nsplit = fp.nsplit;
   fa.seq_add = (app && app->on) ? 1 : 0;
+  fa.kv_div = kv_div;
   fa.scale_log2 = scale * 1.4426950408889634f;
   fa.vqjl = vq->qjl_scale;
   for (int i = 0; i < 4; ++i) fa.vbeta[i] = (float)vb64[i];

@@ -446,8 +446,10 @@ int tq_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q
 }
 
 size_t tq_attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride, int vlayout) {
-  if (!kq || B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || Tstride < 0 || vlayout != TQ_LAYOUT_ROWS) return 0;
-  return tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
+  if (!kq || B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || Tstride < 0) return 0;
+  if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return 0;
+  if ((int64_t)B * M * Hq > 2147483647 / 2) return 0;
+  return tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride, vlayout);
 }
 
 int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
@@ -459,8 +461,8 @@ int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *
   const bool kprod = kq->mode == TQ_PROD;
   if (B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tstride < 0 || !valid_dtype(qt)) return TQ_ERR_INVALID;
   if (vlayout != TQ_LAYOUT_ROWS && vlayout != TQ_LAYOUT_TILE32) return TQ_ERR_INVALID;
-  if (vlayout != TQ_LAYOUT_ROWS) return TQ_ERR_UNSUPPORTED;
-  if ((int64_t)B * M * Hq > 2147483647 / 2) return TQ_ERR_UNSUPPORTED;
+  if ((int64_t)B * M * Hq > 2147483647 / 2 || (int64_t)B * M * Hkv * ((Hq / Hkv + 3) / 4) > 2147483647)
+    return TQ_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return TQ_ERR_INVALID;
   if (B == 0) return TQ_OK;
   if (!q || !out || !q_pos) return TQ_ERR_INVALID;
@@ -468,10 +470,10 @@ int tq_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *
     return TQ_ERR_INVALID;
   if ((Tstride > 0 && (!aligned16(kcodes) || !aligned16(vcodes))) || !aligned16(out) || !aligned16(q))
     return TQ_ERR_INVALID;
-  const size_t need = tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride);
+  const size_t need = tq::attn_prefill_ws_bytes(kq, B, M, Hq, Hkv, Tstride, vlayout);
   if (need > 0 && (!ws || ws_bytes < need)) return TQ_ERR_WORKSPACE;
   return tq::run_attn_prefill(kq, vq, q, qt, B, M, Hq, Hkv, kcodes, knorms, kprod ? kgammas : nullptr, vcodes, vnorms,
-                              vgammas, Tstride, q_pos, scale, out, ws, (hipStream_t)stream);
+                              vgammas, vlayout, Tstride, q_pos, scale, out, ws, (hipStream_t)stream);
 }
 
 int tq_attn_decode_append(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq,

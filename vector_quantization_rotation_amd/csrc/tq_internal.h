@@ -118,11 +118,11 @@ int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *
                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
                     int64_t Tstride, const int32_t *seq_len, float scale, float *out, void *ws, size_t ws_bytes,
                     const AppendArgs *app, hipStream_t st);
-size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride);
+size_t attn_prefill_ws_bytes(const tq_quantizer *kq, int B, int M, int Hq, int Hkv, int64_t Tstride, int vlayout);
 int run_attn_prefill(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int M, int Hq,
                      int Hkv, const uint8_t *kcodes, const uint16_t *knorms, const uint16_t *kgammas,
-                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int64_t Tstride,
-                     const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st);
+                     const uint8_t *vcodes, const uint16_t *vnorms, const uint16_t *vgammas, int vlayout,
+                     int64_t Tstride, const int32_t *q_pos, float scale, float *out, void *ws, hipStream_t st);
 int run_tile_records(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, uint32_t *tiles,
                      hipStream_t st);
 int make_pieces(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
