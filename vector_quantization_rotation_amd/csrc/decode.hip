@@ -4,11 +4,12 @@
 // "仕組み（技術的）"):  x~ = n Pi^T c[idx]  (+ sqrt(pi/2)/d * gamma S^T (2 s - 1)
 // for Algorithm 2).
 //
-// A persistent work-group of 4 waves walks 64-record tiles.  The tile's bits
-// are expanded once into LDS: the centroid c[idx] of every coordinate as two
+// A persistent work-group of NW waves (4; 8 for Algorithm 2 at d = 128) walks
+// 64-record tiles.  The tile's bits are expanded once into LDS: the centroid
+// c[idx] of every coordinate as two
 // bf16 pieces (hi keeps the top 8 significant bits, mid the next 8: c - hi - mid
 // is below 2^-16 |c|) and, for Algorithm 2, the sign plane as +-1 (exact).
-// Wave w owns output columns [w d/4, (w+1) d/4) and keeps two pieces of Pi^T
+// Wave w owns output columns [w d/NW, (w+1) d/NW) and keeps two pieces of Pi^T
 // (and of S^T) for them in registers for the whole launch.  Products:
 // c_hi T_hi + c_hi T_mid + c_mid T_hi (and s T_hi + s T_mid), fp32 accumulate,
 // so a reconstruction is within ~1e-5 of its fp64 value (the gate is 2e-3).  The
@@ -42,13 +43,17 @@ __device__ __forceinline__ uint32_t d_pack2(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// waves per SIMD without spills: Algorithm 2 at d = 128 holds both matrices' pieces and two accumulator sets
-__host__ __device__ constexpr int dec_waves_per_eu(int D, bool PROD) { return PROD && D == 128 ? 1 : 2; }
+// waves per work-group: Algorithm 2 at d = 128 holds the pieces of both matrices and two accumulator sets,
+// so its columns are split over 8 waves (16 each: 64 matrix registers instead of 128), which lets several
+// waves share a SIMD; otherwise 4 waves
+__host__ __device__ constexpr int dec_waves(int D, bool PROD) { return PROD && D == 128 ? 8 : 4; }
 
 template <int D, bool PROD, int BM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu(D, PROD)))) void decode_kernel(DecArgs a) {
-  constexpr int CW = D / 4, NCT = CW / 16, NKS = D / 32, L = 1 << BM;
-  constexpr int PER = D / 4;  // coordinates staged per thread (4 threads per record)
+__global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecArgs a) {
+  constexpr int NW = dec_waves(D, PROD);
+  constexpr int CW = D / NW, NCT = CW / 16, NKS = D / 32, L = 1 << BM;
+  constexpr int PER = D / NW;  // coordinates staged per thread (NW threads per record)
+  static_assert(PER == 16 || PER == 32, "record bits are read as 16- or 32-bit words");
   constexpr int NPL = BM + (PROD ? 1 : 0);
   __shared__ DecLds<D, PROD> sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_p
 #pragma unroll
   for (int i = 0; i < L; ++i) cc[i] = a.c[i];
 
-  const int sr = tid >> 2, sk = (tid & 3) * PER;
+  const int sr = tid / NW, sk = (tid % NW) * PER;
   uint32_t bits[NPL];
   float fn = 0.f, fg = 0.f;
   auto load_raw = [&](int64_t tile) {
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_p
       *reinterpret_cast<uint4 *>(&sh.am[1][sr][sk + i]) = uint4{mi[0], mi[1], mi[2], mi[3]};
       if (PROD) *reinterpret_cast<uint4 *>(&sh.aq[sr][sk + i]) = uint4{sg[0], sg[1], sg[2], sg[3]};
     }
-    if ((tid & 3) == 0) {
+    if (tid % NW == 0) {
       sh.nh[sr] = fn;
       sh.gq[sr] = fg;
     }
@@ -189,13 +194,15 @@ static void launch_decode(DecArgs da, hipStream_t st) {
   static int per_cu = 0;
   if (per_cu <= 0) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_kernel<D, PROD, BM>, 256, 0) != hipSuccess || b <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_kernel<D, PROD, BM>, dec_waves(D, PROD) * 64, 0) !=
+            hipSuccess ||
+        b <= 0)
       b = 1;
     per_cu = b;
   }
   da.ntiles = cdiv64(da.n, DB);
   const unsigned grid = (unsigned)imin64(da.ntiles, (int64_t)device_cus() * per_cu);
-  hipLaunchKernelGGL((decode_kernel<D, PROD, BM>), dim3(grid), dim3(256), 0, st, da);
+  hipLaunchKernelGGL((decode_kernel<D, PROD, BM>), dim3(grid), dim3(dec_waves(D, PROD) * 64), 0, st, da);
 }
 
 bool decode_fused_supported(const tq_quantizer *q) {
