@@ -381,7 +381,8 @@ def main():
                      "encode_ms": round(het_enc * 1e3, 4), "encode_vectors_per_s": round(2 * hn / het_enc, 1),
                      "attn_ms": round(het_att * 1e3, 4), "attn_packed_bytes": hpk,
                      "attn_gbs": round(hpk / het_att / 1e9, 2),
-                     "attn_kernel": ("attn_wide_kernel" if hd == 512 else "attn_fast_kernel") + " (token-tiled values)"
+                     "attn_kernel": ("attn_wide8_kernel" if hd == 512 and hHq == 8 * hHkv else "attn_wide_kernel" if hd == 512
+                                    else "attn_fast_kernel") + " (token-tiled values)"
                      if tiled else "attn_split_kernel (row records)"}
         log(f"{kind} layer: encode {het_enc * 1e3:.3f} ms ({2 * hn} vectors), attention {het_att * 1e3:.4f} ms "
             f"({hpk / het_att / 1e9:.1f} GB/s)")

@@ -1030,17 +1030,18 @@ constexpr int WD_COLS = WD_D / WD_WAVES;  // value columns per wave
 constexpr int WD_NH = WD_COLS / 64;     // 16-byte reads of a value word row per lane (4 columns each)
 constexpr int WD_FOLDMAX = 1024; // steps between folds at most: the int32 digit sums stay below 2^31
 
-template <int KB>
+template <int KB, int STEP = WD_STEP, int WAVES = WD_WAVES>
 struct WideStage {
   static constexpr int KCB = KB * WD_D / 8;                    // key record bytes
-  static constexpr int KEYS = WD_STEP * KCB;                   // the step's key records
-  static constexpr int VALS = (WD_STEP / 32) * 2 * WD_D * 4;   // tile words x two planes x 512 coordinates
+  static constexpr int KEYS = STEP * KCB;                      // the step's key records
+  static constexpr int VALS = (STEP / 32) * 2 * WD_D * 4;      // tile words x two planes x 512 coordinates
   static constexpr int NORMS = 4 * 256;                        // n_K, n_V, gamma_V (256 B each), a landing zone
   static constexpr int BYTES = KEYS + VALS + NORMS;
-  static constexpr int KLOADS = KEYS / 1024 / WD_WAVES;        // 1 KiB direct-to-LDS loads per wave
-  static constexpr int VLOADS = VALS / 1024 / WD_WAVES;
+  static constexpr int KLOADS = KEYS / 1024 / WAVES;           // 1 KiB direct-to-LDS loads per wave
+  static constexpr int VLOADS = VALS / 1024 / WAVES;
   static constexpr int NLOAD = KLOADS + VLOADS + 1;            // (+ one fp16 array, or a load of nothing)
-  static_assert(KEYS % (1024 * WD_WAVES) == 0 && VALS % (1024 * WD_WAVES) == 0, "stage split");
+  static_assert(KEYS % (1024 * WAVES) == 0 && VALS % (1024 * WAVES) == 0, "stage split");
+  static_assert(STEP <= 128, "an fp16 array of a step fits one dword per lane");
 };
 
 // this wave's share of the loads of one stage (tokens t0 .. t0 + WD_STEP - 1).  Waves 0..2 fetch the three
@@ -1048,12 +1049,12 @@ struct WideStage {
 // other waves, aim past every buffer: zeros into the region's tail or the stage's landing zone, no memory
 // touched), so every wave issues the same number of loads, all into the one LDS object of the slot.  Reads
 // past the chunk return zeros.
-template <int KB>
+template <int KB, int STEP = WD_STEP, int WAVES = WD_WAVES>
 __device__ __forceinline__ void wd_stage_load(uint8_t *stage, __amdgpu_buffer_rsrc_t rk,
                                               __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rkn,
                                               __amdgpu_buffer_rsrc_t rvn, __amdgpu_buffer_rsrc_t rvg, int wave,
                                               int lane, int64_t t0) {
-  using S = WideStage<KB>;
+  using S = WideStage<KB, STEP, WAVES>;
   const int sk = __builtin_amdgcn_readfirstlane((int)(t0 * S::KCB));
 #pragma unroll
   for (int i = 0; i < S::KLOADS; ++i) {
@@ -1070,7 +1071,7 @@ __device__ __forceinline__ void wd_stage_load(uint8_t *stage, __amdgpu_buffer_rs
   const int sn = __builtin_amdgcn_readfirstlane((int)(t0 * 2));
   const bool real = wave < 3;
   const __amdgpu_buffer_rsrc_t rn = wave == 0 ? rkn : (wave == 1 ? rvn : rvg);
-  const bool fetch = real && lane < WD_STEP / 2;
+  const bool fetch = real && lane < STEP / 2;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void_t *)(stage + S::KEYS + S::VALS + (real ? wave : 3) * 256), 4,
                                            fetch ? lane * 4 : 0x7FFFFF00, real ? sn : 0, 0, 0);
 }
@@ -1396,6 +1397,387 @@ __global__ __launch_bounds__(WD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
       const int col = WD_COLS * wave + 64 * (c >> 2) + 4 * ln + (c & 3);
       dst[2 + col] = a.vbeta[0] * (2.f * accf[0][c] - YM);
       dst[2 + D + col] = a.vqjl * (2.f * accf[1][c] - YQ);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attn_wide8_kernel<KB>: head dim 512, eight query heads per KV head (the global-layer shape), 1-bit value
+// indices.  One work-group of eight waves serves both four-head groups of a (batch, KV head, chunk), so the
+// key bits of a token are expanded into fp4 operands once for eight heads and the value bits into int8
+// operands once for both groups' weight digits (attn_wide_kernel runs a work-group per head group and
+// expands them twice).
+// * Steps of 128 tokens, staged by direct-to-LDS loads two steps ahead into a three-slot ring as in
+//   attn_wide_kernel (each wave an equal share of every stage).
+// * Key pass: wave w scores tokens 16w..16w+15 against both groups' query digits (their images in LDS,
+//   two MFMAs per fp4 operand).  Lane (head h, token) holds the scores of head h of group 0 and of group 1.
+// * Each lane weighs its token for both heads into the digit rows of the two groups' value operands; the
+//   softmax reference is kept per head as in attn_wide_kernel, the norm caps per work-group.
+// * Value pass: wave w aggregates the step's 128 tokens for value columns 64w..64w+63, each int8 operand of
+//   value bits against both groups' weight digits.
+// ---------------------------------------------------------------------------
+constexpr int W8_WAVES = 8;
+constexpr int W8_STEP = 16 * W8_WAVES;  // tokens per step: 16 per wave
+constexpr int W8_THREADS = 64 * W8_WAVES;
+constexpr int W8_TT = W8_STEP / 64;     // 64-token tiles of the value operand per step
+constexpr int W8_COLS = WD_D / W8_WAVES;  // value columns per wave
+constexpr int W8_NTC = W8_COLS / 16;    // value column tiles per wave (4 columns of a lane each)
+
+template <int KB>
+__global__ __launch_bounds__(W8_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attn_wide8_kernel(FastAttnArgs a) {
+  constexpr int D = WD_D;
+  constexpr int KP = walsh_count(KB);
+  constexpr int NB = D / 128;
+  constexpr bool FOLD = fold_beta(D, KB);
+  constexpr int NI8 = (FOLD ? 1 : KP) * NB;  // query images per head group
+  constexpr int NC = FOLD ? KP : 1;          // accumulators of the key pass per group
+  constexpr float WMAX = 268435328.f;        // 2^28 - 128 (see attn_fast_kernel)
+  using S = WideStage<KB, W8_STEP, W8_WAVES>;
+  static_assert(W8_TT == 2 && W8_NTC == 4, "layout below");
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring0[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring1[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring2[S::BYTES];
+  // flat arrays indexed in one step: the compiler keeps an LDS access apart from the direct-to-LDS loads in
+  // flight only when it can trace the address to its array through a few address computations
+  __shared__ __attribute__((aligned(16))) intx4 s_qa[2 * NI8 * 64 * 2];      // [group][image][lane][half]
+  __shared__ __attribute__((aligned(16))) uint8_t s_wm[2 * W8_TT * 16 * 64];  // [group][tile][digit row][slot]
+  __shared__ __attribute__((aligned(16))) uint8_t s_wq[2 * W8_TT * 16 * 64];
+  // the small exchanges in one object (the compiler keeps LDS objects apart from the direct-to-LDS loads in
+  // flight only while a kernel has few of them)
+  struct Small {
+    int flag[W8_WAVES];
+    float max[W8_WAVES][2][FA_GMAX];
+    float maxn[W8_WAVES][2];
+    float merge[W8_WAVES][2][FA_GMAX][3];
+  };
+  __shared__ Small s_sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 4, ln = lane & 15;
+  const int kofs = (hl & 1) * 4;
+  const int nbg = (int)gridDim.x, bg = blockIdx.x, split = blockIdx.y;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int64_t T = imin64(imax64(__builtin_amdgcn_readfirstlane(a.seq_len[b]), 0) + a.seq_add, a.Tstride);
+  const int64_t seq = (int64_t)(b / a.kv_div) * a.Hkv + g;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = imin64(T, c0 + a.chunk);
+  const int nvalid = c0 < c1 ? (int)((c1 - c0 + W8_STEP - 1) / W8_STEP) : 0;
+  const int nsteps = (nvalid + 2) / 3 * 3;  // whole ring turns
+
+  // the two head groups' images (units g_sub * nbg + bg of the prep kernel) into LDS, one intx8 a thread
+  {
+    const int gs = tid >> 8, i = (tid >> 6) & 3, l = tid & 63;
+    static_assert(NI8 == 4, "one image per thread and group");
+    const intx8 *img = reinterpret_cast<const intx8 *>(a.qimg) + ((int64_t)(gs * nbg + bg) * NI8 + i) * 64;
+    const intx8 v = img[l];
+    const int o = ((gs * NI8 + i) * 64 + l) * 2;
+    s_qa[o] = intx4{v[0], v[1], v[2], v[3]};
+    s_qa[o + 1] = intx4{v[4], v[5], v[6], v[7]};
+  }
+  float qinv2[2], qconst2[2];
+#pragma unroll
+  for (int gs = 0; gs < 2; ++gs) {
+    const int64_t u = (int64_t)gs * nbg + bg;
+    qinv2[gs] = a.qinfo[(u * FA_GMAX + hl) * 2 + 0] * a.scale_log2;
+    qconst2[gs] = a.qinfo[(u * FA_GMAX + hl) * 2 + 1] * a.scale_log2;
+  }
+
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.kcodes + seq * a.Tstride * S::KCB, c1 * S::KCB);
+  const int64_t nbytes = (c1 * 2 + 3) & ~(int64_t)3;
+  const __amdgpu_buffer_rsrc_t rkn = uniform_rsrc(a.knorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvn = uniform_rsrc(a.vnorms + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rvg = uniform_rsrc(a.vgammas + seq * a.Tstride, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.vtiles + seq * a.ntile * 2 * D, ((c1 + 31) >> 5) * 2 * D * 4);
+
+  // per head (lane's head hl of group 0 and of group 1): reference, top score, running sums
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_top[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f}, ym_run[2] = {0.f, 0.f}, yq_run[2] = {0.f, 0.f};
+  float vn_ref = 0.f, vg_ref = 0.f;  // norm and gamma caps of the work-group
+  int since_fold = 0, down_seg = FA_MINSEG, since_down = 1 << 30;
+  float sm = 0.f, sq = 0.f, ism = 0.f, isq = 0.f;
+  float accf[2][2][W8_NTC];
+  intx4 vacc[2][2][W8_NTC];  // [group][plane][column tile]
+#pragma unroll
+  for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int c = 0; c < W8_NTC; ++c) {
+        accf[gs][p][c] = 0.f;
+        vacc[gs][p][c] = intx4{0, 0, 0, 0};
+      }
+
+  // this lane's token in a step and its slot in the value operand (as attn_wide_kernel)
+  const int tw = 16 * wave + ln;
+  const int tt = tw >> 6, tau = tw & 63, bitw = tau & 31, r8 = bitw & 7;
+  const int slot = 16 * (2 * (tau >> 5) + (r8 >> 2)) + 4 * (r8 & 3) + (bitw >> 3);
+  const float kscale = __builtin_amdgcn_ldexpf(1.f, -value_kexp(r8));
+  const uint32_t f4_ones = f4_ones_reg();
+
+  auto body = [&, rk, rv, rkn, rvn, rvg](uint8_t *st, uint8_t *stl, int s) {
+    const int64_t t0 = c0 + (int64_t)s * W8_STEP;
+    wv_wait_vm<S::NLOAD>();
+    __builtin_amdgcn_sched_barrier(0);
+    wd_barrier();
+    // the stage into registers first, then the loads of step s + 2 into the slot step s - 1 used
+    uint4 kw4[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) kw4[p] = *reinterpret_cast<const uint4 *>(st + tw * S::KCB + p * (D / 8) + 16 * hl);
+    uint4 vw4[W8_TT][2];  // [token tile][plane]: 4 columns of this lane group's tile word
+#pragma unroll
+    for (int t2 = 0; t2 < W8_TT; ++t2)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        vw4[t2][p] = *reinterpret_cast<const uint4 *>(
+            st + S::KEYS + ((2 * (2 * t2 + (hl >> 1)) + p) * D + W8_COLS * wave + 4 * ln) * 4);
+    const uint16_t *nrm = reinterpret_cast<const uint16_t *>(st + S::KEYS + S::VALS);
+    const uint32_t hk = nrm[tw], hv = nrm[128 + tw], hg = nrm[256 + tw];
+    // ---- key pass: token tw against both groups' query digits (their images read from LDS before the
+    // loads of step s + 2 are issued, so that no LDS read waits for loads in flight) ----
+    floatx4 cacc[2][NC];
+#pragma unroll
+    for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+      for (int p = 0; p < NC; ++p) cacc[gs][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int wb = 0; wb < NB; ++wb) {
+      uint32_t w[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) w[p] = wb == 0 ? kw4[p].x : wb == 1 ? kw4[p].y : wb == 2 ? kw4[p].z : kw4[p].w;
+      uint32_t wp[KP];
+      walsh_planes<KB>(w, wp);
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+        const uint32_t x = wp[p];
+        intx8 bb;
+        bb[0] = (int)(x & 0x11111111u);
+        bb[1] = (int)(x & 0x22222222u);
+        bb[2] = (int)(x & 0x44444444u);
+        bb[3] = f4_sign_half(x, f4_ones);
+        bb[4] = bb[5] = bb[6] = bb[7] = 0;
+        const int ai = FOLD ? wb : p * NB + wb;
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs) {
+          // (read as two 16-byte halves: a 32-byte LDS read is split by the compiler into accesses it can no
+          // longer tell from the direct-to-LDS loads in flight)
+          const int o = ((gs * NI8 + ai) * 64 + lane) * 2;
+          const intx4 q0 = s_qa[o], q1 = s_qa[o + 1];
+          const intx8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          cacc[gs][FOLD ? p : 0] =
+              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, bb, cacc[gs][FOLD ? p : 0], 0, 4,
+                                                               0, 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0): the reads are done
+    __builtin_amdgcn_sched_barrier(0);
+    wd_stage_load<KB, W8_STEP, W8_WAVES>(stl, rk, rv, rkn, rvn, rvg, wave, lane, t0 + 2 * W8_STEP);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool tvalid = t0 + tw < c1;
+    const float fvn = tvalid ? f16_to_f32((uint16_t)hv) : 0.f;
+    const float fvg = tvalid ? f16_to_f32((uint16_t)hg) : 0.f;
+    const float fkn = f16_to_f32((uint16_t)hk);
+    float sc[2];
+#pragma unroll
+    for (int gs = 0; gs < 2; ++gs) {
+      float v = 0.f;
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {  // digit rows: Q_d 2^-E_d = 1, 2^-4, 2^-9, 2^-14
+        const float x = cacc[gs][p][0] +
+                        (cacc[gs][p][1] * 0.0625f + (cacc[gs][p][2] * (1.f / 512.f) + cacc[gs][p][3] * (1.f / 16384.f)));
+        v = FOLD ? fmaf(2.f * a.kbeta[p], x, v) : x;
+      }
+      sc[gs] = tvalid ? fmaf(v, qinv2[gs], -qconst2[gs]) * fkn : -INFINITY;
+    }
+    // ---- reference test (flags of the work-group): bit 0 a score above a reference's headroom, bit 1 + 4 gs
+    // + h head h of group gs within REF_DROP of its reference, bit 9 a norm or gamma above its cap ----
+    {
+      const bool over = sc[0] > m_ref[0] + FA_SLACK || sc[1] > m_ref[1] + FA_SLACK;
+      const bool over_n = fvn > vn_ref || fvg > vg_ref;
+      const uint64_t near0 = __builtin_amdgcn_ballot_w64(sc[0] >= m_ref[0] - REF_DROP);
+      const uint64_t near1 = __builtin_amdgcn_ballot_w64(sc[1] >= m_ref[1] - REF_DROP);
+      int flag = (__builtin_amdgcn_ballot_w64(over) != 0ull ? 1 : 0) |
+                 (__builtin_amdgcn_ballot_w64(over_n) != 0ull ? 512 : 0);
+#pragma unroll
+      for (int h = 0; h < FA_GMAX; ++h) {
+        flag |= ((near0 >> (16 * h)) & 0xFFFFull) != 0 ? 2 << h : 0;
+        flag |= ((near1 >> (16 * h)) & 0xFFFFull) != 0 ? 32 << h : 0;
+      }
+      if (lane == 0) s_sm.flag[wave] = flag;
+    }
+    float pw[2];
+    uint32_t um[2], uq[2];
+    auto weigh = [&]() {
+#pragma unroll
+      for (int gs = 0; gs < 2; ++gs) {
+        pw[gs] = sc[gs] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[gs] - m_ref[gs]);
+        um[gs] = __float2uint_rn(pw[gs] * fvn * sm);
+        uq[gs] = __float2uint_rn(pw[gs] * fvg * sq);
+        const int o = ((gs * W8_TT + tt) * 16 + 4 * hl) * 64 + slot;
+        s_wm[o] = (uint8_t)(um[gs] >> 21);
+        s_wm[o + 64] = (uint8_t)((um[gs] >> 14) & 127u);
+        s_wm[o + 128] = (uint8_t)((um[gs] >> 7) & 127u);
+        s_wm[o + 192] = (uint8_t)(um[gs] & 127u);
+        s_wq[o] = (uint8_t)(uq[gs] >> 21);
+        s_wq[o + 64] = (uint8_t)((uq[gs] >> 14) & 127u);
+        s_wq[o + 128] = (uint8_t)((uq[gs] >> 7) & 127u);
+        s_wq[o + 192] = (uint8_t)(uq[gs] & 127u);
+      }
+    };
+    weigh();
+    wd_barrier();  // flags and weight digits visible
+    int flags = 0;
+#pragma unroll
+    for (int w = 0; w < W8_WAVES; ++w) flags |= s_sm.flag[w];
+    const bool whole = t0 + W8_STEP <= c1;
+    ++since_fold;
+    ++since_down;
+    const bool low = whole && since_fold >= down_seg && ((flags >> 1) & 0xFF) != 0xFF;
+    if ((flags & 513) || low || since_fold >= WD_FOLDMAX) {
+      if ((flags & 1) && since_down <= 2 * down_seg) down_seg = imin32(2 * down_seg, FA_MAXSEG);
+      if (low) since_down = 0;
+      // move the references to this step's maxima and fold the int32 accumulators
+#pragma unroll
+      for (int gs = 0; gs < 2; ++gs) {
+        const float smax = rows16_max(sc[gs]);
+        if (ln == 0) s_sm.max[wave][gs][hl] = smax;
+      }
+      const float vnm = wave_max_f32(fvn), vgm = wave_max_f32(fvg);
+      if (lane == 0) { s_sm.maxn[wave][0] = vnm; s_sm.maxn[wave][1] = vgm; }
+      wd_barrier();
+      float step_vn = 0.f, step_vg = 0.f;
+#pragma unroll
+      for (int w = 0; w < W8_WAVES; ++w) {
+        step_vn = fmaxf(step_vn, s_sm.maxn[w][0]);
+        step_vg = fmaxf(step_vg, s_sm.maxn[w][1]);
+      }
+      const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
+#pragma unroll
+      for (int gs = 0; gs < 2; ++gs) {
+        float step_m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W8_WAVES; ++w) step_m = fmaxf(step_m, s_sm.max[w][gs][hl]);
+        m_top[gs] = fmaxf(m_top[gs], step_m);
+        const float m_new = moved_reference(m_ref[gs], step_m, m_top[gs], low);
+        const float alpha = m_ref[gs] == -INFINITY ? 0.f : exp2f(m_ref[gs] - m_new);
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          const float isc = pl == 0 ? im : iq;
+#pragma unroll
+          for (int c = 0; c < W8_NTC; ++c) {
+            const intx4 va = vacc[gs][pl][c];
+            const float x = (((float)va[0] * 128.f + (float)va[1]) * 128.f + (float)va[2]) * 128.f + (float)va[3];
+            accf[gs][pl][c] = (accf[gs][pl][c] + x * isc) * alpha;
+            vacc[gs][pl][c] = intx4{0, 0, 0, 0};
+          }
+        }
+        l_run[gs] *= alpha;
+        ym_run[gs] *= alpha;
+        yq_run[gs] *= alpha;
+        m_ref[gs] = m_new;
+      }
+      vn_ref = fmaxf(vn_ref, FA_NCAP * step_vn);
+      vg_ref = fmaxf(vg_ref, FA_NCAP * step_vg);
+      // p <= 2^FA_SLACK and n <= vn_ref, so p n sm <= WMAX kscale
+      sm = vn_ref > 0.f ? WMAX * kscale / (vn_ref * FA_HEADROOM) : 0.f;
+      sq = vg_ref > 0.f ? WMAX * kscale / (vg_ref * FA_HEADROOM) : 0.f;
+      ism = sm > 0.f ? 1.f / sm : 0.f;
+      isq = sq > 0.f ? 1.f / sq : 0.f;
+      since_fold = 0;
+      weigh();       // against the moved references
+      wd_barrier();  // the new digits visible
+    }
+#pragma unroll
+    for (int gs = 0; gs < 2; ++gs) {
+      l_run[gs] += pw[gs];
+      ym_run[gs] = fmaf((float)um[gs], ism, ym_run[gs]);
+      yq_run[gs] = fmaf((float)uq[gs], isq, yq_run[gs]);
+    }
+    // ---- value pass: the step's tokens x this wave's columns, both kinds, both groups ----
+#pragma unroll
+    for (int t2 = 0; t2 < W8_TT; ++t2) {
+      intx4 wa_m[2], wa_q[2];
+#pragma unroll
+      for (int gs = 0; gs < 2; ++gs) {
+        const int o = ((gs * W8_TT + t2) * 16 + ln) * 64 + 16 * hl;
+        wa_m[gs] = *reinterpret_cast<const intx4 *>(&s_wm[o]);
+        wa_q[gs] = *reinterpret_cast<const intx4 *>(&s_wq[o]);
+      }
+      const uint4 w0 = vw4[t2][0], w1 = vw4[t2][1];
+      const uint32_t x0[W8_NTC] = {w0.x, w0.y, w0.z, w0.w}, x1[W8_NTC] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int c = 0; c < W8_NTC; ++c) {
+        const intx4 b0 = value_bits(x0[c], kofs), b1 = value_bits(x1[c], kofs);
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs) {
+          vacc[gs][0][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_m[gs], b0, vacc[gs][0][c], 0, 0, 0);
+          vacc[gs][1][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa_q[gs], b1, vacc[gs][1][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    wd_stage_load<KB, W8_STEP, W8_WAVES>(s_ring0, rk, rv, rkn, rvn, rvg, wave, lane, c0);
+    wd_stage_load<KB, W8_STEP, W8_WAVES>(s_ring1, rk, rv, rkn, rvn, rvg, wave, lane, c0 + W8_STEP);
+    // the query information (loaded before the stages; loads complete in order) is in registers before the
+    // loop, so no wait inside it has to cover it
+    wv_wait_vm<2 * S::NLOAD>();
+    for (int s = 0; s < nsteps; s += 3) {
+      body(s_ring0, s_ring2, s);
+      body(s_ring1, s_ring0, s + 1);
+      body(s_ring2, s_ring1, s + 2);
+    }
+    wv_wait_vm<0>();  // the last two stages' loads (past the chunk) have landed before the work-group ends
+  } else {
+    wv_wait_vm<0>();
+    wd_barrier();  // (the images in LDS are not read without steps; the barrier keeps every wave in step)
+  }
+  // ---- final fold, reductions, partial records: m, l, acc_mse[D], acc_qjl[D] per head ----
+  {
+    const float im = vn_ref * FA_HEADROOM / WMAX, iq = vg_ref * FA_HEADROOM / WMAX;
+#pragma unroll
+    for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float isc = p == 0 ? im : iq;
+#pragma unroll
+        for (int c = 0; c < W8_NTC; ++c) {
+          const intx4 va = vacc[gs][p][c];
+          const float x = (((float)va[0] * 128.f + (float)va[1]) * 128.f + (float)va[2]) * 128.f + (float)va[3];
+          accf[gs][p][c] += x * isc;
+        }
+      }
+  }
+#pragma unroll
+  for (int gs = 0; gs < 2; ++gs) {
+    const float L = rows16_sum(l_run[gs]), YM = rows16_sum(ym_run[gs]), YQ = rows16_sum(yq_run[gs]);
+    if (ln == 0) {
+      s_sm.merge[wave][gs][hl][0] = L;
+      s_sm.merge[wave][gs][hl][1] = YM;
+      s_sm.merge[wave][gs][hl][2] = YQ;
+    }
+  }
+  wd_barrier();
+#pragma unroll
+  for (int gs = 0; gs < 2; ++gs) {
+    float L = 0.f, YM = 0.f, YQ = 0.f;
+#pragma unroll
+    for (int w = 0; w < W8_WAVES; ++w) {
+      L += s_sm.merge[w][gs][hl][0];
+      YM += s_sm.merge[w][gs][hl][1];
+      YQ += s_sm.merge[w][gs][hl][2];
+    }
+    const int h = g * a.G + FA_GMAX * gs + hl;
+    float *dst = a.part + (((int64_t)b * a.Hq + h) * a.nsplit + split) * (2 + 2 * (int64_t)D);
+    if (wave == 0 && ln == 0) { dst[0] = m_ref[gs]; dst[1] = L; }
+#pragma unroll
+    for (int c = 0; c < W8_NTC; ++c) {
+      const int col = W8_COLS * wave + 4 * ln + c;
+      dst[2 + col] = a.vbeta[0] * (2.f * accf[gs][0][c] - YM);
+      dst[2 + D + col] = a.vqjl * (2.f * accf[gs][1][c] - YQ);
     }
   }
 }
@@ -1916,6 +2298,40 @@ FastPlan wide_plan(int KB, int B, int Hq, int Hkv, int64_t T) {
   return p;
 }
 
+// resident work-groups of attn_wide8_kernel<KB> on the device (cached)
+int wide8_slots(int KB) {
+  static int cache[64][4] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int &slot = cache[dev][KB];
+  if (slot > 0) return slot;
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (KB == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide8_kernel<1>, W8_THREADS, 0);
+  if (KB == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide8_kernel<2>, W8_THREADS, 0);
+  if (KB == 3) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_wide8_kernel<3>, W8_THREADS, 0);
+  if (e != hipSuccess || blocks <= 0) blocks = 1;
+  slot = device_cus() * blocks;
+  return slot;
+}
+
+// the eight-head plan: one work-group per (batch, KV head, chunk) serves both head groups; chunks of whole
+// ring turns (three 128-token steps), one per resident work-group
+FastPlan wide8_plan(int KB, int B, int Hq, int Hkv, int64_t T) {
+  FastPlan p = fast_plan(WD_D, KB, 1, B, Hq, Hkv, T);
+  const int64_t units = (int64_t)B * Hkv;
+  const int64_t want = std::max<int64_t>(1, wide8_slots(KB) / std::max<int64_t>(units, 1));
+  const int64_t turn = 3 * (int64_t)W8_STEP;
+  int64_t chunk = (T + want - 1) / want;
+  chunk = std::max<int64_t>(turn, (chunk + turn - 1) / turn * turn);
+  p.chunk = (int)std::min<int64_t>(chunk, 1 << 30);
+  p.nsplit = (int)std::max<int64_t>(1, (T + p.chunk - 1) / p.chunk);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.merge_off = p.part_off + al((size_t)B * Hq * p.nsplit * (2 + 2 * (size_t)WD_D) * 4);
+  p.total = p.merge_off + (size_t)B * Hq * 2 * (size_t)WD_D * 4;
+  return p;
+}
+
 bool fast_supported(int D, int KB, int VB) {
   if (D != 128 && D != 256 && D != 512) return false;
   if (KB < 1 || KB > 4 || VB < 1 || VB > 3) return false;
@@ -1947,6 +2363,7 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   for (int vb = 1; vb <= 3; ++vb) n = std::max(n, fast_plan(D, KB, vb, B, Hq, Hkv, T).total);
   if (wave_supported(D, KB, 1)) n = std::max(n, wave_plan(D, KB, B, Hq, Hkv, T).total);
   if (wide_supported(D, KB, 1)) n = std::max(n, wide_plan(KB, B, Hq, Hkv, T).total);
+  if (wide_supported(D, KB, 1) && Hkv > 0 && Hq == 8 * Hkv) n = std::max(n, wide8_plan(KB, B, Hq, Hkv, T).total);
   return n;
 }
 
@@ -1967,7 +2384,9 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   const bool widek = !wave && wide_supported(D, KB, VB) && Tstride % 8 == 0 && aligned16(kcodes) &&
                      aligned16(knorms) && aligned16(vtiles) && aligned16(vnorms) && aligned16(vgammas) &&
                      Tstride * (int64_t)(KB * D / 8) < (int64_t(1) << 31);
-  if (widek) fp = wide_plan(KB, B, Hq, Hkv, Tstride);
+  // eight query heads per KV head: one eight-wave work-group serves both head groups
+  const bool wide8 = widek && Hq == 8 * Hkv;
+  if (widek) fp = wide8 ? wide8_plan(KB, B, Hq, Hkv, Tstride) : wide_plan(KB, B, Hq, Hkv, Tstride);
   if (wave) {
     const WavePlan wp = wave_plan(D, KB, B, Hq, Hkv, Tstride);
     fp.nsplit = wp.nsplit;
@@ -2052,7 +2471,13 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       }
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
-    {
+    if (wide8) {
+      ProfKernel pk("attn_wide8");
+      const dim3 grid((unsigned)(B * Hkv), (unsigned)fp.nsplit), blk(W8_THREADS);
+      if (KB == 1) hipExtLaunchKernelGGL(attn_wide8_kernel<1>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 2) hipExtLaunchKernelGGL(attn_wide8_kernel<2>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
+      if (KB == 3) hipExtLaunchKernelGGL(attn_wide8_kernel<3>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
+    } else {
       ProfKernel pk("attn_wide");
       const dim3 grid((unsigned)units, (unsigned)fp.nsplit), blk(WD_THREADS);
       if (KB == 1) hipExtLaunchKernelGGL(attn_wide_kernel<1>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
