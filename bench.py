@@ -525,8 +525,24 @@ def main():
         api.attn_decode_append(kq, vq, q, kn_new, vn_new, kc, kn, vt, vn, vg, seq_app, scale, out=out, ws=ws,
                                vlayout=layout)
 
-    app_dt = timed(app_step, reps=args.steps)
-    plain_dt = timed(step, reps=args.steps)
+    # the two steps alternate in short runs, so that the clock's drift under sustained load falls on both alike
+    app_step()
+    step()
+    torch.cuda.synchronize()
+    app_t = plain_t = 0.0
+    runs, per = max(1, args.steps // 4), 4
+    for _ in range(runs):
+        t = time.perf_counter()
+        for _ in range(per):
+            app_step()
+        torch.cuda.synchronize()
+        app_t += time.perf_counter() - t
+        t = time.perf_counter()
+        for _ in range(per):
+            step()
+        torch.cuda.synchronize()
+        plain_t += time.perf_counter() - t
+    app_dt, plain_dt = app_t / (runs * per), plain_t / (runs * per)
     append = {"ms_per_step": round(app_dt * 1e3, 4), "plain_step_ms": round(plain_dt * 1e3, 4),
               "overhead_ms": round((app_dt - plain_dt) * 1e3, 4),
               "workload": f"decode step that encodes one new key and value per (batch, kv head) into the cache at "
