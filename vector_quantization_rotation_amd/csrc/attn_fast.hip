@@ -2370,11 +2370,6 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
 int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
                  float *out, hipStream_t st);
 
-// query rows from which head dim 128 rotates them in a kernel of their own (below, one prep work-group per
-// head reads the whole matrix: fine for a decode step's few hundred heads, not for a prefill chunk's
-// thousands)
-constexpr int64_t kQrotRowsMin = 4096;
-
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
                   const uint16_t *vgammas, int64_t Tstride, const int32_t *seq_len, int kv_div, float scale,
@@ -2415,11 +2410,9 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   pa.qinfo = reinterpret_cast<float *>(w + fp.info_off);
   if (app) pa.app = *app;
   int rc = TQ_ERR_UNSUPPORTED;
-  // head dims of 512, and many rows at head dim 128 (a prefill chunk: one row per query token): the
-  // rotated queries of all B * Hq heads first, spread over many work-groups, each Pi^T entry read serving
-  // eight rows (at head dim 128 the sums run in the prep kernel's order, so the images are the same bits)
-  if ((D >= 512 || (D == 128 && (int64_t)B * Hq >= kQrotRowsMin)) && B > 0) {
-    // (into the merge area, which the split merge uses only after the attention kernel)
+  if (D >= 512 && B > 0) {
+    // the rotated queries of all B * Hq heads first, spread over many work-groups (into the merge area,
+    // which the split merge uses only after the attention kernel)
     float *qp = reinterpret_cast<float *>(w + fp.merge_off);
     {
       ProfScope ps("attn_qrot_rows", st);
