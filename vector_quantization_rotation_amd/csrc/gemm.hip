@@ -14,6 +14,7 @@
 #include <type_traits>
 
 #include "common.cuh"
+#include "quant.cuh"
 
 namespace tq {
 
@@ -154,96 +155,80 @@ struct EpiStore {
 };
 
 // Algorithm-1 index planes for 64 coordinates (one tile column block) per row.
-// For Algorithm 2 also the rotated residual y - n_hat c[idx] and its squared norm over the block (fp32:
-// the fp16 gamma tolerates 1e-5 relative), one partial per (row, block) so no atomics are needed.
-// BM index bits; the cell index is a binary search over the row's scaled boundaries t_k n.  BM = 0
-// (Algorithm 2 at one bit) writes no index plane and the residual is y itself.
-template <int BM>
+// For Algorithm 2 (RES) also the rotated residual y - n_hat c[idx] and its squared norm over the block
+// (fp32: the fp16 gamma tolerates 1e-5 relative), one partial per (row, block) so no atomics are needed.
+// BM index bits; BM = 0 (Algorithm 2 at one bit) writes no index plane and the residual is y itself.
+// A call takes 32 rows of the tile, lane = (row lane % 32, column half lane / 32): the row's norm and
+// boundaries sit in the lane's registers, each coordinate costs one binary search whose bits shift
+// straight into the plane words (the fused encode kernel's search), and the words go out as they are.
+template <int BM, bool RES>
 struct EpiQuant {
   uint8_t *codes;
   int64_t code_bytes;
   int d;
   const float *n32;        // fp32 norms of the rows (chunk-relative)
   const uint16_t *nhat;    // fp16 norms (chunk-relative)
-  float *resid;            // [rows, d] rotated residual, or null (Algorithm 1)
-  float *rsq;              // [rows, d / 64] partial ||r||^2, or null
+  float *resid;            // [rows, d] rotated residual (RES)
+  float *rsq;              // [rows, d / 64] partial ||r||^2 (RES)
   Codebook cb;
   int kp;                  // >= 0: the tile holds y 2^(kx + kp) (fp16 operands; kx from the row's norm)
-  // rows rb..rb+15 of the tile by the calling wave (lane = column)
-  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
+  static constexpr bool kRowLanes = true;
+  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    static_assert(BM > 0 || RES, "no index plane and no residual");
     constexpr int L = 1 << BM;
-    const int lane = threadIdx.x & 63;
-    // the 16 rows' norms: one load per lane, then uniform per row
-    float nl = 0.f, hl = 0.f;
-    if (lane < 16 && row0 + rb + lane < M) {
-      nl = n32[row0 + rb + lane];
-      hl = f16_to_f32(nhat[row0 + rb + lane]);
-    }
-    float tb[L > 1 ? L - 1 : 1], cc[L];  // (BM = 0: one cell, no boundary, centroid 0)
+    const int lane = threadIdx.x & 63, r = lane & 31, hc = lane >> 5;
+    const int64_t row = row0 + r;
+    if (row >= M) return;  // (both lanes of a row leave together)
+    const float n = n32[row];
+    // the tile holds y 2^s; comparing it with t_k (n 2^s) makes the decisions of y > t_k n exactly (the
+    // powers of two commute with the rounding of the product).  A zero row (y = 0) takes the boundaries
+    // t_k themselves, so its coordinates fall in the cell just below 0, as the fused kernel sets them
+    const int s = kp >= 0 ? row_scale_exp(n) + kp : 0;
+    const float ns = n == 0.f ? 1.f : __builtin_amdgcn_ldexpf(n, s);
+    float T[L > 1 ? L - 1 : 1], C[L];
 #pragma unroll
-    for (int k = 0; k < L - 1; ++k) tb[k] = cb.t[k];
+    for (int k = 0; k < L - 1; ++k) T[k] = cb.t[k] * ns;
 #pragma unroll
-    for (int k = 0; k < L; ++k) cc[k] = cb.c[k];
-    const int nblk = d >> 6;
-    float sq[16];  // r^2 of this lane's column, per row (summed over the block below)
-    // lane rr keeps row rr's 64 plane bits, so each plane is stored by 16 lanes at once after the rows
-    unsigned long long pm[BM > 0 ? BM : 1];
+    for (int k = 0; k < L; ++k) C[k] = cb.c[k];
+    const float nh = RES ? f16_to_f32(nhat[row]) : 0.f;
+    uint32_t P[BM > 0 ? BM : 1];
 #pragma unroll
-    for (int p = 0; p < (BM > 0 ? BM : 1); ++p) pm[p] = 0ull;
+    for (int p = 0; p < (BM > 0 ? BM : 1); ++p) P[p] = 0u;
+    float rs = 0.f;
+    const float *src = Cs[r] + 32 * hc;
+    float *rdst = RES ? resid + row * d + col0 + 32 * hc : nullptr;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      sq[rr] = 0.f;
-      const int r = rb + rr;
-      const int64_t row = row0 + r;
-      if (row >= M) continue;
-      const float n = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nl), rr));
-      // the scale undone exactly (a power of two)
-      const float y = kp >= 0 ? __builtin_amdgcn_ldexpf(Cs[r][lane], -(row_scale_exp(n) + kp)) : Cs[r][lane];
-      const float yq = n == 0.0f ? 0.0f : y, nq = n == 0.0f ? 1.0f : n;
-      // binary search: bit s of idx decided against the one boundary the higher bits leave
-      int idx = 0;
+    for (int c4 = 7; c4 >= 0; --c4) {  // columns high to low: bit c of a plane word is column c
+      float r4[4];
 #pragma unroll
-      for (int sbit = BM - 1; sbit >= 0; --sbit) {
-        const int s = 1 << sbit;
-        float t = tb[s - 1];
-#pragma unroll
-        for (int c = 1; c < L / (2 * s); ++c)
-          if (idx == 2 * s * c) t = tb[2 * s * c + s - 1];
-        idx += (yq > t * nq) ? s : 0;
+      for (int e = 3; e >= 0; --e) {
+        const float v = src[4 * c4 + e];
+        float cv = 0.f;
+        if constexpr (BM > 0) quant_coord<BM, RES>(v, T, C, P, cv);
+        if constexpr (RES) {
+          const float y = kp >= 0 ? __builtin_amdgcn_ldexpf(v, -s) : v;  // the scale undone exactly
+          r4[e] = fmaf(-nh, cv, y);
+          rs = fmaf(r4[e], r4[e], rs);
+        }
       }
-#pragma unroll
-      for (int p = 0; p < BM; ++p) {
-        const unsigned long long m = __ballot(((idx >> p) & 1) != 0);
-        pm[p] = lane == rr ? m : pm[p];
-      }
-      if (resid) {
-        float cv = cc[0];
-#pragma unroll
-        for (int k = 1; k < L; ++k) cv = idx == k ? cc[k] : cv;
-        const float nh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), rr));
-        const float rv = y - nh * cv;
-        resid[row * d + col0 + lane] = rv;
-        sq[rr] = rv * rv;
-      }
+      if constexpr (RES) *reinterpret_cast<float4 *>(rdst + 4 * c4) = float4{r4[0], r4[1], r4[2], r4[3]};
     }
-    if (BM > 0 && lane < 16 && row0 + rb + lane < M) {
-      uint8_t *dst = codes + (row0 + rb + lane) * code_bytes + (col0 >> 3);
+    if constexpr (BM > 0) {
+      uint8_t *dst = codes + row * code_bytes + ((col0 + 32 * hc) >> 3);
 #pragma unroll
-      for (int p = 0; p < BM; ++p) *reinterpret_cast<unsigned long long *>(dst + p * (d >> 3)) = pm[p];
+      for (int p = 0; p < BM; ++p) *reinterpret_cast<uint32_t *>(dst + p * (d >> 3)) = P[p];
     }
-    if (resid) {
-      // the 16 row sums over the lanes at once (independent shuffles in flight together)
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sq[rr] += __shfl_xor(sq[rr], o, 64);
-      float mine = sq[0];
-#pragma unroll
-      for (int rr = 1; rr < 16; ++rr) mine = (lane == rr) ? sq[rr] : mine;
-      if (lane < 16 && row0 + rb + lane < M) rsq[(row0 + rb + lane) * nblk + (col0 >> 6)] = mine;
+    if constexpr (RES) {
+      rs += __shfl_xor(rs, 32, 64);
+      if (hc == 0) rsq[row * (d >> 6) + (col0 >> 6)] = rs;
     }
   }
 };
+
+template <class T, class = void>
+struct is_row_lane_epi : std::false_type {};
+template <class T>
+struct is_row_lane_epi<T, std::void_t<decltype(T::kRowLanes)>> : std::bool_constant<T::kRowLanes> {};
 
 // QJL sign plane: bit = [(S r)_i >= 0]
 struct EpiSign {
@@ -397,7 +382,24 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
   uint16_t(*Bs)[PBN][PKP] = reinterpret_cast<uint16_t(*)[PBN][PKP]>(lds + (size_t)NPA * PBM * PKP * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t row0 = (int64_t)blockIdx.x * PBM, col0 = (int64_t)blockIdx.y * PBN;
+  // work-group -> (row block, column block).  Work-groups are dealt to the 8 XCDs in turn (id mod 8), each
+  // with its own L2: the column blocks of one row block take consecutive ids on one XCD, so they run
+  // side by side there and the row block's A operand crosses HBM once instead of once per column block
+  // (row-block counts that are not a multiple of 8: column blocks consecutive, XCDs mixed)
+  int64_t rblk, cblk;
+  {
+    const int ncb = (int)cdiv64(N, PBN);
+    const int64_t p = blockIdx.x;
+    if ((cdiv64(M, PBM) & 7) == 0) {
+      const int64_t j = p >> 3;
+      rblk = (j / ncb) * 8 + (p & 7);
+      cblk = j % ncb;
+    } else {
+      rblk = p / ncb;
+      cblk = p % ncb;
+    }
+  }
+  const int64_t row0 = rblk * PBM, col0 = cblk * PBN;
   const int ar = tid >> 1, ak = (tid & 1) * 16;  // A staging: row ar, k ak..ak+15
   const bool arow_ok = row0 + ar < M;
   int kx = 0;  // fp16 operands: the staged row's scale 2^kx
@@ -519,8 +521,12 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (qr0 + 32 * h < M && qc0 < N) {
+      if constexpr (is_row_lane_epi<EP>::value) {
+        ep(Cw, qr0 + 32 * h, qc0, M, N);
+      } else {
 #pragma unroll 1
-      for (int rb = 0; rb < GBM / 2; rb += 16) ep(Cw, qr0 + 32 * h, qc0, M, N, rb);
+        for (int rb = 0; rb < GBM / 2; rb += 16) ep(Cw, qr0 + 32 * h, qc0, M, N, rb);
+      }
     }
     // this half's reads of the buffer done before the next half overwrites it
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -533,46 +539,51 @@ template <int NPA, class LA, class EP>
 static int gemm_pieces(const char *name, LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N, int K,
                        hipStream_t st) {
   if (M <= 0 || N <= 0) return TQ_OK;
-  dim3 grid((unsigned)cdiv64(M, PBM), (unsigned)cdiv64(N, PBN));
+  const int64_t nblk = cdiv64(M, PBM) * cdiv64(N, PBN);
+  if (nblk > 0x7FFFFFFF) return TQ_ERR_INVALID;
   ProfScope ps(name, st);
-  hipLaunchKernelGGL((gemm_pieces_kernel<NPA, LA, EP>), grid, dim3(256), 0, st, la, b3, ep, M, N, K);
+  hipLaunchKernelGGL((gemm_pieces_kernel<NPA, LA, EP>), dim3((unsigned)nblk), dim3(256), 0, st, la, b3, ep, M, N, K);
   return launch_check();
 }
 
 // ----------------------------------------------------------------------------
 // small kernels: norms, zero fill, gamma finalisation, M = S Pi^T
 // ----------------------------------------------------------------------------
-// one row per 16 lanes (16 rows per work-group): each lane sums the squares of 4 consecutive elements
-// every 64, in fp64 (the fp16 norm must round as the exact value does), loads kept in flight together
+// one row per 16 lanes (16 rows per work-group): each lane sums the squares of its 16-byte pieces of the
+// row (4 fp32 or 8 bf16 / fp16 elements, the 16 lanes covering 256 contiguous bytes at a time) in fp64
+// (the fp16 norm must round as the exact value does), up to four loads in flight together
 template <int XT>
 __global__ __launch_bounds__(256) void norm_kernel(const void *x, int64_t ldx, int d, int64_t n, uint16_t *nhat,
                                                    float *n32) {
+  constexpr int EPL = XT == TQ_F32 ? 4 : 8;  // elements per 16-byte piece
   const int l16 = threadIdx.x & 15;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   double s = 0.0;
   if (row < n) {
-    for (int j0 = 4 * l16; j0 < d; j0 += 256) {
-      float v[4][4];
+    const uint8_t *src = static_cast<const uint8_t *>(x) + row * ldx * (XT == TQ_F32 ? 4 : 2);
+    for (int j0 = EPL * l16; j0 < d; j0 += 4 * 16 * EPL) {
+      uint4 t[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int j = j0 + 64 * u;
-        if (j >= d) {
-          v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.f;
-        } else if (XT == TQ_F32) {
-          const float4 t = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row * ldx + j);
-          v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
-        } else {
-          const uint2 t = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + row * ldx + j);
-          const uint16_t h[4] = {(uint16_t)(t.x & 0xFFFF), (uint16_t)(t.x >> 16), (uint16_t)(t.y & 0xFFFF),
-                                 (uint16_t)(t.y >> 16)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[u][e] = XT == TQ_BF16 ? bf16_to_f32(h[e]) : f16_to_f32(h[e]);
-        }
+        const int j = j0 + 16 * EPL * u;
+        t[u] = j < d ? *reinterpret_cast<const uint4 *>(src + (int64_t)j * (EPL == 4 ? 4 : 2)) : uint4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {t[u].x, t[u].y, t[u].z, t[u].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s = fma((double)v[u][e], (double)v[u][e], s);
+        for (int q = 0; q < 4; ++q) {
+          if (XT == TQ_F32) {
+            const double v = (double)__uint_as_float(w[q]);
+            s = fma(v, v, s);
+          } else {
+            const float lo = XT == TQ_BF16 ? bf16_to_f32((uint16_t)(w[q] & 0xFFFF)) : f16_to_f32((uint16_t)(w[q] & 0xFFFF));
+            const float hi = XT == TQ_BF16 ? bf16_to_f32((uint16_t)(w[q] >> 16)) : f16_to_f32((uint16_t)(w[q] >> 16));
+            s = fma((double)lo, (double)lo, s);
+            s = fma((double)hi, (double)hi, s);
+          }
+        }
+      }
     }
   }
 #pragma unroll
@@ -655,12 +666,15 @@ int encode_chunk(const tq_quantizer *q, LX lx, const void *x, int xt, int64_t ld
   };
   float *rs = prod ? resid : nullptr, *rq = prod ? rsq : nullptr;
   const int64_t cbytes = (int64_t)q->code_bytes;
-  switch (q->bmse) {
-    case 0: rc = rotate(EpiQuant<0>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
-    case 1: rc = rotate(EpiQuant<1>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
-    case 2: rc = rotate(EpiQuant<2>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
-    case 3: rc = rotate(EpiQuant<3>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
-    case 4: rc = rotate(EpiQuant<4>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+  switch (q->bmse * 2 + (prod ? 1 : 0)) {
+    case 1: rc = rotate(EpiQuant<0, true>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 2: rc = rotate(EpiQuant<1, false>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 3: rc = rotate(EpiQuant<1, true>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 4: rc = rotate(EpiQuant<2, false>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 5: rc = rotate(EpiQuant<2, true>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 6: rc = rotate(EpiQuant<3, false>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 7: rc = rotate(EpiQuant<3, true>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
+    case 8: rc = rotate(EpiQuant<4, false>{codes, cbytes, d, n32, norms, rs, rq, q->cb, -1}); break;
     default: rc = TQ_ERR_UNSUPPORTED;
   }
   if (rc != TQ_OK) return rc;
