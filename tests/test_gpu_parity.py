@@ -45,7 +45,10 @@ def _idx_of(codes, d, bits, mode_prod):
     return oracle.parse_mse_record(c, d, bits), None
 
 
-@pytest.mark.parametrize("n,d,bits", [(4096, 128, 2), (4096, 128, 3), (1000, 64, 1), (333, 256, 4), (130, 512, 3)])
+# (1024 and 1100 rows at d > 128: the GEMM path's grid with the column blocks of a row block grouped on one XCD,
+# 8 row blocks, and with a row-block count that is not a multiple of 8)
+@pytest.mark.parametrize("n,d,bits", [(4096, 128, 2), (4096, 128, 3), (1000, 64, 1), (333, 256, 4), (130, 512, 3),
+                                      (1024, 256, 3), (1100, 512, 2)])
 def test_encode_mse_parity(api, n, d, bits):
     x, pi, _, _ = _unit_inputs(n, d) if d == 128 else (synth.unit_test_vectors(n, d, 7, 8), synth.haar_rotation(d, 9), None, None)
     qz = api.Quantizer(d, bits, api.TQ_MSE, pi)
@@ -63,7 +66,7 @@ def test_encode_mse_parity(api, n, d, bits):
     print(f"mse d={d} b={bits}: mismatches {nbad}, tie-zone coords {nties}")
 
 
-@pytest.mark.parametrize("n,d,bits", [(4096, 128, 3), (4096, 128, 2), (257, 256, 4), (130, 512, 3)])
+@pytest.mark.parametrize("n,d,bits", [(4096, 128, 3), (4096, 128, 2), (257, 256, 4), (130, 512, 3), (1024, 512, 3), (1300, 256, 2)])
 def test_encode_prod_parity(api, n, d, bits):
     if d == 128:
         x, pi, s, _ = _unit_inputs(n, d)

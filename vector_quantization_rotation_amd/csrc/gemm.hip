@@ -140,6 +140,12 @@ struct LoadDequant {
 
 typedef float CTile[GBN + 1];
 
+// a wave's 32 x 64 result block of the piece-wise contraction, column-major: column c at Cs[c], its 32 rows
+// and 4 floats of padding (a 144-byte column stride: the 16-byte writes of eight consecutive columns and the
+// 4-byte reads of 32 consecutive rows each fall in distinct LDS banks)
+constexpr int GCS = 36;
+typedef float CCol[GCS];
+
 // ----------------------------------------------------------------------------
 // epilogues (run by all 256 threads with the tile in LDS)
 // ----------------------------------------------------------------------------
@@ -158,7 +164,7 @@ struct EpiStore {
 // For Algorithm 2 (RES) also the rotated residual y - n_hat c[idx] and its squared norm over the block
 // (fp32: the fp16 gamma tolerates 1e-5 relative), one partial per (row, block) so no atomics are needed.
 // BM index bits; BM = 0 (Algorithm 2 at one bit) writes no index plane and the residual is y itself.
-// A call takes 32 rows of the tile, lane = (row lane % 32, column half lane / 32): the row's norm and
+// A call takes a wave's 32 x 64 block, lane = (row lane % 32, column half lane / 32): the row's norm and
 // boundaries sit in the lane's registers, each coordinate costs one binary search whose bits shift
 // straight into the plane words (the fused encode kernel's search), and the words go out as they are.
 template <int BM, bool RES>
@@ -173,7 +179,7 @@ struct EpiQuant {
   Codebook cb;
   int kp;                  // >= 0: the tile holds y 2^(kx + kp) (fp16 operands; kx from the row's norm)
   static constexpr bool kRowLanes = true;
-  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+  __device__ void operator()(const CCol *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
     static_assert(BM > 0 || RES, "no index plane and no residual");
     constexpr int L = 1 << BM;
     const int lane = threadIdx.x & 63, r = lane & 31, hc = lane >> 5;
@@ -195,14 +201,14 @@ struct EpiQuant {
 #pragma unroll
     for (int p = 0; p < (BM > 0 ? BM : 1); ++p) P[p] = 0u;
     float rs = 0.f;
-    const float *src = Cs[r] + 32 * hc;
+    const CCol *src = Cs + 32 * hc;  // column 32 hc + c of row r: src[c][r]
     float *rdst = RES ? resid + row * d + col0 + 32 * hc : nullptr;
 #pragma unroll
     for (int c4 = 7; c4 >= 0; --c4) {  // columns high to low: bit c of a plane word is column c
       float r4[4];
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
-        const float v = src[4 * c4 + e];
+        const float v = src[4 * c4 + e][r];
         float cv = 0.f;
         if constexpr (BM > 0) quant_coord<BM, RES>(v, T, C, P, cv);
         if constexpr (RES) {
@@ -230,24 +236,22 @@ struct is_row_lane_epi : std::false_type {};
 template <class T>
 struct is_row_lane_epi<T, std::void_t<decltype(T::kRowLanes)>> : std::bool_constant<T::kRowLanes> {};
 
-// QJL sign plane: bit = [(S r)_i >= 0]
+// QJL sign plane: bit = [(S r)_i >= 0].  Lane = (row lane % 32, column half lane / 32) of a wave's 32 x 64
+// block: each lane shifts its 32 sign bits into one word (columns high to low) and stores it
 struct EpiSign {
   uint8_t *codes;
   int64_t code_bytes;
   int d, plane;
-  // rows rb..rb+15 of the tile by the calling wave (lane = column)
-  __device__ void operator()(const CTile *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N, int rb) const {
-    const int lane = threadIdx.x & 63;
-    unsigned long long pm = 0ull;  // lane rr keeps row rr's 64 sign bits; 16 lanes store them at once
+  static constexpr bool kRowLanes = true;
+  __device__ void operator()(const CCol *Cs, int64_t row0, int64_t col0, int64_t M, int64_t N) const {
+    const int lane = threadIdx.x & 63, r = lane & 31, hc = lane >> 5;
+    const int64_t row = row0 + r;
+    if (row >= M) return;
+    const CCol *src = Cs + 32 * hc;
+    uint32_t w = 0u;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      if (row0 + rb + rr >= M) break;
-      const unsigned long long m = __ballot(Cs[rb + rr][lane] >= 0.0f);
-      pm = lane == rr ? m : pm;
-    }
-    if (lane < 16 && row0 + rb + lane < M)
-      *reinterpret_cast<unsigned long long *>(codes + (row0 + rb + lane) * code_bytes + plane * (d >> 3) + (col0 >> 3)) =
-          pm;
+    for (int c = 31; c >= 0; --c) w = (w << 1) | (src[c][r] >= 0.0f ? 1u : 0u);
+    *reinterpret_cast<uint32_t *>(codes + row * code_bytes + plane * (d >> 3) + ((col0 + 32 * hc) >> 3)) = w;
   }
 };
 
@@ -328,7 +332,13 @@ static int gemm(const char *name, LA la, LB lb, EP ep, int64_t M, int64_t N, int
 // k-steps staged in LDS with the next step's loads in registers; the epilogues
 // of the fp32 kernel run once per quadrant.
 // ----------------------------------------------------------------------------
-constexpr int PBM = 128, PBN = 128, PBK = 32, PKP = 40;
+constexpr int PBM = 128, PBN = 128, PBK = 32;
+
+// element offset (u16) of row r's k chunk c (8 elements, 16 bytes) in a staged k-step: 64-byte rows, the
+// chunks XOR-swizzled by (r / 2) % 4, so that a fragment read (eight consecutive rows, one chunk) and a
+// staging write (two rows and all four chunks, or four rows and two chunks) each cover eight distinct
+// 16-byte bank groups
+__device__ __forceinline__ int pk_off(int r, int c) { return r * PBK + 8 * (c ^ ((r >> 1) & 3)); }
 
 typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 
@@ -368,7 +378,8 @@ __device__ __forceinline__ floatx4 g_terms_half(const gf16x8 &a, const gf16x8 (&
 }
 
 template <int NPA, class LA, class EP>
-__global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N,
+__global__ __launch_bounds__(256) void
+gemm_pieces_kernel(LA la, const uint16_t *b3, EP ep, int64_t M, int64_t N,
                                                           int K) {
   // fp16 operands: one row piece (scaled), two matrix pieces [2][N][K]; else NPA bf16 row pieces, three
   // matrix pieces [3][N][K]
@@ -376,10 +387,10 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
   static_assert(!HP || NPA == 1, "fp16 operands: one row piece");
   constexpr int NB = HP ? 2 : 3;
   // one buffer: the staged pieces during the contraction, then each wave's 64 x 64 result tile
-  constexpr size_t AB = (size_t)(NPA + NB) * PBM * PKP * 2, CT = (size_t)4 * (GBM / 2) * (GBN + 1) * 4;
+  constexpr size_t AB = (size_t)(NPA + NB) * PBM * PBK * 2, CT = (size_t)4 * GBN * GCS * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[AB > CT ? AB : CT];
-  uint16_t(*As)[PBM][PKP] = reinterpret_cast<uint16_t(*)[PBM][PKP]>(lds);
-  uint16_t(*Bs)[PBN][PKP] = reinterpret_cast<uint16_t(*)[PBN][PKP]>(lds + (size_t)NPA * PBM * PKP * 2);
+  uint16_t *As = reinterpret_cast<uint16_t *>(lds);                                  // [NPA][PBM] rows
+  uint16_t *Bs = reinterpret_cast<uint16_t *>(lds + (size_t)NPA * PBM * PBK * 2);    // [NB][PBN] rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   // work-group -> (row block, column block).  Work-groups are dealt to the 8 XCDs in turn (id mod 8), each
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
         for (int q = 0; q < 4; ++q)
           w[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_ldexpf(v[8 * h + 2 * q], kx),
                                                                          __builtin_amdgcn_ldexpf(v[8 * h + 2 * q + 1], kx)));
-        *reinterpret_cast<uint4 *>(&As[0][ar][ak + 8 * h]) = uint4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<uint4 *>(As + pk_off(ar, (ak >> 3) + h)) = uint4{w[0], w[1], w[2], w[3]};
       } else {
         uint32_t w[3][4];
 #pragma unroll
@@ -456,13 +467,14 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
           for (int p = 0; p < 3; ++p) w[p][q] = g_pack2(p0[p], p1[p]);
         }
 #pragma unroll
-        for (int p = 0; p < NPA; ++p) *reinterpret_cast<uint4 *>(&As[p][ar][ak + 8 * h]) = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
+        for (int p = 0; p < NPA; ++p)
+          *reinterpret_cast<uint4 *>(As + p * PBM * PBK + pk_off(ar, (ak >> 3) + h)) = uint4{w[p][0], w[p][1], w[p][2], w[p][3]};
       }
     }
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
       const int e = tid + 256 * i, p = e >> 9, rem = e & 511, br = rem >> 2, kk = (rem & 3) * 8;
-      *reinterpret_cast<uint4 *>(&Bs[p][br][kk]) = rb[i];
+      *reinterpret_cast<uint4 *>(Bs + p * PBN * PBK + pk_off(br, kk >> 3)) = rb[i];
     }
   };
 
@@ -476,12 +488,13 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
     if constexpr (HP) {
       gf16x8 af[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) af[rt] = *reinterpret_cast<const gf16x8 *>(&As[0][64 * wm + 16 * rt + fr][fk]);
+      for (int rt = 0; rt < 4; ++rt) af[rt] = *reinterpret_cast<const gf16x8 *>(As + pk_off(64 * wm + 16 * rt + fr, fk >> 3));
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         gf16x8 bf[3];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) bf[p] = *reinterpret_cast<const gf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+        for (int p = 0; p < 2; ++p)
+          bf[p] = *reinterpret_cast<const gf16x8 *>(Bs + p * PBN * PBK + pk_off(64 * wn + 16 * ct + fr, fk >> 3));
         bf[2] = bf[1];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms_half(af[rt], bf, acc[rt][ct]);
@@ -492,42 +505,39 @@ __global__ __launch_bounds__(256) void gemm_pieces_kernel(LA la, const uint16_t 
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          af[rt][p] = p < NPA ? *reinterpret_cast<const gbf16x8 *>(&As[p][64 * wm + 16 * rt + fr][fk]) : af[rt][0];
+          af[rt][p] = p < NPA ? *reinterpret_cast<const gbf16x8 *>(As + p * PBM * PBK + pk_off(64 * wm + 16 * rt + fr, fk >> 3))
+                              : af[rt][0];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         gbf16x8 bf[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) bf[p] = *reinterpret_cast<const gbf16x8 *>(&Bs[p][64 * wn + 16 * ct + fr][fk]);
+        for (int p = 0; p < 3; ++p)
+          bf[p] = *reinterpret_cast<const gbf16x8 *>(Bs + p * PBN * PBK + pk_off(64 * wn + 16 * ct + fr, fk >> 3));
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = g_terms<NPA>(af[rt], bf, acc[rt][ct]);
       }
     }
   }
-  // every wave turns its own 64 x 64 quadrant to row-major in its part of the buffer, 32 rows at a time,
-  // and runs the epilogue on them 16 rows at a time (no work-group barrier after the first; the half
-  // quadrants keep the buffer at 33 KB, so the fp16-operand form fits four work-groups per CU)
+  // every wave stages its own 64 x 64 quadrant, 32 rows at a time, column-major in its part of the buffer
+  // (one 16-byte write per accumulator tile: a lane's four rows of one column are adjacent) and runs the
+  // epilogue on each half (no work-group barrier after the first)
+  static_assert(is_row_lane_epi<EP>::value, "epilogues take a wave's 32 x 64 block");
   __syncthreads();  // every read of the staged pieces done
-  CTile *Cw = reinterpret_cast<CTile *>(lds + (size_t)wave * (GBM / 2) * (GBN + 1) * 4);
+  CCol *Cw = reinterpret_cast<CCol *>(lds + (size_t)wave * GBN * GCS * 4);
   const int64_t qr0 = row0 + 64 * wm, qc0 = col0 + 64 * wn;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Cw[16 * rt + 4 * (lane >> 4) + e][16 * ct + fr] = acc[2 * h + rt][ct][e];
+      for (int ct = 0; ct < 4; ++ct) {
+        const floatx4 v = acc[2 * h + rt][ct];
+        *reinterpret_cast<float4 *>(&Cw[16 * ct + fr][16 * rt + 4 * (lane >> 4)]) = float4{v[0], v[1], v[2], v[3]};
+      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (qr0 + 32 * h < M && qc0 < N) {
-      if constexpr (is_row_lane_epi<EP>::value) {
-        ep(Cw, qr0 + 32 * h, qc0, M, N);
-      } else {
-#pragma unroll 1
-        for (int rb = 0; rb < GBM / 2; rb += 16) ep(Cw, qr0 + 32 * h, qc0, M, N, rb);
-      }
-    }
+    if (qr0 + 32 * h < M && qc0 < N) ep(Cw, qr0 + 32 * h, qc0, M, N);
     // this half's reads of the buffer done before the next half overwrites it
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
