@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
     ap.add_argument("--cpu-encode-rows", type=int, default=524288, help="rows per kind the oracle encodes")
-    ap.add_argument("--only", choices=["", "encode", "attention", "global", "search"], default="",
+    ap.add_argument("--only", choices=["", "encode", "attention", "global", "global_encode", "search"], default="",
                     help="a short run of one part (for counter profiles): the one-layer encode, the timed "
-                         "attention steps, the global-layer attention steps, or the search scan")
+                         "attention steps, the global-layer attention steps, the global-layer encode, or the "
+                         "search scan")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
@@ -141,6 +142,34 @@ def global_only(steps: int, warmup: int, calib: bool = False):
                                            "gbs": round(pk / dt / 1e9, 2)}}), flush=True)
 
 
+def global_encode_only(steps: int):
+    """The global-layer encode (keys mse 3-bit and values prod 2-bit of batch 4 x 4 KV heads x 65536 tokens,
+    head_dim 512, bf16 rows: the GEMM path) run steps times, for counter profiles; prints one JSON line."""
+    import torch
+    from vector_quantization_rotation_amd import api, synth, workloads
+    L = workloads.HET_LAYERS["global"]
+    hB, hHkv, hT, hd = L["B"], L["Hkv"], L["T"], L["d"]
+    hch = synth.outlier_channels(hHkv, hd, 4, L["seeds"]["chan"])
+    Kr = synth.kv_bf16_torch((hB, hHkv, hT, hd), L["seeds"]["K"], hch, "cuda", student_t_nu=workloads.HET_NU).view(-1, hd)
+    Vr = synth.kv_bf16_torch((hB, hHkv, hT, hd), L["seeds"]["V"], hch, "cuda", student_t_nu=workloads.HET_NU).view(-1, hd)
+    kq = api.Quantizer(hd, 3, api.TQ_MSE, synth.haar_rotation(hd, L["seeds"]["piK"]))
+    vq = api.Quantizer(hd, 2, api.TQ_PROD, synth.haar_rotation(hd, L["seeds"]["piV"]),
+                       synth.gaussian_projection(hd, L["seeds"]["sV"]))
+    n = Kr.shape[0]
+    kc = torch.empty((n, kq.code_bytes), dtype=torch.uint8, device="cuda")
+    vc = torch.empty((n, vq.code_bytes), dtype=torch.uint8, device="cuda")
+    kn, vn, vg = (torch.empty((n,), dtype=torch.int16, device="cuda") for _ in range(3))
+    times = []
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kq.encode(Kr, codes=kc, norms=kn)
+        vq.encode(Vr, codes=vc, norms=vn, gammas=vg)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    print(json.dumps({"global_encode": {"ms": [round(t * 1e3, 3) for t in times], "vectors": 2 * n}}), flush=True)
+
+
 def search_only(steps: int):
     """The search workload (10^6 records of d 1536, prod 4-bit, 1000 queries, top-10): encode once, then the
     scan + top-k `steps` times, for counter profiles; prints one JSON line."""
@@ -191,6 +220,9 @@ def main():
         return
     if args.only == "global":
         global_only(args.steps, args.warmup, args.copy_calib)
+        return
+    if args.only == "global_encode":
+        global_encode_only(args.steps)
         return
     if args.only == "search":
         search_only(args.steps)
