@@ -45,10 +45,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, kv-head) slices the oracle times")
     ap.add_argument("--cpu-encode-rows", type=int, default=524288, help="rows per kind the oracle encodes")
-    ap.add_argument("--only", choices=["", "encode", "attention", "global", "global_encode", "search"], default="",
+    ap.add_argument("--only", choices=["", "encode", "attention", "global", "global_encode", "prefill", "search"],
+                    default="",
                     help="a short run of one part (for counter profiles): the one-layer encode, the timed "
-                         "attention steps, the global-layer attention steps, the global-layer encode, or the "
-                         "search scan")
+                         "attention steps, the global-layer attention steps, the global-layer encode, the "
+                         "chunked prefill over token-tiled values, or the search scan")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
@@ -170,6 +171,30 @@ def global_encode_only(steps: int):
     print(json.dumps({"global_encode": {"ms": [round(t * 1e3, 3) for t in times], "vectors": 2 * n}}), flush=True)
 
 
+def prefill_only(steps: int):
+    """The chunked prefill of the benchmark (512 causal query tokens x 32 heads over 8 KV heads, head_dim 128,
+    against a 4096-token cache, token-tiled values) run steps times, for kernel traces; prints one JSON line."""
+    import torch
+    from vector_quantization_rotation_amd import _lib, api, workloads
+    Hq, Hkv, d = 32, 8, 128
+    pB, pM, pT = 1, 512, 4096
+    pc = workloads.build_attention_cache(pB, Hq, Hkv, pT, d, tiles=True)
+    pq = torch.randn((pB, pM, Hq, d), generator=torch.Generator("cuda").manual_seed(721), device="cuda").to(torch.bfloat16)
+    qpos = torch.full((pB,), pT - pM, dtype=torch.int32, device="cuda")
+    pout = torch.empty((pB, pM, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty((_lib.load().tq_attn_prefill_ws_bytes(pc.kq.handle, pB, pM, Hq, Hkv, pT, 1),), dtype=torch.uint8,
+                     device="cuda")
+    times = []
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        api.attn_prefill(pc.kq, pc.vq, pq, pc.kcodes, pc.knorms, pc.vtiles, pc.vnorms, pc.vgammas, qpos,
+                         1 / math.sqrt(d), out=pout, ws=ws, vlayout=api.TQ_LAYOUT_TILE32)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    print(json.dumps({"prefill": {"ms": [round(t * 1e3, 3) for t in times], "query_tokens": pB * pM}}), flush=True)
+
+
 def search_only(steps: int):
     """The search workload (10^6 records of d 1536, prod 4-bit, 1000 queries, top-10): encode once, then the
     scan + top-k `steps` times, for counter profiles; prints one JSON line."""
@@ -223,6 +248,9 @@ def main():
         return
     if args.only == "global_encode":
         global_encode_only(args.steps)
+        return
+    if args.only == "prefill":
+        prefill_only(args.steps)
         return
     if args.only == "search":
         search_only(args.steps)

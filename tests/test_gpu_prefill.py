@@ -93,7 +93,8 @@ def test_prefill_one_token_equals_decode_step(api):
 @pytest.mark.parametrize("d,kb,vb,B,M,Hq,Hkv,T,qpos", [
     (128, 3, 2, 2, 37, 8, 2, 304, [100, 250]),     # the wave-streaming kernel (stride a multiple of 8)
     (128, 3, 2, 1, 64, 32, 8, 200, [0]),           # the first chunk of a prompt
-    (128, 3, 2, 1, 160, 32, 8, 400, [200]),        # 5120 query rows: rotated in a kernel of their own
+    (128, 3, 2, 1, 160, 32, 8, 400, [200]),        # 5120 query rows of one split each: rotated back by one GEMM
+    (128, 3, 2, 1, 128, 32, 1, 3200, [3000]),      # 4096 rows over several splits: merge, then the GEMM
     (128, 2, 3, 1, 20, 8, 2, 301, [270]),          # 2-bit value indices: the four-wave kernel
     (256, 3, 2, 1, 12, 16, 4, 160, [140]),         # head_dim 256
     (512, 3, 2, 2, 9, 8, 1, 200, [150, 40]),       # head_dim 512: the global-layer kernel

@@ -226,6 +226,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int6
   const int j = (int)(e % (2 * d));
   const int64_t rec = 2 + 2 * (int64_t)d;
   const float *pp = part + bh * nsplit * rec;
+  if (nsplit == 1) {  // (a prefill chunk's rows: one split each) the general form below reduces to v / l
+    const float l = pp[1], v = pp[2 + j];
+    merged[e] = l > 0.f ? v / l : 0.f;
+    return;
+  }
   float M = -INFINITY;
   for (int q0 = 0; q0 < nsplit; q0 += FIN_CHUNK) {
     float m[FIN_CHUNK], l[FIN_CHUNK];
@@ -459,10 +464,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *part, in
 
 size_t attn_merge_ws_bytes(int BH, int d) { return (size_t)BH * 2 * d * sizeof(float); }
 
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
-                 float *out, hipStream_t st) {
+// rows from which the rotation back runs as one GEMM (a prefill chunk: one row per query token and head),
+// after the merge kernel, or straight over the records when every row took one split.  Below, one fused
+// launch whose work-groups each read the d x 2d matrix for four rows: fine for a decode step's few hundred
+// rows, while the 16384 rows of a 512-token chunk made it read 512 MB from L2 (111 us; the GEMM 20 us)
+constexpr int kCombineGemmRows = 4096;
+
+int attn_combine(const float *part, int BH, int nsplit, int d, const tq_quantizer *vq, float *merged, float *out,
+                 hipStream_t st) {
   if (BH == 0) return TQ_OK;
   ProfScope ps("attn_combine", st);
+  const float *pi = vq->pi, *s = vq->s;
+  if (BH >= kCombineGemmRows && vq->piT && vq->sT) {
+    if (nsplit == 1) return rotate_back(part, BH, d, vq->piT, vq->sT, out, true, st);
+    const int64_t n = (int64_t)BH * 2 * d;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, part, (int64_t)BH, nsplit,
+                       d, merged);
+    const int rc = launch_check();
+    if (rc != TQ_OK) return rc;
+    return rotate_back(merged, BH, d, vq->piT, vq->sT, out, false, st);
+  }
   if (nsplit <= CMB_SPLITS && (d == 64 || d == 128 || d == 256)) {
     const dim3 grid((unsigned)cdiv64(BH, 4), (unsigned)(d / 32));
     if (d == 64) hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);
@@ -578,7 +599,7 @@ static int run_attn_rows(const tq_quantizer *kq, const tq_quantizer *vq, const v
   if ((rc = launch_check()) != TQ_OK) return rc;
   float *merged = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
                                             (((size_t)BH * p.nsplit * partial_floats(d) * 4 + 255) & ~(size_t)255));
-  return attn_combine(part, (int)BH, p.nsplit, d, vq->pi, vq->s, merged, out, st);
+  return attn_combine(part, (int)BH, p.nsplit, d, vq, merged, out, st);
 }
 
 int run_attn_decode(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,

@@ -1862,12 +1862,13 @@ __device__ __forceinline__ void prep_images(const PrepArgs &a, int unit, int h, 
   // short of the bits' sums by half the digits' values of those coordinates (a constant of the query,
   // taken off the score's offset below).  This work-group writes the 16 lanes of its head (rows 4 h ..
   // 4 h + 3 of the four lane groups) in every image.
+  // (a thread takes one word position w of one k-group gg of image ii and writes it for the four digit
+  // rows: the four rows' words hold the digits of the same four coordinates)
   constexpr int NI8 = (FOLD ? 1 : KP) * (D / 128);
-  for (int e = tid; e < NI8 * 16 * 8; e += 256) {
-    const int w = e & 7, r = (e >> 3) & 15, ii = e >> 7;
+  for (int e = tid; e < NI8 * 4 * 8; e += 256) {
+    const int w = e & 7, gg = (e >> 3) & 3, ii = e >> 5;
     const int wb = ii % (D / 128), p = ii / (D / 128);
-    const int dg = r & 3, gg = r >> 2, il = 16 * gg + 4 * h + dg;
-    uint32_t word = 0;
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
     if (present) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
@@ -1878,10 +1879,13 @@ __device__ __forceinline__ void prep_images(const PrepArgs &a, int unit, int h, 
         const float f = t == 0 ? 2.f : t == 1 ? 1.f : t == 2 ? 0.5f : -1.f;
         uint8_t o[4];
         split_fix4_e4m3(fminf(fmaxf((FOLD ? 1.f : 2.f * a.kbeta[p]) * qp[j] * sq, -224.f), 224.f), f, o);
-        word |= (uint32_t)o[dg] << (8 * bb);
+#pragma unroll
+        for (int dg = 0; dg < 4; ++dg) word[dg] |= (uint32_t)o[dg] << (8 * bb);
       }
     }
-    a.qimg[(((int64_t)unit * NI8 + ii) * 64 + il) * 8 + w] = (int)word;
+#pragma unroll
+    for (int dg = 0; dg < 4; ++dg)
+      a.qimg[(((int64_t)unit * NI8 + ii) * 64 + 16 * gg + 4 * h + dg) * 8 + w] = (int)word[dg];
   }
   // half the digit values of the images at coordinates 3 mod 4 (the sign-form nibbles)
   float cs = 0.f;
@@ -2367,8 +2371,8 @@ size_t attn_fast_ws_bytes(int D, int KB, int B, int Hq, int Hkv, int64_t T) {
   return n;
 }
 
-int attn_combine(const float *part, int BH, int nsplit, int d, const float *pi, const float *s, float *merged,
-                 float *out, hipStream_t st);
+int attn_combine(const float *part, int BH, int nsplit, int d, const tq_quantizer *vq, float *merged, float *out,
+                 hipStream_t st);
 
 int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q, int qt, int B, int Hq, int Hkv,
                   const uint8_t *kcodes, const uint16_t *knorms, const uint32_t *vtiles, const uint16_t *vnorms,
@@ -2450,7 +2454,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       if (KB == 3) hipExtLaunchKernelGGL(attn_wave_kernel<3>, grid, dim3(64), 0, st, pk.start, pk.stop, 0, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
-    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq, reinterpret_cast<float *>(w + fp.merge_off), out,
                         st);
   }
   if (widek) {
@@ -2485,7 +2489,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
       if (KB == 3) hipExtLaunchKernelGGL(attn_wide_kernel<3>, grid, blk, 0, st, pk.start, pk.stop, 0, fa);
     }
     if ((rc = launch_check()) != TQ_OK) return rc;
-    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+    return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq, reinterpret_cast<float *>(w + fp.merge_off), out,
                         st);
   }
 #define TQ_FAST(DD, KK, VV) \
@@ -2499,7 +2503,7 @@ int run_attn_fast(const tq_quantizer *kq, const tq_quantizer *vq, const void *q,
   TQ_FAST(512, 1, 1) TQ_FAST(512, 2, 1) TQ_FAST(512, 3, 1)
 #undef TQ_FAST
   if (rc != TQ_OK) return rc;
-  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq->pi, vq->s, reinterpret_cast<float *>(w + fp.merge_off), out,
+  return attn_combine(fa.part, B * Hq, fp.nsplit, D, vq, reinterpret_cast<float *>(w + fp.merge_off), out,
                         st);
 }
 

@@ -798,6 +798,31 @@ size_t score_ws_bytes(const tq_quantizer *q, int64_t m, int64_t n, int k) {
   return b;
 }
 
+// the attention terms of rows that took one split each: a row's split record [m, l, terms (2 d)] read as
+// its terms / l (0 while l = 0), the merge of a single split
+struct LoadSplit1 {
+  const float *part;
+  int d;
+  __device__ void operator()(int64_t r, int k, float *v) const {
+    const float *rec = part + r * (2 + 2 * (int64_t)d);
+    const float l = rec[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = l > 0.f ? rec[2 + k + i] / l : 0.f;
+  }
+};
+
+// attention output of many rows on the fp32 matrix cores: out[r] = Pi^T a_mse[r] + S^T a_qjl[r], as one
+// GEMM against [Pi^T | S^T], over merged rows [rows][2 d] (the Algorithm 2 value terms, already scaled),
+// or, with `split1`, straight over one-split records
+int rotate_back(const float *merged, int64_t rows, int d, const float *piT, const float *sT, float *out, bool split1,
+                hipStream_t st) {
+  if (split1)
+    return gemm("attn_rotate_back", LoadSplit1{merged, d}, LoadCols2{piT, sT, d}, EpiStore{out, d}, rows, d, 2 * d,
+                st);
+  return gemm("attn_rotate_back", LoadF32{merged, 2 * (int64_t)d}, LoadCols2{piT, sT, d}, EpiStore{out, d}, rows, d,
+              2 * d, st);
+}
+
 // rotated queries [Pi q | S q] (the second half for Algorithm 2 only), fp32 [m][kq]
 int rotate_queries(const tq_quantizer *q, const float *queries, int64_t m, int64_t ldq, float *qrot, hipStream_t st) {
   const int d = q->d;

@@ -140,6 +140,8 @@ int run_encode_cache(const tq_quantizer *q, const void *x, int xt, int64_t nseq,
 int run_tile_records_at(const tq_quantizer *q, const uint8_t *codes, int64_t nseq, int64_t T, int64_t toff,
                         int64_t ntile_dst, uint32_t *tiles, hipStream_t st);
 int compute_sPiT(int d, const float *s, const float *pi, float *m, hipStream_t st);
+int rotate_back(const float *merged, int64_t rows, int d, const float *piT, const float *sT, float *out, bool split1,
+                hipStream_t st);
 int device_cus();  // compute units of the current device (cached)
 bool decode_fused_supported(const tq_quantizer *q);
 int run_decode_fused(const tq_quantizer *q, const uint8_t *codes, const uint16_t *norms, const uint16_t *gammas,
