@@ -101,14 +101,21 @@ def _oracle_encoded(qz_bits, prod, x, pi, s):
     return _dev(enc["record"]), _dev(parity.f16_bits(enc["n_hat"])), gam, xt
 
 
-@pytest.mark.parametrize("mode,bits", [("mse", 2), ("prod", 3), ("mse", 4), ("prod", 2)])
-def test_decode_parity(api, mode, bits):
-    x, pi, s, _ = _unit_inputs()
+# (1000 rows: a last 64-record tile of 40, whose rows the kernel stores and no row past it)
+@pytest.mark.parametrize("mode,bits,n", [("mse", 2, 4096), ("prod", 3, 4096), ("mse", 4, 4096), ("prod", 2, 4096),
+                                         ("mse", 3, 1000), ("prod", 3, 1000)])
+def test_decode_parity(api, mode, bits, n):
+    x, pi, s, _ = _unit_inputs(n)
     d = 128
     prod = mode == "prod"
     qz = api.Quantizer(d, bits, api.TQ_PROD if prod else api.TQ_MSE, pi, s if prod else None)
     codes, norms, gammas, ref = _oracle_encoded(bits, prod, x, pi, s)
-    out = qz.decode(codes, norms, gammas).cpu().numpy()
+    # rows of d within a wider buffer (row stride d + 4) with 64 rows below: what lies outside stays as it was
+    big = torch.full((n + 64, d + 4), 7.0, dtype=torch.float32, device="cuda")
+    qz.decode(codes, norms, gammas, out=big[:n, :d])
+    big = big.cpu().numpy()
+    assert np.all(big[n:] == 7.0) and np.all(big[:n, d:] == 7.0)
+    out = big[:n, :d]
     err = parity.rel_rows(out, ref)
     assert np.all(err <= parity.RTOL), err.max()
     # the kernel's own arithmetic bound, far inside the gate: each product carries the top 16 significant

@@ -34,8 +34,13 @@ struct DecArgs {
 
 template <int D, bool PROD>
 struct __attribute__((aligned(16))) DecLds {
-  uint16_t am[2][DB][D + 8];              // c[idx] pieces
-  uint16_t aq[PROD ? DB : 1][D + 8];      // 2 s - 1
+  union {
+    struct {
+      uint16_t am[2][DB][D + 8];          // c[idx] pieces
+      uint16_t aq[PROD ? DB : 1][D + 8];  // 2 s - 1
+    } op;
+    float ot[DB][D + 4];                  // the tile's output rows, staged for whole-row stores
+  } u;
   float nh[DB], gq[DB];                   // n and qjl gamma per record
 };
 
@@ -125,9 +130,9 @@ __global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_wave
         mi[q] = d_pack2(m2[0], m2[1]);
         sg[q] = s2[0] | (s2[1] << 16);
       }
-      *reinterpret_cast<uint4 *>(&sh.am[0][sr][sk + i]) = uint4{hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<uint4 *>(&sh.am[1][sr][sk + i]) = uint4{mi[0], mi[1], mi[2], mi[3]};
-      if (PROD) *reinterpret_cast<uint4 *>(&sh.aq[sr][sk + i]) = uint4{sg[0], sg[1], sg[2], sg[3]};
+      *reinterpret_cast<uint4 *>(&sh.u.op.am[0][sr][sk + i]) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4 *>(&sh.u.op.am[1][sr][sk + i]) = uint4{mi[0], mi[1], mi[2], mi[3]};
+      if (PROD) *reinterpret_cast<uint4 *>(&sh.u.op.aq[sr][sk + i]) = uint4{sg[0], sg[1], sg[2], sg[3]};
     }
     if (tid % NW == 0) {
       sh.nh[sr] = fn;
@@ -150,10 +155,10 @@ __global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_wave
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + j16, k = 32 * ks + 8 * g4;
-        const dbf16x8 ah = *reinterpret_cast<const dbf16x8 *>(&sh.am[0][r][k]);
-        const dbf16x8 am = *reinterpret_cast<const dbf16x8 *>(&sh.am[1][r][k]);
+        const dbf16x8 ah = *reinterpret_cast<const dbf16x8 *>(&sh.u.op.am[0][r][k]);
+        const dbf16x8 am = *reinterpret_cast<const dbf16x8 *>(&sh.u.op.am[1][r][k]);
         dbf16x8 aq;
-        if (PROD) aq = *reinterpret_cast<const dbf16x8 *>(&sh.aq[r][k]);
+        if (PROD) aq = *reinterpret_cast<const dbf16x8 *>(&sh.u.op.aq[r][k]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           floatx4 c = accm[rt][ct];
@@ -170,22 +175,30 @@ __global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_wave
         }
       }
     }
-    // ---- out = n acc_mse + qjl gamma acc_sign (lane: rows 16 rt + 4 g4 + e, column 16 ct + j16) ----
+    // ---- out = n acc_mse + qjl gamma acc_sign (lane: rows 16 rt + 4 g4 + e, column 16 ct + j16), staged in
+    // LDS over the operands (every wave's reads of them done), then stored as whole rows: a wave's own
+    // columns are only 16 or 32 floats of a row ----
+    __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e;
-        const int64_t row = row0 + r;
-        if (row >= a.n) continue;
         const float nr = sh.nh[r], gr = PROD ? sh.gq[r] : 0.f;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float v = nr * accm[rt][ct][e];
           if (PROD) v = fmaf(gr, accq[rt][ct][e], v);
-          a.out[row * a.ldo + CW * wave + 16 * ct + j16] = v;
+          sh.u.ot[r][CW * wave + 16 * ct + j16] = v;
         }
       }
+    __syncthreads();
+    const int rows = (int)imin64(DB, a.n - row0);
+    for (int i = tid; i < rows * (D / 4); i += NW * 64) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      *reinterpret_cast<float4 *>(a.out + (row0 + r) * a.ldo + 4 * c4) =
+          *reinterpret_cast<const float4 *>(&sh.u.ot[r][4 * c4]);
+    }
   }
 }
 
