@@ -2,9 +2,11 @@
 //
 // One tiled kernel computes Z = A B^T (A: M x K, B: N x K, both read through
 // operand loaders) with v_mfma_f32_16x16x4_f32 and hands the 64 x 64 output
-// tile, staged in LDS, to an epilogue.  Loaders read dense fp32/bf16/fp16 rows
-// or dequantize packed records on the fly; epilogues store fp32, quantize and
-// pack index planes with wavefront ballots (Algorithm 1), or pack QJL sign bits
+// tile, staged in LDS, to an epilogue that stores fp32 (decode at d > 128,
+// query rotation, the attention output's rotation back); loaders read dense
+// fp32/bf16/fp16 rows or dequantize packed records on the fly.  The encode at
+// d > 128 runs the piece-wise kernel below (bf16 or fp16 matrix cores), whose
+// epilogues quantize and pack index planes (Algorithm 1) or QJL sign bits
 // (Algorithm 2).  Algorithm steps as on the ai-navigate-news Gemma 4 post,
 // section "仕組み（技術的）".
 //
@@ -330,7 +332,9 @@ static int gemm(const char *name, LA la, LB lb, EP ep, int64_t M, int64_t N, int
 // are checked against the fp64 definition with a 1e-5 tie zone).  A 128 x 128
 // tile per work-group, each wave a 64 x 64 quadrant (4 x 4 MFMA tiles), 32-deep
 // k-steps staged in LDS with the next step's loads in registers; the epilogues
-// of the fp32 kernel run once per quadrant.
+// take each wave's quadrant in two 32 x 64 halves, lane = (row, column half).
+// bf16 / fp16 rows up to d = 512 take fp16 operands instead (row-scaled rows,
+// two fp16 pieces of the matrix), as the fused encode kernel does.
 // ----------------------------------------------------------------------------
 constexpr int PBM = 128, PBN = 128, PBK = 32;
 
