@@ -59,6 +59,7 @@ def _cache(api, d, kmode, kb, vb, B, Hkv, T, seed):
     (128, "mse", 3, 2, 1, 64, 32, 8, 200, [0]),         # the first chunk of a prompt
     (256, "prod", 3, 2, 2, 9, 16, 4, 160, [151, 17]),    # Algorithm-2 keys
     (64, "mse", 2, 1, 1, 20, 4, 4, 64, [30]),            # 1-bit values
+    (128, "mse", 3, 2, 1, 128, 32, 8, 600, [400]),       # 4096 rows: the rotation back as one GEMM
 ])
 def test_attn_prefill(api, d, kmode, kb, vb, B, M, Hq, Hkv, T, qpos):
     rng = np.random.default_rng(600 + d + M)
