@@ -78,6 +78,34 @@ __global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_wave
   float cc[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) cc[i] = a.c[i];
+  // up to four centroids (BM <= 2): each bf16 piece of every centroid in a byte table of two words
+  // (centroid k in bytes 2k, 2k + 1), so that one byte permute picks the pieces of two coordinates, with
+  // the permute selectors of every pair of index values (and the +-1 pairs of the sign plane) in LDS
+  __shared__ uint32_t s_sel[16 + 4];
+  uint32_t lh_lo = 0u, lh_hi = 0u, lm_lo = 0u, lm_hi = 0u;
+  if constexpr (BM <= 2) {
+    uint32_t ph[4] = {0u, 0u, 0u, 0u}, pm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      const float h = __uint_as_float(__float_as_uint(cc[k]) & 0xFFFF0000u);
+      ph[k] = __float_as_uint(h) >> 16;
+      pm[k] = __float_as_uint(cc[k] - h) >> 16;
+    }
+    lh_lo = ph[0] | (ph[1] << 16);
+    lh_hi = ph[2] | (ph[3] << 16);
+    lm_lo = pm[0] | (pm[1] << 16);
+    lm_hi = pm[2] | (pm[3] << 16);
+    // w = plane-0 bits of the pair | plane-1 bits << 2 (BM = 2), or the plane-0 bits (BM = 1)
+    if (tid < 16) {
+      const int w = tid;
+      const int i0 = BM == 2 ? (w & 1) | ((w >> 1) & 2) : (w & 1);
+      const int i1 = BM == 2 ? ((w >> 1) & 1) | ((w >> 2) & 2) : ((w >> 1) & 1);
+      s_sel[w] = 0x01000100u + 0x0202u * (uint32_t)i0 + 0x02020000u * (uint32_t)i1;
+    } else if (tid < 20) {
+      const int sb = tid - 16;
+      s_sel[tid] = ((sb & 1) ? 0x3F80u : 0xBF80u) | (((sb & 2) ? 0x3F80u : 0xBF80u) << 16);
+    }
+  }
 
   const int sr = tid / NW, sk = (tid % NW) * PER;
   uint32_t bits[NPL];
@@ -104,6 +132,18 @@ __global__ __launch_bounds__(dec_waves(D, PROD) * 64) __attribute__((amdgpu_wave
 #pragma unroll
     for (int i = 0; i < PER; i += 8) {
       uint32_t hi[4], mi[4], sg[4];
+      if constexpr (BM <= 2) {  // (the tables are in LDS: the loop's first barrier has passed)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = i + 2 * q;
+          uint32_t w = (bits[0] >> j) & 3u;
+          if (BM == 2) w |= ((bits[1] >> j) & 3u) << 2;
+          const uint32_t sel = s_sel[w];
+          hi[q] = __builtin_amdgcn_perm(lh_hi, lh_lo, sel);
+          mi[q] = __builtin_amdgcn_perm(lm_hi, lm_lo, sel);
+          if (PROD) sg[q] = s_sel[16 + ((bits[BM] >> j) & 3u)];
+        }
+      } else
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float h2[2], m2[2];
