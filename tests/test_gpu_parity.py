@@ -101,12 +101,14 @@ def _oracle_encoded(qz_bits, prod, x, pi, s):
     return _dev(enc["record"]), _dev(parity.f16_bits(enc["n_hat"])), gam, xt
 
 
-# (1000 rows: a last 64-record tile of 40, whose rows the kernel stores and no row past it)
-@pytest.mark.parametrize("mode,bits,n", [("mse", 2, 4096), ("prod", 3, 4096), ("mse", 4, 4096), ("prod", 2, 4096),
-                                         ("mse", 3, 1000), ("prod", 3, 1000)])
-def test_decode_parity(api, mode, bits, n):
-    x, pi, s, _ = _unit_inputs(n)
-    d = 128
+# (1000 rows: a last 64-record tile of 40, whose rows the kernel stores and no row past it; head dim 64: a
+# thread's 16 coordinates as 16-bit plane words; 1 and 2 index bits expand by byte permutes, 3 by a select tree)
+@pytest.mark.parametrize("mode,bits,n,d", [("mse", 2, 4096, 128), ("prod", 3, 4096, 128), ("mse", 4, 4096, 128),
+                                           ("prod", 2, 4096, 128), ("mse", 3, 1000, 128), ("prod", 3, 1000, 128),
+                                           ("mse", 1, 1000, 128), ("mse", 2, 1000, 64), ("prod", 3, 1000, 64),
+                                           ("prod", 4, 1000, 64)])
+def test_decode_parity(api, mode, bits, n, d):
+    x, pi, s, _ = _unit_inputs(n, d)
     prod = mode == "prod"
     qz = api.Quantizer(d, bits, api.TQ_PROD if prod else api.TQ_MSE, pi, s if prod else None)
     codes, norms, gammas, ref = _oracle_encoded(bits, prod, x, pi, s)
