@@ -80,7 +80,8 @@ def measured_traffic():
 
 def encode_only(steps: int):
     """The one-layer encode workload (keys Algorithm 1 3-bit, values Algorithm 2 3-bit, 2 x 2^21 bf16 rows of
-    d 128) run `steps` times, for counter profiles of the encode kernels; prints one JSON line."""
+    d 128) run `steps` times, then the decode of the value records to fp32 rows `steps` times, for profiles of
+    the encode and decode kernels; prints one JSON line."""
     import torch
     from vector_quantization_rotation_amd import api, synth
     d, eB, eH, eT = 128, 8, 8, 32768
@@ -98,8 +99,20 @@ def encode_only(steps: int):
         vq.encode(V, codes=vc, norms=vn, gammas=vg)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    print(json.dumps({"encode": {"ms": round(dt * 1e3, 4), "vectors": 2 * K.shape[0],
-                                 "value": round(2 * K.shape[0] / dt, 1), "unit": "vectors/s"}}), flush=True)
+    del K
+    dec = torch.empty((V.shape[0], d), dtype=torch.float32, device="cuda")
+    del V
+    vq.decode(vc, vn, vg, out=dec)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        vq.decode(vc, vn, vg, out=dec)
+    torch.cuda.synchronize()
+    ddt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"encode": {"ms": round(dt * 1e3, 4), "vectors": 2 * kc.shape[0],
+                                 "value": round(2 * kc.shape[0] / dt, 1), "unit": "vectors/s"},
+                      "decode": {"ms": round(ddt * 1e3, 4), "vectors": dec.shape[0],
+                                 "value": round(dec.shape[0] / ddt, 1), "unit": "vectors/s"}}), flush=True)
 
 
 def copy_calibration():

@@ -484,7 +484,7 @@ int attn_combine(const float *part, int BH, int nsplit, int d, const tq_quantize
     if (rc != TQ_OK) return rc;
     return rotate_back(merged, BH, d, vq->piT, vq->sT, out, false, st);
   }
-  if (nsplit <= CMB_SPLITS && (d == 64 || d == 128 || d == 256)) {
+  if (nsplit >= 1 && nsplit <= CMB_SPLITS && (d == 64 || d == 128 || d == 256)) {
     const dim3 grid((unsigned)cdiv64(BH, 4), (unsigned)(d / 32));
     if (d == 64) hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);
     if (d == 128) hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(256), 0, st, part, (int64_t)BH, nsplit, d, pi, s, out);

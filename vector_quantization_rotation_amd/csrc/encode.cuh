@@ -478,6 +478,7 @@ encode_kernel(EncArgs a) {
           *reinterpret_cast<uint4 *>(&sh.rp[p][lane][CW * wave + 8 * c8]) = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
       }
     }
+    quant_fix_planes<BM>(plane, CW == 32 ? 0xFFFFFFFFu : (1u << CW) - 1u);
     if (n == 0.0f) {  // zero vector: every coordinate takes cell L/2 - 1
 #pragma unroll
       for (int p = 0; p < BM; ++p) plane[p] = (((L / 2 - 1) >> p) & 1) ? 0xFFFFFFFFu : 0u;

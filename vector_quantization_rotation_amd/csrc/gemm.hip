@@ -222,6 +222,7 @@ struct EpiQuant {
       if constexpr (RES) *reinterpret_cast<float4 *>(rdst + 4 * c4) = float4{r4[0], r4[1], r4[2], r4[3]};
     }
     if constexpr (BM > 0) {
+      quant_fix_planes<BM>(P);
       uint8_t *dst = codes + row * code_bytes + ((col0 + 32 * hc) >> 3);
 #pragma unroll
       for (int p = 0; p < BM; ++p) *reinterpret_cast<uint32_t *>(dst + p * (d >> 3)) = P[p];
