@@ -48,7 +48,7 @@ def _idx_of(codes, d, bits, mode_prod):
 # (1024 and 1100 rows at d > 128: the GEMM path's grid with the column blocks of a row block grouped on one XCD,
 # 8 row blocks, and with a row-block count that is not a multiple of 8)
 @pytest.mark.parametrize("n,d,bits", [(4096, 128, 2), (4096, 128, 3), (1000, 64, 1), (333, 256, 4), (130, 512, 3),
-                                      (1024, 256, 3), (1100, 512, 2)])
+                                      (1024, 256, 3), (1100, 512, 2), (1000, 64, 3), (777, 64, 4)])
 def test_encode_mse_parity(api, n, d, bits):
     x, pi, _, _ = _unit_inputs(n, d) if d == 128 else (synth.unit_test_vectors(n, d, 7, 8), synth.haar_rotation(d, 9), None, None)
     qz = api.Quantizer(d, bits, api.TQ_MSE, pi)
@@ -66,7 +66,8 @@ def test_encode_mse_parity(api, n, d, bits):
     print(f"mse d={d} b={bits}: mismatches {nbad}, tie-zone coords {nties}")
 
 
-@pytest.mark.parametrize("n,d,bits", [(4096, 128, 3), (4096, 128, 2), (257, 256, 4), (130, 512, 3), (1024, 512, 3), (1300, 256, 2)])
+@pytest.mark.parametrize("n,d,bits", [(4096, 128, 3), (4096, 128, 2), (257, 256, 4), (130, 512, 3), (1024, 512, 3), (1300, 256, 2),
+                                      (1024, 128, 4), (1000, 64, 3)])
 def test_encode_prod_parity(api, n, d, bits):
     if d == 128:
         x, pi, s, _ = _unit_inputs(n, d)

@@ -115,7 +115,7 @@ def _boundary_rows(d, t, rng, n_rows):
 
 
 @pytest.mark.parametrize("rot", ["identity", "haar"])
-@pytest.mark.parametrize("mode,bits", [("mse", 3), ("mse", 2), ("prod", 3)])
+@pytest.mark.parametrize("mode,bits", [("mse", 3), ("mse", 2), ("mse", 4), ("prod", 3), ("prod", 4)])
 def test_encode_boundary_exact_coordinates(api, rot, mode, bits):
     d, n = 128, 512
     rng = np.random.default_rng(81)
